@@ -1,0 +1,278 @@
+/*
+ * la.h - C ABI of the streaming timestep-forcing denoise step (Live Avatar hot path)
+ *        for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited below:
+ *   NOTES = papernotes.org, "Live Avatar: Streaming Real-time Audio-Driven Avatar
+ *           Generation with Infinite Length"
+ *   NEWS  = 10100.com, "连续直播上万秒不崩脸！阿里开源Live Avatar …"
+ *   POP   = admirer.cn popular article on Live Avatar
+ *   BLOG  = gitcode.csdn.net, "Live Avatar 深度解析：首个 14B 参数实时流式无限时长数字人"
+ *
+ * One stage of the timestep-forcing pipeline owns one fixed denoise step
+ * t_i -> t_{i-1} and a local noisy KV cache per layer (NOTES, 关键设计 4; NEWS,
+ * TPP figure caption).  Per block and layer the step rotates Q/K with 3D RoPE
+ * and the sink K with the rolling offset (la_rope3d_rolling), attends over
+ * {sink, cached blocks, the block} (la_block_attn_fwd), appends the block's
+ * K/V to the window (la_kvcache_append_evict), replaces the sink once after
+ * block 1 (la_sink_replace), and finally moves the latent one Euler step
+ * (la_fm_euler_step).
+ *
+ * Conventions shared by every call
+ *   - Device buffers are allocated, owned and freed by the caller.  The library
+ *     never allocates or frees device memory and keeps no global state apart
+ *     from a thread-local copy of the last HIP error text.
+ *   - Activations are contiguous and token-major: [tokens][heads][head_dim].
+ *     Tokens are ordered frame-major, then latent row h, then column w.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is enqueued on it; nothing synchronises.  Host-side state
+ *     (la_kvring) changes at call time, so the order of calls is the order of
+ *     state changes.
+ *   - Argument, shape, dtype and state errors are detected before any launch
+ *     and change nothing.  A failed launch returns LA_ERR_HIP (see
+ *     la_last_hip_error).  A fault inside a kernel surfaces at the caller's
+ *     next synchronisation.
+ *   - No handle is thread-safe.
+ */
+#ifndef LA_H_
+#define LA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = -1,  /* NULL pointer, non-positive size, bad enum value      */
+  LA_ERR_SHAPE = -2,        /* sizes disagree with the ring or a kernel's limits    */
+  LA_ERR_DTYPE = -3,        /* dtype not supported by this call                     */
+  LA_ERR_STATE = -4,        /* block out of order, second sink replacement, ...     */
+  LA_ERR_NOISE_LEVEL = -5,  /* append at another noise level than the cache's      */
+  LA_ERR_HIP = -6           /* a HIP runtime call or launch failed                  */
+} la_status;
+
+typedef enum la_dtype { LA_BF16 = 0, LA_F32 = 1 } la_dtype;
+
+typedef void* la_stream_t; /* hipStream_t */
+
+#define LA_MAX_WINDOW 64
+#define LA_MAX_BLOCK_FRAMES 4
+
+/*
+ * la_kvring - one layer's rolling noisy KV cache plus its attention sink.
+ * A plain host struct owned by the caller; it only points at device memory.
+ *
+ *   k_slots, v_slots : device, [W][block_tokens][heads][head_dim] of dtype.
+ *                      Slot s holds block b with (b - 1) mod W == s.
+ *   sink_k_raw       : device, [sink_tokens][heads][head_dim], the sink's
+ *                      unrotated K (it is re-rotated at every block).
+ *   sink_v           : device, same shape, the sink's V.
+ *   slot_block[s]    : block id held by slot s (0 = empty).
+ *   last_block       : id of the last appended block (0 = none yet).
+ *   noise_level      : the stage's t_i; every cached entry is at this level.
+ *   sink_replaced    : 1 after the one-time replacement.
+ *
+ * Ring rules (BLOG, 疑问 4; NOTES, 关键设计 2): the cache holds the K/V that
+ * this stage computed from its own noisy input x_{t_i} for the last W blocks,
+ * oldest evicted first, with no clean refresh.  The index fields are part of
+ * the bit-exact contract and may be saved and restored together with the
+ * device buffers to checkpoint a stage.
+ */
+typedef struct la_kvring {
+  void* k_slots;
+  void* v_slots;
+  void* sink_k_raw;
+  void* sink_v;
+  int32_t W;
+  int32_t block_tokens;
+  int32_t sink_tokens;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t dtype;          /* la_dtype */
+  float noise_level;
+  int32_t sink_replaced;
+  int64_t last_block;
+  int64_t slot_block[LA_MAX_WINDOW];
+} la_kvring;
+
+/* Text for a status code (static storage). */
+const char* la_status_string(int status);
+
+/* Text of the last HIP error seen on this thread ("" if none). */
+const char* la_last_hip_error(void);
+
+/* Library version string (static storage). */
+const char* la_version(void);
+
+/*
+ * la_kvring_init - fill *r for an empty window.  Pure host; touches no device
+ * memory (the slot contents are unspecified until blocks are appended).
+ * 1 <= W <= LA_MAX_WINDOW; all sizes > 0; pointers non-NULL.
+ */
+la_status la_kvring_init(la_kvring* r, void* k_slots, void* v_slots, void* sink_k_raw,
+                         void* sink_v, int32_t W, int32_t block_tokens, int32_t sink_tokens,
+                         int32_t heads, int32_t head_dim, la_dtype dtype, float noise_level);
+
+/*
+ * la_kvring_advance - where appending block `block_id` would go, without
+ * changing anything.  Pure host.  *slot = (block_id - 1) mod W; *evicted =
+ * the block that leaves the window (block_id - W) or 0 if none.  Returns
+ * LA_ERR_STATE unless block_id == r->last_block + 1.
+ */
+la_status la_kvring_advance(const la_kvring* r, int64_t block_id, int32_t* slot,
+                            int64_t* evicted);
+
+/* Number of cached blocks, min(last_block, W).  Pure host. */
+int32_t la_kvring_count(const la_kvring* r);
+
+/*
+ * 3D RoPE tables.  head_dim d is split into bands (d - 4*floor(d/6),
+ * 2*floor(d/6), 2*floor(d/6)) for the (frame, h, w) axes; pair k of a band of
+ * width w_a (dims 2k, 2k+1 of the band) turns by p * theta^(-2k/w_a), where
+ * p is the token's coordinate on that axis: (x, y) -> (x cos - y sin,
+ * x sin + y cos).  (The pages name RoPE over the video's positions without
+ * its axes or base; this is the conventional 3D factorisation.)
+ *
+ * la_rope_table_bytes: size of the spatial (h, w) cos/sin table.
+ * la_rope_table_fill:  compute it on the device in float64 and store float32
+ *                      into dev_table (caller-owned, >= la_rope_table_bytes,
+ *                      4-byte aligned).  Asynchronous on `stream`.
+ */
+size_t la_rope_table_bytes(int32_t Hl, int32_t Wl, int32_t head_dim);
+la_status la_rope_table_fill(void* dev_table, int32_t Hl, int32_t Wl, int32_t head_dim,
+                             double theta, la_stream_t stream);
+
+/*
+ * la_rope3d_rolling - Rolling RoPE for one block (NOTES, 关键设计 3: the sink's
+ * temporal offset follows the active block so their relative distance stays
+ * constant; POP, RSFM section: sink position = current position + a fixed
+ * offset; BLOG, 疑问 5: after the one-time replacement only the sink's
+ * position encoding changes).
+ *
+ *   q_in/q_out, k_in/k_out : [n_frames*Hl*Wl][heads][head_dim]; token
+ *       (j*Hl + h)*Wl + w is rotated at (f0 + j, h, w).  Either pair may be
+ *       NULL (skipped).  Out-of-place or in place (out == in).
+ *   sink_k_in/sink_k_out   : [Hl*Wl][heads][head_dim], the raw sink K rotated
+ *       at (f0 + sink_delta, h, w).  May be NULL (skipped).
+ *   dev_table              : filled by la_rope_table_fill for (Hl, Wl, head_dim, theta).
+ *   The temporal cos/sin are computed on the host in float64 for these
+ *   positions at every call, so positions can grow without bound (10,000 s
+ *   streams) without float32 angle error.
+ *   dtype LA_BF16: bf16 in/out, float32 arithmetic, round-to-nearest-even
+ *   store.  LA_F32: float32 throughout.  1 <= n_frames <= LA_MAX_BLOCK_FRAMES;
+ *   head_dim % 8 == 0, 8 <= head_dim <= 256, and the frame band holds at most
+ *   48 pairs.
+ *   Pointers must be 16-byte aligned.
+ */
+la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                            int32_t n_frames, int64_t f0, const void* sink_k_in,
+                            void* sink_k_out, int64_t sink_delta, const void* dev_table,
+                            int32_t Hl, int32_t Wl, int32_t heads, int32_t head_dim,
+                            la_dtype dtype, double theta, la_stream_t stream);
+
+/*
+ * la_block_attn_fwd - block attention of the current block (NOTES, 整体框架:
+ * a block of 3 latent frames attends causally, at block granularity, to the
+ * static sink frame and the sliding KV cache; 关键设计 2: the cache holds noisy
+ * K/V at the block's own noise level).  For every head:
+ *
+ *     out = softmax(scale * Q K_all^T) V_all,
+ *     K_all = [sink_k_rot ; cached blocks of r (oldest first) ; k_cur_rot]
+ *     V_all = [r->sink_v  ; cached blocks of r               ; v_cur]
+ *
+ * with no mask (the block sees itself bidirectionally; later blocks do not
+ * exist yet).  Reads la_kvring_count(r) cached blocks; call it before
+ * appending the current block.
+ *
+ *   q_rot, k_cur_rot, v_cur, out : [n_q][heads][head_dim]; n_q = r->block_tokens.
+ *   sink_k_rot : [r->sink_tokens][heads][head_dim] (output of la_rope3d_rolling).
+ *   lse_or_null: if non-NULL, float32 [heads][n_q] natural-log
+ *                log(sum exp(scale q.k)) per row.
+ *   LA_BF16: bf16 MFMA products with float32 accumulation and float32 online
+ *            softmax, bf16 output (round-to-nearest-even); head_dim == 128.
+ *   LA_F32 : float32 throughout; head_dim 64 or 128.
+ *   Pointers 16-byte aligned; `out` must not alias an input.
+ */
+la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot,
+                            const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
+                            float* lse_or_null, float scale, la_stream_t stream);
+
+/*
+ * la_kvcache_append_evict - put block `block_id`'s rotated K and its V
+ * (both [block_tokens][heads][head_dim], computed by this stage from its own
+ * noisy input, BLOG 疑问 4) into slot (block_id - 1) mod W, evicting block
+ * block_id - W.  Requires block_id == r->last_block + 1 (else LA_ERR_STATE)
+ * and noise_level == r->noise_level (else LA_ERR_NOISE_LEVEL: the timestep-
+ * forcing rule of NEWS 方法概述, the cache and the latent share one noise
+ * level).  *evicted_or_null receives the evicted id or 0.  The copy is
+ * enqueued on `stream`; the index update happens at call time.
+ */
+la_status la_kvcache_append_evict(la_kvring* r, const void* k_rot, const void* v,
+                                  int64_t block_id, float noise_level,
+                                  int64_t* evicted_or_null, la_stream_t stream);
+
+/*
+ * la_sink_replace - Adaptive Attention Sink (NOTES, 关键设计 3; BLOG, 疑问 5):
+ * once, after the first block, copy the new raw sink K and V (each
+ * [sink_tokens][heads][head_dim]) into r->sink_k_raw / r->sink_v.  A second
+ * call returns LA_ERR_STATE and changes nothing; so does a call before block
+ * 1 has been appended.
+ */
+la_status la_sink_replace(la_kvring* r, const void* k_new_raw, const void* v_new,
+                          la_stream_t stream);
+
+/*
+ * la_fm_euler_step - flow-matching Euler update in place (NOTES, 损失函数:
+ * the model predicts the velocity v of the path, v = x_1 - x_0):
+ * x[i] = x[i] + dt * v[i] for 0 <= i < n, float32, one rounding per element
+ * (fused multiply-add).  n == 0 is a no-op.  x and v must not overlap
+ * partially (x == v is allowed).
+ */
+la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_stream_t stream);
+
+/*
+ * la_denoise_step - one block through one timestep-forcing stage t_i -> t_{i-1}
+ * (NOTES, 关键设计 4: each pipeline GPU runs one fixed denoise step with its
+ * local noisy caches and hands only the latent on; BLOG, 疑问 6).  For every
+ * layer l, in order, on `stream`:
+ *   1. la_rope3d_rolling of q_raw[l], k_raw[l] at f0 = frames_per_block *
+ *      (block_id - 1) into q_rot_ws / k_rot_ws, and of rings[l].sink_k_raw at
+ *      f0 + sink_delta into sink_k_rot_ws;
+ *   2. la_block_attn_fwd into attn_out[l];
+ *   3. la_kvcache_append_evict of (k_rot_ws, v_raw[l]) as block block_id;
+ *   4. if block_id == 1 and sink_k_new != NULL: la_sink_replace with
+ *      (sink_k_new[l], sink_v_new[l]) (Adaptive Attention Sink, NOTES 关键设计 3);
+ * then la_fm_euler_step(x, vel, n_latent, dt) if x != NULL.
+ *
+ *   rings[n_layers]        : one la_kvring per layer, identical geometry and
+ *                            noise level, all at last_block == block_id - 1.
+ *   q_raw/k_raw/v_raw/attn_out : arrays of n_layers device pointers, each
+ *                            [block_tokens][heads][head_dim].
+ *   q_rot_ws, k_rot_ws     : device workspaces [block_tokens][heads][head_dim],
+ *                            reused by every layer (stream order keeps them safe).
+ *   sink_k_rot_ws          : device workspace [sink_tokens][heads][head_dim].
+ *   rope_table             : la_rope_table_fill output for (Hl, Wl, head_dim, theta);
+ *                            block_tokens must equal frames_per_block*Hl*Wl and
+ *                            sink_tokens Hl*Wl.
+ *   scale                  : softmax scale (1/sqrt(head_dim) for the model).
+ * The whole step is validated before the first launch; on an error nothing is
+ * enqueued and no ring changes.  Pointer arrays are host memory read at call
+ * time.
+ */
+la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
+                          const void* const* q_raw, const void* const* k_raw,
+                          const void* const* v_raw, void* const* attn_out, void* q_rot_ws,
+                          void* k_rot_ws, void* sink_k_rot_ws, const void* const* sink_k_new,
+                          const void* const* sink_v_new, const void* rope_table, int32_t Hl,
+                          int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
+                          double theta, float scale, float* x, const float* vel,
+                          int64_t n_latent, float dt, la_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H_ */

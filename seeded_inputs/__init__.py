@@ -17,6 +17,7 @@ generation stays bounded; block ``b`` uses entry ``(b - 1) % pool``.
 from __future__ import annotations
 
 import dataclasses
+import functools
 from typing import Optional, Tuple
 
 import numpy as np
@@ -62,28 +63,45 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 class Stored:
     """A synthetic tensor as the kernels store it and as the oracle reads it."""
 
-    storage: np.ndarray  # uint16 bf16 bit patterns, or float32
-    values: np.ndarray   # float64, exactly the stored values
+    storage: np.ndarray  # uint16 bf16 bit patterns, or float32 (read-only)
     dtype: str           # "bf16" or "f32"
+
+    @property
+    def values(self) -> np.ndarray:
+        """float64, exactly the stored values."""
+        if self.dtype == "bf16":
+            return bf16_bits_to_f64(self.storage)
+        return self.storage.astype(np.float64)
 
 
 def make_stored(x64: np.ndarray, dtype: str) -> Stored:
     if dtype == "bf16":
-        bits = f64_to_bf16_bits(x64)
-        return Stored(bits, bf16_bits_to_f64(bits), dtype)
-    if dtype == "f32":
+        s = f64_to_bf16_bits(x64)
+    elif dtype == "f32":
         s = np.asarray(x64, dtype=np.float64).astype(np.float32)
-        return Stored(s, s.astype(np.float64), dtype)
-    raise ValueError(f"unknown dtype {dtype!r}")
+    else:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    s.flags.writeable = False
+    return Stored(s, dtype)
 
 
-def tensor(cfg_id: int, layer: int, entry: int, tid: int, shape, dtype: str,
-           scale: float = 1.0) -> Stored:
-    """One seeded tensor, N(0,1) times ``scale``, rounded to ``dtype``."""
+@functools.lru_cache(maxsize=96)
+def _tensor_cached(cfg_id, layer, entry, tid, shape, dtype, scale) -> Stored:
     x = gaussian((cfg_id, layer, entry, tid), shape)
     if scale != 1.0:
         x = x * scale
     return make_stored(x, dtype)
+
+
+def tensor(cfg_id: int, layer: int, entry: int, tid: int, shape, dtype: str,
+           scale: float = 1.0) -> Stored:
+    """One seeded tensor, N(0,1) times ``scale``, rounded to ``dtype`` (memoised)."""
+    return _tensor_cached(int(cfg_id), int(layer), int(entry), int(tid),
+                          tuple(int(s) for s in shape), dtype, float(scale))
+
+
+def clear_cache() -> None:
+    _tensor_cached.cache_clear()
 
 
 @dataclasses.dataclass(frozen=True)

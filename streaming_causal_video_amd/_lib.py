@@ -1,0 +1,325 @@
+"""ctypes binding of liblahip (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does
+nothing but check tensors (device, dtype, contiguity, size), pass their
+device pointers and the current HIP stream, and turn a non-zero status into
+an exception.  All arithmetic runs in the HIP kernels.  There is no fallback:
+if the library is missing, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "liblahip.so")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_STATE, LA_ERR_NOISE_LEVEL, \
+    LA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+LA_BF16, LA_F32 = 0, 1
+LA_MAX_WINDOW = 64
+LA_MAX_BLOCK_FRAMES = 4
+
+EXPORTED = [
+    "la_status_string", "la_last_hip_error", "la_version", "la_kvring_init", "la_kvring_advance",
+    "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
+    "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
+    "la_denoise_step",
+]
+
+
+class la_kvring(ctypes.Structure):
+    """Mirror of the C struct la_kvring (include/la.h)."""
+
+    _fields_ = [
+        ("k_slots", ctypes.c_void_p),
+        ("v_slots", ctypes.c_void_p),
+        ("sink_k_raw", ctypes.c_void_p),
+        ("sink_v", ctypes.c_void_p),
+        ("W", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
+        ("sink_tokens", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("noise_level", ctypes.c_float),
+        ("sink_replaced", ctypes.c_int32),
+        ("last_block", ctypes.c_int64),
+        ("slot_block", ctypes.c_int64 * LA_MAX_WINDOW),
+    ]
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = _load()
+        msg = lib.la_status_string(status).decode()
+        if status == LA_ERR_HIP:
+            msg += " (" + lib.la_last_hip_error().decode() + ")"
+        super().__init__(f"{what}: {msg} [{status}]")
+        self.status = status
+
+
+_LIB = None
+
+
+def _load():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m streaming_causal_video_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, D, VP = (ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_double, ctypes.c_void_p)
+    R = P(la_kvring)
+    sig = {
+        "la_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "la_last_hip_error": (ctypes.c_char_p, []),
+        "la_version": (ctypes.c_char_p, []),
+        "la_kvring_init": (ctypes.c_int, [R, VP, VP, VP, VP, I32, I32, I32, I32, I32, ctypes.c_int, F]),
+        "la_kvring_advance": (ctypes.c_int, [R, I64, P(I32), P(I64)]),
+        "la_kvring_count": (I32, [R]),
+        "la_rope_table_bytes": (ctypes.c_size_t, [I32, I32, I32]),
+        "la_rope_table_fill": (ctypes.c_int, [VP, I32, I32, I32, D, VP]),
+        "la_rope3d_rolling": (ctypes.c_int, [VP, VP, VP, VP, I32, I64, VP, VP, I64, VP, I32, I32,
+                                             I32, I32, ctypes.c_int, D, VP]),
+        "la_block_attn_fwd": (ctypes.c_int, [R, VP, VP, VP, VP, I32, VP, VP, F, VP]),
+        "la_kvcache_append_evict": (ctypes.c_int, [R, VP, VP, I64, F, P(I64), VP]),
+        "la_sink_replace": (ctypes.c_int, [R, VP, VP, VP]),
+        "la_fm_euler_step": (ctypes.c_int, [VP, VP, I64, F, VP]),
+        "la_denoise_step": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP, VP,
+                                           P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, VP,
+                                           I64, F, VP]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def lib():
+    """The loaded CDLL (raises ImportError if liblahip.so has not been built)."""
+    return _load()
+
+
+# ---------------------------------------------------------------- helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, name: str, shape=None, dtype=None):
+    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, what: str):
+    if status != LA_OK:
+        raise LAError(status, what)
+
+
+# ---------------------------------------------------------------- C entry points
+def la_version() -> str:
+    return _load().la_version().decode()
+
+
+def la_kvring_init(ring: "la_kvring", k_slots, v_slots, sink_k_raw, sink_v, W: int,
+                   block_tokens: int, sink_tokens: int, heads: int, head_dim: int,
+                   dtype: int, noise_level: float) -> None:
+    """Pointers may be tensors or raw integer addresses."""
+    def addr(x):
+        return ctypes.c_void_p(x if isinstance(x, int) else x.data_ptr())
+    _check(_load().la_kvring_init(ctypes.byref(ring), addr(k_slots), addr(v_slots),
+                                  addr(sink_k_raw), addr(sink_v), W, block_tokens, sink_tokens,
+                                  heads, head_dim, dtype, noise_level), "la_kvring_init")
+
+
+def la_kvring_advance(ring: "la_kvring", block_id: int):
+    """(slot, evicted) for appending block_id; raises LAError(LA_ERR_STATE) if out of order."""
+    slot = ctypes.c_int32()
+    ev = ctypes.c_int64()
+    _check(_load().la_kvring_advance(ctypes.byref(ring), block_id, ctypes.byref(slot),
+                                     ctypes.byref(ev)), "la_kvring_advance")
+    return slot.value, ev.value
+
+
+def la_kvring_count(ring: "la_kvring") -> int:
+    return _load().la_kvring_count(ctypes.byref(ring))
+
+
+def la_rope_table_bytes(Hl: int, Wl: int, head_dim: int) -> int:
+    return _load().la_rope_table_bytes(Hl, Wl, head_dim)
+
+
+def la_rope_table_fill(table, Hl: int, Wl: int, head_dim: int, theta: float = 10000.0) -> None:
+    torch = _torch()
+    need = la_rope_table_bytes(Hl, Wl, head_dim)
+    if table.dtype != torch.float32 or table.numel() * 4 < need:
+        raise ValueError("table must be float32 with at least la_rope_table_bytes bytes")
+    _check(_load().la_rope_table_fill(_ptr(table, "table"), Hl, Wl, head_dim, theta, _stream()),
+           "la_rope_table_fill")
+
+
+def la_rope3d_rolling(q_in, q_out, k_in, k_out, n_frames: int, f0: int, sink_k_in, sink_k_out,
+                      sink_delta: int, table, Hl: int, Wl: int, heads: int, head_dim: int,
+                      theta: float = 10000.0) -> None:
+    ref = next(t for t in (q_in, k_in, sink_k_in) if t is not None)
+    dt = _dtype_code(ref)
+    blk = (n_frames * Hl * Wl, heads, head_dim)
+    snk = (Hl * Wl, heads, head_dim)
+    args = [_ptr(q_in, "q_in", blk, ref.dtype), _ptr(q_out, "q_out", blk, ref.dtype),
+            _ptr(k_in, "k_in", blk, ref.dtype), _ptr(k_out, "k_out", blk, ref.dtype)]
+    sargs = [_ptr(sink_k_in, "sink_k_in", snk, ref.dtype),
+             _ptr(sink_k_out, "sink_k_out", snk, ref.dtype)]
+    _check(_load().la_rope3d_rolling(*args, n_frames, f0, *sargs, sink_delta,
+                                     _ptr(table, "table"), Hl, Wl, heads, head_dim, dt, theta,
+                                     _stream()), "la_rope3d_rolling")
+
+
+def la_block_attn_fwd(ring: "la_kvring", q_rot, sink_k_rot, k_cur_rot, v_cur, out,
+                      lse: Optional[object] = None, scale: Optional[float] = None) -> None:
+    torch = _torch()
+    dtype = torch.bfloat16 if ring.dtype == LA_BF16 else torch.float32
+    blk = (ring.block_tokens, ring.heads, ring.head_dim)
+    snk = (ring.sink_tokens, ring.heads, ring.head_dim)
+    if scale is None:
+        scale = ring.head_dim ** -0.5
+    lse_p = None
+    if lse is not None:
+        lse_p = _ptr(lse, "lse", (ring.heads, ring.block_tokens), torch.float32)
+    _check(_load().la_block_attn_fwd(
+        ctypes.byref(ring), _ptr(q_rot, "q_rot", blk, dtype), _ptr(sink_k_rot, "sink_k_rot", snk, dtype),
+        _ptr(k_cur_rot, "k_cur_rot", blk, dtype), _ptr(v_cur, "v_cur", blk, dtype),
+        ring.block_tokens, _ptr(out, "out", blk, dtype), lse_p, scale, _stream()),
+        "la_block_attn_fwd")
+
+
+def la_kvcache_append_evict(ring: "la_kvring", k_rot, v, block_id: int, noise_level: float) -> int:
+    """Returns the evicted block id (0 if none)."""
+    torch = _torch()
+    dtype = torch.bfloat16 if ring.dtype == LA_BF16 else torch.float32
+    blk = (ring.block_tokens, ring.heads, ring.head_dim)
+    ev = ctypes.c_int64()
+    _check(_load().la_kvcache_append_evict(ctypes.byref(ring), _ptr(k_rot, "k_rot", blk, dtype),
+                                           _ptr(v, "v", blk, dtype), block_id, noise_level,
+                                           ctypes.byref(ev), _stream()), "la_kvcache_append_evict")
+    return ev.value
+
+
+def la_sink_replace(ring: "la_kvring", k_new_raw, v_new) -> None:
+    torch = _torch()
+    dtype = torch.bfloat16 if ring.dtype == LA_BF16 else torch.float32
+    snk = (ring.sink_tokens, ring.heads, ring.head_dim)
+    _check(_load().la_sink_replace(ctypes.byref(ring), _ptr(k_new_raw, "k_new_raw", snk, dtype),
+                                   _ptr(v_new, "v_new", snk, dtype), _stream()), "la_sink_replace")
+
+
+def la_fm_euler_step(x, v, dt: float) -> None:
+    torch = _torch()
+    if x.dtype != torch.float32 or v.dtype != torch.float32 or x.numel() != v.numel():
+        raise ValueError("x and v must be float32 tensors of equal size")
+    _check(_load().la_fm_euler_step(_ptr(x, "x"), _ptr(v, "v"), x.numel(), dt, _stream()),
+           "la_fm_euler_step")
+
+
+def _ptr_array(ts, name):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t, f"{name}[{i}]").value
+    return arr
+
+
+def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_ws, k_rot_ws,
+                    sink_k_rot_ws, rope_table, Hl: int, Wl: int, frames_per_block: int = 3,
+                    sink_delta: int = -1, theta: float = 10000.0, scale: Optional[float] = None,
+                    sink_k_new=None, sink_v_new=None, x=None, vel=None, dt: float = -0.25) -> None:
+    """rings: a ctypes array of la_kvring (see KVRingStack); the other per-layer
+    arguments are lists of tensors."""
+    n = len(rings)
+    if scale is None:
+        scale = rings[0].head_dim ** -0.5
+    skn = _ptr_array(sink_k_new, "sink_k_new") if sink_k_new is not None else None
+    svn = _ptr_array(sink_v_new, "sink_v_new") if sink_v_new is not None else None
+    n_lat = 0 if x is None else x.numel()
+    if x is not None and (vel is None or vel.numel() != n_lat):
+        raise ValueError("vel must match x")
+    _check(_load().la_denoise_step(
+        rings, n, block_id, _ptr_array(q_raw, "q_raw"), _ptr_array(k_raw, "k_raw"),
+        _ptr_array(v_raw, "v_raw"), _ptr_array(attn_out, "attn_out"), _ptr(q_rot_ws, "q_rot_ws"),
+        _ptr(k_rot_ws, "k_rot_ws"), _ptr(sink_k_rot_ws, "sink_k_rot_ws"), skn, svn,
+        _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta, scale,
+        _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, _stream()), "la_denoise_step")
+
+
+# ---------------------------------------------------------------- one layer's cache
+class KVRing:
+    """One layer's ring + sink: device buffers from torch, index state in la_kvring."""
+
+    def __init__(self, W: int, block_tokens: int, sink_tokens: int, heads: int, head_dim: int,
+                 dtype, noise_level: float, device="cuda"):
+        torch = _torch()
+        self.k_slots = torch.empty((W, block_tokens, heads, head_dim), dtype=dtype, device=device)
+        self.v_slots = torch.empty_like(self.k_slots)
+        self.sink_k_raw = torch.empty((sink_tokens, heads, head_dim), dtype=dtype, device=device)
+        self.sink_v = torch.empty_like(self.sink_k_raw)
+        self.state = la_kvring()
+        la_kvring_init(self.state, self.k_slots, self.v_slots, self.sink_k_raw, self.sink_v, W,
+                       block_tokens, sink_tokens, heads, head_dim,
+                       LA_BF16 if dtype == torch.bfloat16 else LA_F32, noise_level)
+
+    @property
+    def count(self) -> int:
+        return la_kvring_count(self.state)
+
+    def slot_ids(self):
+        return [int(self.state.slot_block[s]) for s in range(self.state.W)]
+
+
+class KVRingStack:
+    """Per-layer rings for a whole stage, with the la_kvring structs contiguous so that
+    la_denoise_step can take them as one array."""
+
+    def __init__(self, n_layers: int, W: int, block_tokens: int, sink_tokens: int, heads: int,
+                 head_dim: int, dtype, noise_level: float, device="cuda"):
+        torch = _torch()
+        self.k_slots = torch.empty((n_layers, W, block_tokens, heads, head_dim), dtype=dtype,
+                                   device=device)
+        self.v_slots = torch.empty_like(self.k_slots)
+        self.sink_k_raw = torch.empty((n_layers, sink_tokens, heads, head_dim), dtype=dtype,
+                                      device=device)
+        self.sink_v = torch.empty_like(self.sink_k_raw)
+        self.states = (la_kvring * n_layers)()
+        code = LA_BF16 if dtype == torch.bfloat16 else LA_F32
+        for l in range(n_layers):
+            la_kvring_init(self.states[l], self.k_slots[l], self.v_slots[l], self.sink_k_raw[l],
+                           self.sink_v[l], W, block_tokens, sink_tokens, heads, head_dim, code,
+                           noise_level)

@@ -1,0 +1,287 @@
+// Block attention, bf16 MFMA, head_dim 128, for gfx950 (CDNA4).
+//
+// out = softmax(scale * Q K_all^T) V_all per head, over the keys of a segment
+// table {rotated sink, cached blocks, the block itself} with no mask
+// (papernotes.org "Live Avatar: Streaming Real-time Audio-Driven Avatar
+// Generation with Infinite Length", 整体框架 and 关键设计 2: a 3-latent-frame
+// block attends to the sink frame and to the sliding noisy KV cache).
+//
+// Design (MI355X-first, not a port of the pages' FlashAttention):
+//  * One workgroup = 4 waves = 128 query rows of one head; each wave owns 32
+//    query rows for the whole key range and keeps its Q fragments, the running
+//    row max / row sum and the output accumulator in registers.
+//  * Keys are walked as one virtual range over the segment table, 64 keys per
+//    tile, so tiles straddle segment boundaries and only the very last tile
+//    can be partial.  K and V tiles are staged global -> registers -> LDS,
+//    double buffered, one barrier per tile; the next tile's global loads are in
+//    flight while the current tile is computed.
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: in the 32x32 result each lane holds one query
+//    (lane % 32) and half of the tile's keys, so the row max needs one
+//    v_permlane32_swap per tile and the row sum none until the end.
+//  * K rows are fed to the MFMA in an order that swaps bits 2 and 3 of the row
+//    index; then the probabilities P^T come out of the score accumulator
+//    already in the B-operand layout of the second product O^T = V^T P^T, with
+//    no shuffle.  V^T operands come straight from the row-major V tile through
+//    the gfx950 LDS transpose read ds_read_b64_tr_b16.
+//  * Online softmax in float32 with the scale folded into a base-2 exponent
+//    (one FMA and one v_exp_f32 per score); P is rounded to bf16 for the second
+//    product with v_cvt_pk_bf16_f32.
+//  * Workgroups are renumbered so that all query tiles of a head run on the
+//    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 while
+//    they stream the head's K/V.
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int D = 128;
+constexpr int BM = 128;  // query rows per workgroup
+constexpr int BN = 64;   // keys per tile
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int KP = 136;  // K row pitch in LDS (bf16): 272 B, 16 rows hit 16 disjoint bank quads
+constexpr int VP = 160;  // V row pitch in LDS (bf16): 320 B, conflict-free transpose reads
+constexpr int KBUF = BN * KP;
+constexpr int VBUF = BN * VP;
+constexpr int STAGE = KBUF + VBUF;
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row of the K tile that feeds MFMA row i: bits 2 and 3 of i swapped.
+__device__ __forceinline__ int k_row_perm(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
+                          amdgpu_waves_per_eu(2, 2))) void
+attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
+                 float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
+                 float c2, int qtiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+  // XCD-aware renumbering: consecutive logical ids on one XCD.
+  const int nwg = gridDim.x;
+  const int pid = blockIdx.x;
+  const int per = (nwg + 7) / 8;
+  const int tall = (nwg % 8) == 0 ? 8 : (nwg % 8);
+  const int xcd = pid % 8, loc = pid / 8;
+  const int lin = xcd < tall ? xcd * per + loc : tall * per + (xcd - tall) * (per - 1) + loc;
+  const int head = lin / qtiles;
+  const int qt = lin - head * qtiles;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t rs = (int64_t)heads * D;
+
+  // Q^T B-operand fragments: lane holds Q[qrow][16 s + 8 hh .. +7].
+  const int qrow = qt * BM + wave * 32 + l32;
+  bf16x8_t qf[8];
+  if (qrow < nq) {
+    const uint16_t* qp = q + qrow * rs + head * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = bf16x8_t{};
+  }
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
+  float m_run = -INFINITY;  // running max of scale*log2(e)*score
+  float l_run = 0.f;        // this lane's half of the running row sum
+
+  // Loader: thread covers 16-byte chunk lcc of rows lr0 + 16 i.
+  const int lcc = tid & 15;
+  const int lr0 = tid >> 4;
+  const int ntiles = (nk + BN - 1) / BN;
+  uint4 kreg[4], vreg[4];
+
+  auto gload = [&](int tile) {
+    const int t0 = tile * BN;
+    int s0 = 0;
+    while (t0 >= segs.end[s0]) ++s0;
+    const int tend = min(t0 + BN, nk);
+    if (tend <= segs.end[s0]) {
+      const int start = s0 ? segs.end[s0 - 1] : 0;
+      const uint16_t* kb = static_cast<const uint16_t*>(segs.k[s0]);
+      const uint16_t* vb = static_cast<const uint16_t*>(segs.v[s0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = t0 + lr0 + 16 * i;
+        if (key < nk) {
+          const int64_t off = (int64_t)(key - start) * rs + head * D + lcc * 8;
+          kreg[i] = *reinterpret_cast<const uint4*>(kb + off);
+          vreg[i] = *reinterpret_cast<const uint4*>(vb + off);
+        } else {
+          kreg[i] = make_uint4(0, 0, 0, 0);
+          vreg[i] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = t0 + lr0 + 16 * i;
+        if (key < nk) {
+          int s = s0;
+          while (key >= segs.end[s]) ++s;
+          const int start = s ? segs.end[s - 1] : 0;
+          const int64_t off = (int64_t)(key - start) * rs + head * D + lcc * 8;
+          kreg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(segs.k[s]) + off);
+          vreg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(segs.v[s]) + off);
+        } else {
+          kreg[i] = make_uint4(0, 0, 0, 0);
+          vreg[i] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* kb = lds + buf * STAGE;
+    uint16_t* vb = kb + KBUF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lr0 + 16 * i;
+      *reinterpret_cast<uint4*>(kb + row * KP + lcc * 8) = kreg[i];
+      *reinterpret_cast<uint4*>(vb + row * VP + lcc * 8) = vreg[i];
+    }
+  };
+
+  const int krow_a = k_row_perm(l32);
+  // transpose-read address pieces for V^T fragments
+  const int vrow_a = 8 * hh + ((lane & 15) >> 2);
+  const int vcol_a = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  gload(0);
+  for (int j = 0; j < ntiles; ++j) {
+    lstore(j & 1);
+    if (j + 1 < ntiles) gload(j + 1);
+    __syncthreads();
+    const uint16_t* kb = lds + (j & 1) * STAGE;
+    const uint16_t* vb = kb + KBUF;
+
+    // S^T[key][query] for two 32-key blocks.
+    f32x16_t st[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      st[b] = f32x16_t{};
+      const uint16_t* kr = kb + (32 * b + krow_a) * KP + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * s);
+        st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[b], 0, 0, 0);
+      }
+    }
+    if ((j + 1) * BN > nk) {
+      // mask keys past the end: accumulator row i holds key 32 b + perm(i)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (j * BN + 32 * b + k_row_perm(i) >= nk) st[b][r] = -INFINITY;
+        }
+    }
+
+    float mx = st[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[b][r]);
+    mx = swap_halves_max(mx);
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+
+    // P^T fragments: ks = 2 b + half, elements r = 8 half .. 8 half + 7.
+    bf16x8_t pf[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e], c2, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e + 1], c2, -m_new));
+          psum += p0 + p1;
+          w[e] = pack_bf16(p0, p1);
+        }
+        pf[2 * b + half] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    l_run += psum;
+
+    // O^T[d][query] += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* vp0 = vb + (16 * ks + vrow_a) * VP + 32 * db + vcol_a;
+        const s16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp0));
+        const s16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp0 + 4 * VP));
+        const s16x8_t a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pf[ks],
+                                                       o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  const float lt = swap_halves_sum(l_run);
+  if (qrow < nq) {
+    const float inv = 1.f / lt;
+    uint16_t* op = out + qrow * rs + head * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t w0 = pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+        const uint32_t w1 = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * g) = make_uint2(w0, w1);
+      }
+    if (lse != nullptr && hh == 0)
+      lse[(int64_t)head * nq + qrow] = (m_run + __log2f(lt)) * 0.69314718055994531f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
+                            int nk, int heads, float scale, hipStream_t s) {
+  const int qtiles = (nq + BM - 1) / BM;
+  const float c2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
+                     nk, heads, c2, qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace la

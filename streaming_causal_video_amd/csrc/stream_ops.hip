@@ -1,0 +1,119 @@
+// HBM-bound streaming kernels: cache append / sink replacement copies and the
+// flow-matching Euler update, for gfx950.
+//
+// Cache append (gitcode.csdn.net "Live Avatar 深度解析…", 疑问 4: the cache
+// stores the K/V of the step's own noisy x_t with no refresh pass) and the
+// one-time sink replacement (papernotes.org "Live Avatar: Streaming Real-time
+// Audio-Driven Avatar Generation with Infinite Length", 关键设计 3) are plain
+// byte copies of two tensors (K and V) in one launch.  The Euler update follows
+// the flow-matching velocity of the same notes' 损失函数 section:
+// x <- x + dt * v, one fused multiply-add per element.
+//
+// Both kernels move 16-byte vectors, several per thread with all loads issued
+// before the first store, so each wave keeps 4 KiB in flight.
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void copy2_kernel(u32x4_t* __restrict__ d0,
+                                                         const u32x4_t* __restrict__ s0,
+                                                         u32x4_t* __restrict__ d1,
+                                                         const u32x4_t* __restrict__ s1,
+                                                         int64_t n16) {
+  const u32x4_t* src = blockIdx.y ? s1 : s0;
+  u32x4_t* dst = blockIdx.y ? d1 : d0;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  u32x4_t r[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n16) r[u] = __builtin_nontemporal_load(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n16) __builtin_nontemporal_store(r[u], dst + i);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void euler_vec_kernel(float4* __restrict__ x,
+                                                             const float4* __restrict__ v,
+                                                             int64_t n4, float* __restrict__ xt,
+                                                             const float* __restrict__ vt,
+                                                             int tail, float dt) {
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  float4 a[kUnroll], b[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n4) {
+      a[u] = x[i];
+      b[u] = v[i];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n4) {
+      float4 y;
+      y.x = fmaf(dt, b[u].x, a[u].x);
+      y.y = fmaf(dt, b[u].y, a[u].y);
+      y.z = fmaf(dt, b[u].z, a[u].z);
+      y.w = fmaf(dt, b[u].w, a[u].w);
+      x[i] = y;
+    }
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < tail) {
+    xt[threadIdx.x] = fmaf(dt, vt[threadIdx.x], xt[threadIdx.x]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void euler_scalar_kernel(float* __restrict__ x,
+                                                                const float* __restrict__ v,
+                                                                int64_t n, float dt) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads)
+    x[i] = fmaf(dt, v[i], x[i]);
+}
+
+}  // namespace
+
+hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size_t bytes,
+                        hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t per_wg = kThreads * kUnroll;
+  dim3 grid((unsigned)((n16 + per_wg - 1) / per_wg), d1 ? 2 : 1);
+  hipLaunchKernelGGL(copy2_kernel, grid, dim3(kThreads), 0, s, static_cast<u32x4_t*>(d0),
+                     static_cast<const u32x4_t*>(s0), static_cast<u32x4_t*>(d1),
+                     static_cast<const u32x4_t*>(s1), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)v % 16 == 0);
+  if (aligned) {
+    const int64_t n4 = n / 4;
+    const int tail = (int)(n - 4 * n4);
+    const int64_t per_wg = kThreads * kUnroll;
+    const int64_t wgs = n4 > 0 ? (n4 + per_wg - 1) / per_wg : 1;
+    hipLaunchKernelGGL(euler_vec_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s,
+                       reinterpret_cast<float4*>(x), reinterpret_cast<const float4*>(v), n4,
+                       x + 4 * n4, v + 4 * n4, tail, dt);
+  } else {
+    int64_t wgs = (n + kThreads - 1) / kThreads;
+    if (wgs > 65536) wgs = 65536;
+    hipLaunchKernelGGL(euler_scalar_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, x, v, n,
+                       dt);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace la

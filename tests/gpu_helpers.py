@@ -1,0 +1,134 @@
+"""Helpers for GPU parity tests: upload seeded inputs, drive one streamed layer
+through the C ABI, compare with tolerances."""
+
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+import seeded_inputs as si
+
+THETA = 10000.0
+FRAMES_PER_BLOCK = 3
+SINK_DELTA = -1          # sink one latent frame before the block's first frame
+NOISE_LEVEL = 0.75       # this stage's t_i (stage t_3 -> t_2 of the 4-step grid)
+
+# Tolerances stated for the path: bf16 attention vs the float64 oracle.
+ATTN_MAX_ABS = 2e-2
+ATTN_REL_L2 = 5e-3
+F32_MAX_ABS = 1e-5
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def to_dev(st: si.Stored):
+    t = torch()
+    if st.dtype == "bf16":
+        return t.from_numpy(np.array(st.storage).view(np.int16)).cuda().view(t.bfloat16)
+    return t.from_numpy(np.array(st.storage)).cuda()
+
+
+def to_f64(x) -> np.ndarray:
+    return x.detach().double().cpu().numpy()
+
+
+def bf16_bits(x) -> np.ndarray:
+    t = torch()
+    return x.detach().contiguous().view(t.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def check_attention(got: np.ndarray, ref: np.ndarray, what: str) -> None:
+    err = np.abs(got - ref)
+    r = rel_l2(got, ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert err.max() <= ATTN_MAX_ABS and r <= ATTN_REL_L2, \
+        f"{what}: max-abs {err.max():.3e} (<= {ATTN_MAX_ABS}), rel-L2 {r:.3e} (<= {ATTN_REL_L2})"
+
+
+def block_f0(block: int) -> int:
+    return FRAMES_PER_BLOCK * (block - 1)
+
+
+class GpuLayerStream:
+    """One layer of the stage streamed block by block through the C ABI.
+
+    Per block b: la_rope3d_rolling (Q, K at f0(b); raw sink K at f0(b)+delta),
+    la_block_attn_fwd, la_kvcache_append_evict, and after block 1 la_sink_replace
+    with the first latent frame of block 1's raw K and V.
+    """
+
+    def __init__(self, shape: si.LayerShape, layer: int = 0, keep_lse: bool = False):
+        import streaming_causal_video_amd as L
+        t = torch()
+        self.L = L
+        self.shape = shape
+        self.layer = layer
+        self.dtype = t.bfloat16 if shape.dtype == "bf16" else t.float32
+        s = shape
+        self.ring = L.KVRing(s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, self.dtype,
+                             NOISE_LEVEL)
+        sk, sv = s.initial_sink(layer)
+        self.ring.sink_k_raw.copy_(to_dev(sk))
+        self.ring.sink_v.copy_(to_dev(sv))
+        nbytes = L.la_rope_table_bytes(s.Hl, s.Wl, s.head_dim)
+        self.table = t.empty(nbytes // 4, dtype=t.float32, device="cuda")
+        L.la_rope_table_fill(self.table, s.Hl, s.Wl, s.head_dim, THETA)
+        blk = (s.block_tokens, s.heads, s.head_dim)
+        self.q_rot = t.empty(blk, dtype=self.dtype, device="cuda")
+        self.k_rot = t.empty_like(self.q_rot)
+        self.sink_k_rot = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=self.dtype,
+                                  device="cuda")
+        self.out = t.empty_like(self.q_rot)
+        self.lse = t.empty((s.heads, s.block_tokens), dtype=t.float32, device="cuda") if keep_lse else None
+        self._dev = {}
+
+    def block_dev(self, block: int):
+        e = self.shape.entry(block)
+        if e not in self._dev:
+            self._dev[e] = tuple(to_dev(x) for x in self.shape.block_inputs(self.layer, block))
+        return self._dev[e]
+
+    def step(self, block: int):
+        L, s = self.L, self.shape
+        q, k, v = self.block_dev(block)
+        f0 = block_f0(block)
+        L.la_rope3d_rolling(q, self.q_rot, k, self.k_rot, FRAMES_PER_BLOCK, f0,
+                            self.ring.sink_k_raw, self.sink_k_rot, SINK_DELTA, self.table, s.Hl,
+                            s.Wl, s.heads, s.head_dim, THETA)
+        L.la_block_attn_fwd(self.ring.state, self.q_rot, self.sink_k_rot, self.k_rot, v, self.out,
+                            self.lse)
+        ev = L.la_kvcache_append_evict(self.ring.state, self.k_rot, v, block, NOISE_LEVEL)
+        if block == 1:
+            n = s.sink_tokens
+            L.la_sink_replace(self.ring.state, k[:n], v[:n])
+        return ev
+
+
+@functools.lru_cache(maxsize=None)
+def gpu_available() -> bool:
+    try:
+        t = torch()
+        return t.cuda.is_available()
+    except Exception:
+        return False
