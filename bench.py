@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Throughput of the streaming timestep-forcing denoise step on one MI355X.
+
+Default workload (one "step" = one block through one denoise stage): 40 layers,
+each with its own bf16 KV ring (window 4 blocks) and 1560-token sink, each layer
+running 3D Rolling RoPE (Q, K, sink K), block attention 40 heads x 128 over
+Nq = 4680 query tokens and Nk = 1560 + 4*4680 + 4680 = 24960 keys, and the ring
+append/evict; then one flow-matching Euler update (dt = -0.25) of a
+16x3x60x104 fp32 latent.  Steady state: blocks >= 5 (ring full).  The
+one-time sink replacement happens in warm-up at block 1.
+
+All inputs are synthetic N(0,1) tensors resident in HBM before the timed
+region (there are no trained weights).  One JSON line goes to stdout; progress
+goes to stderr.
+
+Other workloads (--workload): c2 (one 40x128 layer, attention timed alone),
+c5 (720p-shaped layer, 44x80 tokens per frame, streamed for 1000 blocks:
+sustained blocks/s and cache-update GB/s).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "block-attn TFLOP/s + denoise-step blocks/s at 1 GPU; % bf16 MFMA / HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FRAMES = 3
+DELTA = -1
+THETA = 10000.0
+NOISE = 0.75
+DT = -0.25
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attn_flops(nq, nk, d, h):
+    return 4.0 * nq * nk * d * h
+
+
+# --------------------------------------------------------------------------- GPU
+def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
+    import torch
+    import streaming_causal_video_amd as L
+
+    L.lib()
+    dev = "cuda"
+    bt, st = FRAMES * Hl * Wl, Hl * Wl
+    nk = st + (W + 1) * bt
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    def randn(shape, dtype=torch.bfloat16):
+        return torch.randn(shape, device=dev, dtype=torch.float32, generator=gen).to(dtype)
+
+    log(f"setup: {n_layers} layers, Hl={Hl} Wl={Wl} W={W} H={H} d={d}, Nq={bt} Nk={nk}")
+    stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, NOISE)
+    for l in range(n_layers):
+        stack.sink_k_raw[l].copy_(randn((st, H, d)))
+        stack.sink_v[l].copy_(randn((st, H, d)))
+    pool = 2
+    ins = [[tuple(randn((bt, H, d)) for _ in range(3)) for _ in range(n_layers)] for _ in range(pool)]
+    outs = [torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
+    qws = torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev)
+    kws = torch.empty_like(qws)
+    sws = torch.empty((st, H, d), dtype=torch.bfloat16, device=dev)
+    table = torch.empty(L.la_rope_table_bytes(Hl, Wl, d) // 4, dtype=torch.float32, device=dev)
+    L.la_rope_table_fill(table, Hl, Wl, d, THETA)
+    lat_shape = (16, 3, 60, 104)
+    x = torch.randn(lat_shape, device=dev, generator=gen) if with_euler else None
+    vels = [torch.randn(lat_shape, device=dev, generator=gen) for _ in range(pool)] if with_euler else None
+    torch.cuda.synchronize()
+
+    def step(b, events=None):
+        e = b % pool
+        q = [ins[e][l][0] for l in range(n_layers)]
+        k = [ins[e][l][1] for l in range(n_layers)]
+        v = [ins[e][l][2] for l in range(n_layers)]
+        skn = [t[:st] for t in k] if b == 1 else None
+        svn = [t[:st] for t in v] if b == 1 else None
+        L.la_denoise_step(stack.states, b, q, k, v, outs, qws, kws, sws, table, Hl, Wl, FRAMES,
+                          DELTA, THETA, sink_k_new=skn, sink_v_new=svn, x=x,
+                          vel=vels[e] if with_euler else None, dt=DT, timing_events=events)
+
+    # warm-up: block 1 (sink replacement) .. the ring is full after block W
+    block = 0
+    for _ in range(W + args.warmup):
+        block += 1
+        step(block)
+    torch.cuda.synchronize()
+    log(f"warm-up done ({block} blocks)")
+
+    nev = 6 * n_layers + 2
+    ev_objs = []
+    ev_arrays = []
+    for _ in range(args.steps):
+        objs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+        for o in objs:
+            o.record()  # creates the underlying HIP event
+        arr = (ctypes.c_void_p * nev)(*[o.cuda_event for o in objs])
+        ev_objs.append(objs)
+        ev_arrays.append(arr)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        block += 1
+        step(block, ev_arrays[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+
+    def avg(off):
+        vals = [objs[6 * l + off].elapsed_time(objs[6 * l + off + 1])
+                for objs in ev_objs for l in range(n_layers)]
+        return float(np.mean(vals)), float(np.std(vals))
+
+    rope_ms, _ = avg(0)
+    attn_ms, attn_sd = avg(2)
+    app_ms, _ = avg(4)
+    eul = [objs[6 * n_layers].elapsed_time(objs[6 * n_layers + 1]) for objs in ev_objs]
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall / args.steps * 1e3:.3f} ms/step)")
+    fl = attn_flops(bt, nk, d, H)
+    rope_bytes = 2 * (2 * bt + st) * H * d * 2
+    app_bytes = 2 * 2 * bt * H * d * 2
+    res = {
+        "ms_per_step": ms_step,
+        "blocks_per_s": 1e3 / ms_step,
+        "attn_ms": attn_ms, "attn_ms_sd": attn_sd,
+        "attn_tflops": fl / (attn_ms * 1e-3) / 1e12,
+        "attn_flop_per_launch": fl,
+        "rope_us": rope_ms * 1e3, "rope_gbs": rope_bytes / (rope_ms * 1e-3) / 1e9,
+        "rope_bytes": rope_bytes,
+        "append_us": app_ms * 1e3, "append_gbs": app_bytes / (app_ms * 1e-3) / 1e9,
+        "append_bytes": app_bytes,
+        "euler_us": float(np.mean(eul)) * 1e3,
+        "nq": bt, "nk": nk,
+    }
+    return res
+
+
+# --------------------------------------------------------------------------- oracle on host cores
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(Hl, Wl, W, H, d, n_layers, budget_s=15.0):
+    """Time the float64 oracle on this host on a bounded sample of one step:
+    (layer, head) units of RoPE + attention + append, extrapolated to all
+    n_layers x H units, plus the Euler update on the whole latent."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import Ring, attention_lse, euler_step, rope3d
+
+    rng = np.random.default_rng(0)
+    bt, st = FRAMES * Hl * Wl, Hl * Wl
+    q = rng.standard_normal((bt, 1, d))
+    k = rng.standard_normal((bt, 1, d))
+    v = rng.standard_normal((bt, 1, d))
+    sk = rng.standard_normal((st, 1, d))
+    sv = rng.standard_normal((st, 1, d))
+    cached_k = [rng.standard_normal((bt, 1, d)) for _ in range(W)]
+    cached_v = [rng.standard_normal((bt, 1, d)) for _ in range(W)]
+    f0 = FRAMES * 100
+    units = 0
+    t_start = time.perf_counter()
+    while True:
+        ring = Ring(W, NOISE)
+        for i in range(W):
+            ring.append(i + 1, cached_k[i], cached_v[i], NOISE)
+        qr = rope3d(q, FRAMES, Hl, Wl, f0, THETA)
+        kr = rope3d(k, FRAMES, Hl, Wl, f0, THETA)
+        skr = rope3d(sk, 1, Hl, Wl, f0 + DELTA, THETA)
+        ck, cv = ring.keys_values()
+        attention_lse(qr, np.concatenate([skr, *ck, kr]), np.concatenate([sv, *cv, v]), d ** -0.5)
+        ring.append(W + 1, kr, v, NOISE)
+        units += 1
+        if time.perf_counter() - t_start >= budget_s or units >= n_layers * H:
+            break
+    t_units = (time.perf_counter() - t_start) / units
+    lat = rng.standard_normal((16, 3, 60, 104)).astype(np.float32)
+    vel = rng.standard_normal((16, 3, 60, 104)).astype(np.float32)
+    te = time.perf_counter()
+    euler_step(lat, vel, DT).astype(np.float32)
+    t_euler = time.perf_counter() - te
+    t_step = t_units * n_layers * H + t_euler
+    return {
+        "value": 1.0 / t_step,
+        "unit": "blocks/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{units} of {n_layers * H} (layer, head) units of one step "
+                   f"(RoPE of Q, K, sink K + fp64 attention over {bt} x "
+                   f"{st + (W + 1) * bt} keys + ring append), timed "
+                   f"{t_units * units:.1f} s and scaled x{n_layers * H / units:.0f}; Euler on the "
+                   f"whole latent timed once"),
+        "seconds_per_step_extrapolated": t_step,
+        "host_cpus": os.cpu_count(),
+        "host_affinity": len(os.sched_getaffinity(0)),
+    }
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", choices=["c4", "c2", "c5"], default="c4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU's stage only (asked for {args.gpus} GPUs); the multi-GPU "
+              "pipeline is not part of this build.", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-process; WORLD_SIZE > 1 is not supported.", file=sys.stderr)
+        return 2
+
+    if args.workload == "c4":
+        geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
+        name = ("C4 full denoise step: 40 layers x (3D Rolling RoPE + bf16 block attention "
+                "40x128, Nq 4680, Nk 24960 + ring append/evict, W=4, 1560-token sink) + "
+                "flow-matching Euler on fp32 16x3x60x104")
+    elif args.workload == "c2":
+        geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=1)
+        name = "C2 one layer: bf16 block attention 40x128, Nq 4680, Nk 24960 (+RoPE, append, Euler)"
+    else:
+        geo = dict(Hl=44, Wl=80, W=4, H=40, d=128, n_layers=1)
+        name = ("C5 720p-shaped layer: 44x80 tokens/frame, Nq 10560, Nk 56320 (sink + 4 cached "
+                "blocks + block), streamed blocks")
+        if args.steps == 10:
+            args.steps = 1000
+    r = gpu_step_bench(args, **geo)
+    peak_frac = r["attn_tflops"] / PEAK_BF16_TFLOPS
+    out = {
+        "metric": METRIC,
+        "value": round(r["blocks_per_s"], 4),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) Q/K/V, sinks, latent and velocity resident in HBM (no trained weights)",
+        "config": {"workload": name, "layers": geo["n_layers"], "heads": geo["H"],
+                   "head_dim": geo["d"], "block_tokens": r["nq"], "sink_tokens": geo["Hl"] * geo["Wl"],
+                   "window_blocks": geo["W"], "nk": r["nk"], "parallelism": "none (1 GPU = 1 stage)"},
+        "attn_tflops": round(r["attn_tflops"], 2),
+        "attn_ms": round(r["attn_ms"], 4),
+        "roofline": {"bound": "mfma", "achieved": round(r["attn_tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(peak_frac, 4),
+                     "traffic": None, "kernel": "attn_bf16_kernel",
+                     "flop_per_launch": r["attn_flop_per_launch"]},
+        "streaming_kernels": {
+            "rope_us": round(r["rope_us"], 2), "rope_GBps": round(r["rope_gbs"], 1),
+            "rope_frac_hbm": round(r["rope_gbs"] / PEAK_HBM_GBS, 4),
+            "append_us": round(r["append_us"], 2), "append_GBps": round(r["append_gbs"], 1),
+            "append_frac_hbm": round(r["append_gbs"] / PEAK_HBM_GBS, 4),
+            "euler_us": round(r["euler_us"], 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on host cores ...")
+        out["cpu_baseline"] = cpu_baseline(geo["Hl"], geo["Wl"], geo["W"], geo["H"], geo["d"],
+                                           geo["n_layers"], args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -258,6 +258,11 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *                            block_tokens must equal frames_per_block*Hl*Wl and
  *                            sink_tokens Hl*Wl.
  *   scale                  : softmax scale (1/sqrt(head_dim) for the model).
+ *   timing_events          : NULL, or 6*n_layers + 2 caller-created hipEvent_t
+ *                            (as void*) recorded on `stream` around each layer's
+ *                            RoPE [6l, 6l+1], attention [6l+2, 6l+3] and append
+ *                            (+ sink replacement) [6l+4, 6l+5], and around the
+ *                            Euler update [6n, 6n+1]; for measuring kernels in place.
  * The whole step is validated before the first launch; on an error nothing is
  * enqueued and no ring changes.  Pointer arrays are host memory read at call
  * time.
@@ -269,7 +274,8 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                           int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
                           double theta, float scale, float* x, const float* vel,
-                          int64_t n_latent, float dt, la_stream_t stream);
+                          int64_t n_latent, float dt, void* const* timing_events,
+                          la_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -92,7 +92,7 @@ def _load():
         "la_fm_euler_step": (ctypes.c_int, [VP, VP, I64, F, VP]),
         "la_denoise_step": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP, VP,
                                            P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, VP,
-                                           I64, F, VP]),
+                                           I64, F, P(VP), VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -261,9 +261,11 @@ def _ptr_array(ts, name):
 def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_ws, k_rot_ws,
                     sink_k_rot_ws, rope_table, Hl: int, Wl: int, frames_per_block: int = 3,
                     sink_delta: int = -1, theta: float = 10000.0, scale: Optional[float] = None,
-                    sink_k_new=None, sink_v_new=None, x=None, vel=None, dt: float = -0.25) -> None:
+                    sink_k_new=None, sink_v_new=None, x=None, vel=None, dt: float = -0.25,
+                    timing_events=None) -> None:
     """rings: a ctypes array of la_kvring (see KVRingStack); the other per-layer
-    arguments are lists of tensors."""
+    arguments are lists of tensors.  timing_events: None or a ctypes array of
+    6*len(rings)+2 raw hipEvent_t handles."""
     n = len(rings)
     if scale is None:
         scale = rings[0].head_dim ** -0.5
@@ -277,7 +279,7 @@ def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_w
         _ptr_array(v_raw, "v_raw"), _ptr_array(attn_out, "attn_out"), _ptr(q_rot_ws, "q_rot_ws"),
         _ptr(k_rot_ws, "k_rot_ws"), _ptr(sink_k_rot_ws, "sink_k_rot_ws"), skn, svn,
         _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta, scale,
-        _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, _stream()), "la_denoise_step")
+        _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, timing_events, _stream()), "la_denoise_step")
 
 
 # ---------------------------------------------------------------- one layer's cache

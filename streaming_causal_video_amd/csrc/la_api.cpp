@@ -273,7 +273,8 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                           int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
                           double theta, float scale, float* x, const float* vel,
-                          int64_t n_latent, float dt, la_stream_t stream) {
+                          int64_t n_latent, float dt, void* const* timing_events,
+                          la_stream_t stream) {
   // ---- validate the whole step before enqueuing anything
   if (!rings || n_layers < 1 || !q_raw || !k_raw || !v_raw || !attn_out || !q_rot_ws ||
       !k_rot_ws || !sink_k_rot_ws || !rope_table)
@@ -298,17 +299,35 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
       return LA_ERR_INVALID_ARG;
   }
   if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
+  if (timing_events)
+    for (int i = 0; i < 6 * n_layers + 2; ++i)
+      if (!timing_events[i]) return LA_ERR_INVALID_ARG;
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> la_status {
+    if (!timing_events) return LA_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(timing_events[i]), hs));
+  };
+#define LA_TRY(expr)                 \
+  do {                               \
+    const la_status st_ = (expr);    \
+    if (st_ != LA_OK) return st_;    \
+  } while (0)
   // ---- enqueue
   for (int l = 0; l < n_layers; ++l) {
     la_kvring* r = &rings[l];
+    LA_TRY(mark(6 * l));
     la_status st = la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
                                      r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
                                      r->heads, r->head_dim, (la_dtype)r->dtype, theta, stream);
     if (st != LA_OK) return st;
+    LA_TRY(mark(6 * l + 1));
+    LA_TRY(mark(6 * l + 2));
     st = la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot_ws, v_raw[l], r->block_tokens,
                            attn_out[l], nullptr, scale, stream);
     if (st != LA_OK) return st;
+    LA_TRY(mark(6 * l + 3));
+    LA_TRY(mark(6 * l + 4));
     st = la_kvcache_append_evict(r, k_rot_ws, v_raw[l], block_id, r->noise_level, nullptr,
                                  stream);
     if (st != LA_OK) return st;
@@ -316,8 +335,12 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
       st = la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream);
       if (st != LA_OK) return st;
     }
+    LA_TRY(mark(6 * l + 5));
   }
-  if (x && n_latent > 0) return la_fm_euler_step(x, vel, n_latent, dt, stream);
+  LA_TRY(mark(6 * n_layers));
+  if (x && n_latent > 0) LA_TRY(la_fm_euler_step(x, vel, n_latent, dt, stream));
+  LA_TRY(mark(6 * n_layers + 1));
+#undef LA_TRY
   return LA_OK;
 }
 

@@ -54,6 +54,21 @@ def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     return np.abs(ordered(a_bits) - ordered(b_bits))
 
 
+def check_rope_bf16(got_bits: np.ndarray, exact: np.ndarray, raw: np.ndarray, what: str) -> None:
+    """bf16 RoPE bound: within 1 bf16 ulp of the oracle's value rounded to nearest even,
+    or, where the rotation cancels, within half an ulp plus the float32 arithmetic bound
+    2**-21 * |(x, y)| of the pair (cos/sin rounded to float32, one product rounded, one
+    fused multiply-add: about 3 * 2**-24 * (|x| + |y|))."""
+    d = bf16_ulp_distance(got_bits, si.f64_to_bf16_bits(exact))
+    pair = np.sqrt(raw[..., 0::2] ** 2 + raw[..., 1::2] ** 2)
+    pair = np.repeat(pair, 2, axis=-1)
+    got = si.bf16_bits_to_f64(got_bits)
+    mag = np.maximum(np.abs(exact), 1e-300)
+    half_ulp = np.ldexp(1.0, np.floor(np.log2(mag)).astype(np.int64) - 8)
+    ok = (d <= 1) | (np.abs(got - exact) <= half_ulp + 2.0 ** -21 * pair)
+    assert ok.all(), f"{what}: {int((~ok).sum())} elements outside the bound (max {int(d.max())} ulps)"
+
+
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
 

@@ -7,7 +7,7 @@ import pytest
 import seeded_inputs as si
 from oracle import Ring, euler_step, linear_path_point, rope3d, uniform_grid
 
-from gpu_helpers import (F32_MAX_ABS, NOISE_LEVEL, THETA, bf16_bits, bf16_ulp_distance, say,
+from gpu_helpers import (F32_MAX_ABS, NOISE_LEVEL, THETA, bf16_bits, check_rope_bf16, say,
                          to_dev, to_f64, torch)
 
 pytestmark = pytest.mark.gpu
@@ -95,10 +95,7 @@ def _rope_case(L, shape, f0, delta=-1, heads=None, inplace=False):
                                     ("sink", sk, sko, 1, f0 + delta)):
         ref = rope3d(raw.values[:, hs, :], nf, s.Hl, s.Wl, pos, THETA)
         if s.dtype == "bf16":
-            got_bits = bf16_bits(out)[:, hs, :]
-            ref_bits = si.f64_to_bf16_bits(ref)
-            d = bf16_ulp_distance(got_bits, ref_bits)
-            assert d.max() <= 1, f"{name}: {int(d.max())} bf16 ulps"
+            check_rope_bf16(bf16_bits(out)[:, hs, :], ref, raw.values[:, hs, :], name)
         else:
             err = np.abs(to_f64(out)[:, hs, :] - ref).max()
             assert err <= F32_MAX_ABS, f"{name}: max-abs {err:.3e}"

@@ -1,0 +1,156 @@
+"""Long streams and the whole-stage step driver on the GPU, against the float64 oracle."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import StreamOracle, euler_step
+
+from gpu_helpers import (FRAMES_PER_BLOCK, NOISE_LEVEL, SINK_DELTA, THETA, GpuLayerStream,
+                         check_attention, say, to_dev, to_f64, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    import streaming_causal_video_amd as lib
+    lib.lib()
+    return lib
+
+
+@pytest.mark.timeout(900)
+def test_c3_200_blocks_checked_at_1_50_200(L):
+    """40x128 layer, window 8 (Nk 43680 in steady state), 200 streamed blocks with
+    Rolling-RoPE re-offset, append/evict and the sink replacement after block 1."""
+    t = torch()
+    shape = si.C3
+    gs = GpuLayerStream(shape)
+    orc = StreamOracle(shape, heads=[0, 39])
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 4679], rng.integers(0, shape.block_tokens, 64)]))
+    for b in range(1, 201):
+        gs.step(b)
+        if b in (1, 50, 200):
+            say(f"C3 block {b}")
+            t.cuda.synchronize()
+            got = to_f64(gs.out)[rows][:, orc.heads, :]
+            ref = orc.block_output(b, rows=rows)
+            check_attention(got, ref, f"C3 block {b}")
+            ids = sorted(int(x) for x in gs.ring.slot_ids() if x)
+            assert ids == list(range(max(1, b - shape.W + 1), b + 1))
+
+
+def _stage(L, shape, n_layers):
+    t = torch()
+    s = shape
+    stack = L.KVRingStack(n_layers, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim,
+                          t.bfloat16 if s.dtype == "bf16" else t.float32, NOISE_LEVEL)
+    for l in range(n_layers):
+        sk, sv = s.initial_sink(l)
+        stack.sink_k_raw[l].copy_(to_dev(sk))
+        stack.sink_v[l].copy_(to_dev(sv))
+    table = t.empty(L.la_rope_table_bytes(s.Hl, s.Wl, s.head_dim) // 4, dtype=t.float32,
+                    device="cuda")
+    L.la_rope_table_fill(table, s.Hl, s.Wl, s.head_dim, THETA)
+    return stack, table
+
+
+def test_denoise_step_matches_oracle_and_per_op_path(L):
+    """la_denoise_step over 3 layers and 6 blocks: each layer's attention equals the
+    per-op C-ABI path bit for bit and the oracle within tolerance; the latent takes
+    one Euler step per block."""
+    t = torch()
+    shape = si.MID_BF16
+    s = shape
+    n_layers = 3
+    stack, table = _stage(L, shape, n_layers)
+    blk = (s.block_tokens, s.heads, s.head_dim)
+    outs = [t.empty(blk, dtype=t.bfloat16, device="cuda") for _ in range(n_layers)]
+    qws, kws = t.empty(blk, dtype=t.bfloat16, device="cuda"), t.empty(blk, dtype=t.bfloat16, device="cuda")
+    sws = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+    per_op = [GpuLayerStream(shape, layer=l) for l in range(n_layers)]
+    oracles = [StreamOracle(shape, layer=l) for l in range(n_layers)]
+    lat = si.latent(102, 0, si.TID_X, si.C4_LATENT_SHAPE)
+    x = to_dev(lat)
+    x_ref = lat.values.copy()
+    for b in range(1, 7):
+        ins = [s.block_inputs(l, b) for l in range(n_layers)]
+        dev = [tuple(to_dev(z) for z in trip) for trip in ins]
+        vel = si.latent(102, b, si.TID_VEL, si.C4_LATENT_SHAPE)
+        veld = to_dev(vel)
+        nsink = s.sink_tokens
+        L.la_denoise_step(
+            stack.states, b, [d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev], outs,
+            qws, kws, sws, table, s.Hl, s.Wl, FRAMES_PER_BLOCK, SINK_DELTA, THETA,
+            sink_k_new=[d[1][:nsink] for d in dev] if b == 1 else None,
+            sink_v_new=[d[2][:nsink] for d in dev] if b == 1 else None,
+            x=x, vel=veld, dt=-0.25)
+        x_ref = euler_step(x_ref, vel.values, -0.25).astype(np.float32).astype(np.float64)
+        for l in range(n_layers):
+            per_op[l].step(b)
+        t.cuda.synchronize()
+        for l in range(n_layers):
+            assert t.equal(outs[l].view(t.int16), per_op[l].out.view(t.int16)), (b, l)
+            if b in (1, 2, 6):
+                check_attention(to_f64(outs[l]), oracles[l].block_output(b), f"layer {l} block {b}")
+        np.testing.assert_array_equal(x.cpu().numpy(), x_ref.astype(np.float32))
+    for l in range(n_layers):
+        assert stack.states[l].last_block == 6 and stack.states[l].sink_replaced == 1
+
+
+def test_denoise_step_refuses_before_any_launch(L):
+    t = torch()
+    shape = si.SMALL_BF16
+    s = shape
+    stack, table = _stage(L, shape, 2)
+    blk = (s.block_tokens, s.heads, s.head_dim)
+    z = [t.zeros(blk, dtype=t.bfloat16, device="cuda") for _ in range(2)]
+    ws = t.empty(blk, dtype=t.bfloat16, device="cuda")
+    sws = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+    before = [bytes(stack.states[l]) for l in range(2)]
+    with pytest.raises(L.LAError):  # block 2 before block 1
+        L.la_denoise_step(stack.states, 2, z, z, z, [ws, ws], ws, ws, sws, table, s.Hl, s.Wl)
+    with pytest.raises(L.LAError):  # wrong frame geometry
+        L.la_denoise_step(stack.states, 1, z, z, z, [ws, ws], ws, ws, sws, table, s.Hl + 1, s.Wl)
+    stack.states[1].noise_level = 0.5  # layers disagree on the noise level
+    with pytest.raises(L.LAError):
+        L.la_denoise_step(stack.states, 1, z, z, z, [ws, ws], ws, ws, sws, table, s.Hl, s.Wl)
+    stack.states[1].noise_level = NOISE_LEVEL
+    assert [bytes(stack.states[l]) for l in range(2)] == before
+
+
+def test_checkpoint_restore_continues_bit_identically(L):
+    """A stage's resumable state is the ring/sink index struct plus the device buffers;
+    restoring it after block 4 and continuing gives the same bits as never stopping."""
+    t = torch()
+    shape = si.MID_BF16
+    a = GpuLayerStream(shape)
+    for b in range(1, 5):
+        a.step(b)
+    t.cuda.synchronize()
+    saved_struct = bytes(a.ring.state)
+    saved = [x.clone() for x in (a.ring.k_slots, a.ring.v_slots, a.ring.sink_k_raw, a.ring.sink_v)]
+    for b in range(5, 9):
+        a.step(b)
+    t.cuda.synchronize()
+    ref_out = a.out.clone()
+    ref_slots = a.ring.k_slots.clone()
+
+    bstream = GpuLayerStream(shape)
+    for dst, src in zip((bstream.ring.k_slots, bstream.ring.v_slots, bstream.ring.sink_k_raw,
+                         bstream.ring.sink_v), saved):
+        dst.copy_(src)
+    ctypes.memmove(ctypes.addressof(bstream.ring.state), saved_struct, len(saved_struct))
+    # the struct holds device pointers: point them at the new buffers
+    bstream.ring.state.k_slots = bstream.ring.k_slots.data_ptr()
+    bstream.ring.state.v_slots = bstream.ring.v_slots.data_ptr()
+    bstream.ring.state.sink_k_raw = bstream.ring.sink_k_raw.data_ptr()
+    bstream.ring.state.sink_v = bstream.ring.sink_v.data_ptr()
+    for b in range(5, 9):
+        bstream.step(b)
+    t.cuda.synchronize()
+    assert t.equal(bstream.out.view(t.int16), ref_out.view(t.int16))
+    assert t.equal(bstream.ring.k_slots.view(t.int16), ref_slots.view(t.int16))
