@@ -25,6 +25,11 @@ ARCH = "gfx950"
 
 SOURCES = ["la_api.cpp", "rope.hip", "stream_ops.hip", "attn_bf16.hip", "attn_f32.hip"]
 
+# Per-source extra flags.  The bf16 attention never sees NaN inputs, so it is
+# built without NaN-quieting semantics: fmaxf then maps to bare v_max/v_max3
+# instead of canonicalising every operand first.
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
 # hipcc flags.  Packed-fp32 instruction selection is switched off for device code.
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -44,7 +49,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

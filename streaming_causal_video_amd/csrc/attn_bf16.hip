@@ -26,7 +26,16 @@
 //    the gfx950 LDS transpose read ds_read_b64_tr_b16.
 //  * Online softmax in float32 with the scale folded into a base-2 exponent
 //    (one FMA and one v_exp_f32 per score); P is rounded to bf16 for the second
-//    product with v_cvt_pk_bf16_f32.
+//    product with v_cvt_pk_bf16_f32, and the row sum is taken from those same
+//    bf16 pairs with v_dot2c_f32_bf16 (two scores per instruction, consistent
+//    with the P V product it normalises).
+//  * Lazy rescaling: the running max is only raised when a tile's max exceeds
+//    it by more than 2^8 (in exp2 units), so O and the row sum are rescaled on
+//    a handful of tiles instead of every tile.  Exact: numerator and
+//    denominator use the same reference max; P stays <= 256.
+//  * Loader: per-thread 32-bit row offsets are computed once; per tile only a
+//    scalar segment base changes.  Tiles that straddle a segment boundary or
+//    run past the last key take a slower per-row path with zero fill.
 //  * Workgroups are renumbered so that all query tiles of a head run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 while
 //    they stream the head's K/V.
@@ -53,6 +62,7 @@ constexpr int VP = 160;  // V row pitch in LDS (bf16): 320 B, conflict-free tran
 constexpr int KBUF = BN * KP;
 constexpr int VBUF = BN * VP;
 constexpr int STAGE = KBUF + VBUF;
+constexpr float kRescaleSlack = 8.f;  // log2 units: P <= 2^8 between rescales
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2_t f = {lo, hi};
@@ -120,38 +130,37 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const int lcc = tid & 15;
   const int lr0 = tid >> 4;
   const int ntiles = (nk + BN - 1) / BN;
+  const uint32_t rs_bytes = (uint32_t)rs * 2u;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    voff[i] = (uint32_t)(lr0 + 16 * i) * rs_bytes + (uint32_t)(head * D * 2 + lcc * 16);
   uint4 kreg[4], vreg[4];
+  int seg = 0;  // segment holding the first key of the tile being loaded (scalar)
 
   auto gload = [&](int tile) {
     const int t0 = tile * BN;
-    int s0 = 0;
-    while (t0 >= segs.end[s0]) ++s0;
-    const int tend = min(t0 + BN, nk);
-    if (tend <= segs.end[s0]) {
-      const int start = s0 ? segs.end[s0 - 1] : 0;
-      const uint16_t* kb = static_cast<const uint16_t*>(segs.k[s0]);
-      const uint16_t* vb = static_cast<const uint16_t*>(segs.v[s0]);
+    while (t0 >= segs.end[seg]) ++seg;
+    const int start = seg ? segs.end[seg - 1] : 0;
+    if (t0 + BN <= segs.end[seg]) {
+      // whole tile inside one segment: scalar base + precomputed 32-bit offsets
+      const uint32_t sbase = (uint32_t)(t0 - start) * rs_bytes;
+      const char* kb = static_cast<const char*>(segs.k[seg]) + sbase;
+      const char* vb = static_cast<const char*>(segs.v[seg]) + sbase;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = t0 + lr0 + 16 * i;
-        if (key < nk) {
-          const int64_t off = (int64_t)(key - start) * rs + head * D + lcc * 8;
-          kreg[i] = *reinterpret_cast<const uint4*>(kb + off);
-          vreg[i] = *reinterpret_cast<const uint4*>(vb + off);
-        } else {
-          kreg[i] = make_uint4(0, 0, 0, 0);
-          vreg[i] = make_uint4(0, 0, 0, 0);
-        }
+        kreg[i] = *reinterpret_cast<const uint4*>(kb + voff[i]);
+        vreg[i] = *reinterpret_cast<const uint4*>(vb + voff[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = t0 + lr0 + 16 * i;
         if (key < nk) {
-          int s = s0;
+          int s = seg;
           while (key >= segs.end[s]) ++s;
-          const int start = s ? segs.end[s - 1] : 0;
-          const int64_t off = (int64_t)(key - start) * rs + head * D + lcc * 8;
+          const int st = s ? segs.end[s - 1] : 0;
+          const int64_t off = (int64_t)(key - st) * rs + head * D + lcc * 8;
           kreg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(segs.k[s]) + off);
           vreg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(segs.v[s]) + off);
         } else {
@@ -176,6 +185,8 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   // transpose-read address pieces for V^T fragments
   const int vrow_a = 8 * hh + ((lane & 15) >> 2);
   const int vcol_a = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   gload(0);
   for (int j = 0; j < ntiles; ++j) {
@@ -185,20 +196,21 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* kb = lds + (j & 1) * STAGE;
     const uint16_t* vb = kb + KBUF;
 
-    // S^T[key][query] for two 32-key blocks.
+    // S^T[key][query] for two 32-key blocks, chains interleaved.
     f32x16_t st[2];
+    st[0] = f32x16_t{};
+    st[1] = f32x16_t{};
+    const uint16_t* kr0 = kb + krow_a * KP + 8 * hh;
+    const uint16_t* kr1 = kr0 + 32 * KP;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      st[b] = f32x16_t{};
-      const uint16_t* kr = kb + (32 * b + krow_a) * KP + 8 * hh;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * s);
-        st[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[b], 0, 0, 0);
-      }
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(kr0 + 16 * s);
+      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(kr1 + 16 * s);
+      st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], st[0], 0, 0, 0);
+      st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], st[1], 0, 0, 0);
     }
     if ((j + 1) * BN > nk) {
-      // mask keys past the end: accumulator row i holds key 32 b + perm(i)
+      // last tile: mask keys past the end (accumulator row i holds key 32 b + perm(i))
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -208,22 +220,23 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
         }
     }
 
-    float mx = st[0][0];
+    float mx = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
+    mx = swap_halves_max(mx) * c2;
+    // raise the reference max only when this tile would push P above 2^8
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[b][r]);
-    mx = swap_halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    }
 
     // P^T fragments: ks = 2 b + half, elements r = 8 half .. 8 half + 7.
     bf16x8_t pf[4];
-    float psum = 0.f;
+    const float nm = -m_run;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -231,14 +244,14 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e], c2, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e + 1], c2, -m_new));
-          psum += p0 + p1;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e], c2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e + 1], c2, nm));
           w[e] = pack_bf16(p0, p1);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[e]), ones,
+                                                  l_run, false);
         }
         pf[2 * b + half] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       }
-    l_run += psum;
 
     // O^T[d][query] += V^T P^T
 #pragma unroll

@@ -186,6 +186,10 @@ la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* s
   const int64_t nk64 = (int64_t)r->sink_tokens + (int64_t)(count + 1) * r->block_tokens;
   if (nk64 > INT32_MAX / 2 || (int64_t)n_q * r->heads * r->head_dim > ((int64_t)1 << 40))
     return LA_ERR_SHAPE;
+  // the bf16 kernel addresses a segment with 32-bit byte offsets
+  const int64_t seg_rows = (r->sink_tokens > r->block_tokens ? r->sink_tokens : r->block_tokens) + 64;
+  if (r->dtype == LA_BF16 && seg_rows * r->heads * r->head_dim * 2 >= ((int64_t)1 << 32))
+    return LA_ERR_SHAPE;
 
   la::AttnSegs segs;
   memset(&segs, 0, sizeof(segs));

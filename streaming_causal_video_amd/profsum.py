@@ -1,0 +1,71 @@
+"""Summarise a rocprofv3 kernel trace: per-kernel dispatch count and durations.
+
+Usage:
+    python -m streaming_causal_video_amd.profsum <results.db | kernel_trace.csv> [--last N]
+
+``--last N`` restricts each kernel to its last N dispatches (the steady-state
+part of a streamed run, after the ring has filled).  Reads the SQLite database
+that rocprofv3 writes by default or the CSV kernel trace of
+``--output-format csv``.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import re
+import sqlite3
+import statistics
+import sys
+
+
+def short_name(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    n = re.sub(r"\(.*", "", n)
+    return n[:60]
+
+
+def load(path: str):
+    """[(kernel name, start_ns, end_ns)] in dispatch order."""
+    if path.endswith(".db"):
+        con = sqlite3.connect(path)
+        rows = con.execute("select name, start, end from kernels order by start").fetchall()
+        return [(r[0], int(r[1]), int(r[2])) for r in rows]
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out.sort(key=lambda t: t[1])
+    return out
+
+
+def summarise(rows, last=None):
+    by = {}
+    for name, s, e in rows:
+        by.setdefault(name, []).append((e - s) / 1e3)
+    res = []
+    for name, d in by.items():
+        sel = d[-last:] if last else d
+        res.append((short_name(name), len(d), len(sel), sum(sel), statistics.mean(sel),
+                    statistics.median(sel), min(sel), max(sel)))
+    res.sort(key=lambda r: -r[3])
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("trace")
+    ap.add_argument("--last", type=int, default=None)
+    a = ap.parse_args(argv)
+    rows = summarise(load(a.trace), a.last)
+    tot = sum(r[3] for r in rows)
+    print(f"{'kernel':60s} {'calls':>6s} {'used':>5s} {'avg_us':>10s} {'median_us':>10s} "
+          f"{'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
+    for n, calls, used, s, avg, med, mn, mx in rows:
+        print(f"{n:60s} {calls:6d} {used:5d} {avg:10.2f} {med:10.2f} {mn:9.2f} {mx:9.2f} "
+              f"{100 * s / tot:6.2f}")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
