@@ -38,6 +38,12 @@ THETA = 10000.0
 NOISE = 0.75
 DT = -0.25
 
+# Calibrated HBM traffic per attention launch at the C2/C4 shape (Nq 4680, Nk 24960),
+# from rocprofv3 FETCH_SIZE/WRITE_SIZE runs scaled by a copy kernel of known size,
+# keyed by the attention kernel version the library reports; any other version
+# reports null (the counters were taken on a different kernel).
+ATTN_TRAFFIC_BYTES = {"attn-v4": 1.089e9}
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -252,6 +258,9 @@ def main():
         if args.steps == 10:
             args.steps = 1000
     r = gpu_step_bench(args, **geo)
+    import streaming_causal_video_amd as L
+    version = L.la_version().split()[-1]
+    traffic = ATTN_TRAFFIC_BYTES.get(version) if args.workload in ("c4", "c2") else None
     peak_frac = r["attn_tflops"] / PEAK_BF16_TFLOPS
     out = {
         "metric": METRIC,
@@ -273,7 +282,7 @@ def main():
         "attn_ms": round(r["attn_ms"], 4),
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tflops"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(peak_frac, 4),
-                     "traffic": None, "kernel": "attn_bf16_kernel",
+                     "traffic": traffic, "kernel": "attn_bf16_kernel", "kernel_version": version,
                      "flop_per_launch": r["attn_flop_per_launch"]},
         "streaming_kernels": {
             "rope_us": round(r["rope_us"], 2), "rope_GBps": round(r["rope_gbs"], 1),

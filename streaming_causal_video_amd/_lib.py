@@ -64,6 +64,20 @@ class LAError(RuntimeError):
 _LIB = None
 
 
+def _hip_runtimes_mapped():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                p = line.split()[-1] if line.strip() else ""
+                if "libamdhip64.so" in os.path.basename(p):
+                    paths.add(os.path.realpath(p))
+    except OSError:
+        pass
+    return paths
+
+
 def _load():
     global _LIB
     if _LIB is not None:
@@ -71,7 +85,18 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
                           "`python -m streaming_causal_video_amd.build`")
+    # The library takes PyTorch's device pointers, streams and events, so it must
+    # run on the same HIP runtime as PyTorch.  PyTorch ships its own copy with the
+    # same soname: loading torch first makes the dynamic linker bind liblahip's
+    # libamdhip64.so.7 dependency to it instead of mapping a second runtime.
+    import torch  # noqa: F401
+    import torch.cuda  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are mapped into this process "
+                          f"({sorted(runtimes)}); import torch before anything loads "
+                          "/opt/rocm's libamdhip64")
     P, I32, I64, F, D, VP = (ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_double, ctypes.c_void_p)
     R = P(la_kvring)

@@ -22,8 +22,12 @@
 //  * K rows are fed to the MFMA in an order that swaps bits 2 and 3 of the row
 //    index; then the probabilities P^T come out of the score accumulator
 //    already in the B-operand layout of the second product O^T = V^T P^T, with
-//    no shuffle.  V^T operands come straight from the row-major V tile through
-//    the gfx950 LDS transpose read ds_read_b64_tr_b16.
+//    no shuffle.
+//  * V is stored transposed in LDS (V^T: 128 rows of 64 keys, 144-byte pitch):
+//    each loader thread transposes a 4-key x 8-dim piece in registers with
+//    v_perm_b32, so the V^T operand of the second product is read with plain
+//    ds_read_b128 at immediate offsets (measured on gfx950: 16-byte LDS reads
+//    deliver ~2.4x the bytes per clock of the transposing ds_read_b64_tr_b16).
 //  * Online softmax in float32 with the scale folded into a base-2 exponent
 //    (one FMA and one v_exp_f32 per score); P is rounded to bf16 for the second
 //    product with v_cvt_pk_bf16_f32, and the row sum is taken from those same
@@ -48,9 +52,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int D = 128;
 constexpr int BM = 128;  // query rows per workgroup
@@ -58,9 +59,9 @@ constexpr int BN = 64;   // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int KP = 136;  // K row pitch in LDS (bf16): 272 B, 16 rows hit 16 disjoint bank quads
-constexpr int VP = 160;  // V row pitch in LDS (bf16): 320 B, conflict-free transpose reads
+constexpr int VTP = 72;  // V^T row pitch in LDS (bf16): 144 B, 16 rows hit 16 disjoint bank quads
 constexpr int KBUF = BN * KP;
-constexpr int VBUF = BN * VP;
+constexpr int VBUF = D * VTP;
 constexpr int STAGE = KBUF + VBUF;
 constexpr float kRescaleSlack = 8.f;  // log2 units: P <= 2^8 between rescales
 
@@ -88,12 +89,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                  float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
-                 float c2, int qtiles) {
+                 float c2, int qtiles, int nwg) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
   // XCD-aware renumbering: consecutive logical ids on one XCD.
-  const int nwg = gridDim.x;
-  const int pid = blockIdx.x;
+  const int pid = __builtin_amdgcn_workgroup_id_x();
   const int per = (nwg + 7) / 8;
   const int tall = (nwg % 8) == 0 ? 8 : (nwg % 8);
   const int xcd = pid % 8, loc = pid / 8;
@@ -101,7 +101,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const int head = lin / qtiles;
   const int qt = lin - head * qtiles;
 
-  const int tid = threadIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
@@ -126,15 +126,22 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   float m_run = -INFINITY;  // running max of scale*log2(e)*score
   float l_run = 0.f;        // this lane's half of the running row sum
 
-  // Loader: thread covers 16-byte chunk lcc of rows lr0 + 16 i.
+  // Loader.  K: thread covers 16-byte chunk lcc of tile rows lr0 + 16 i (16 lanes
+  // read one 256-byte row).  V: thread covers 16-byte chunk vc (dims 8 vc .. 8 vc + 7)
+  // of tile rows 4 kq + i (a wave reads 64 contiguous bytes of every row) and
+  // writes it transposed.
   const int lcc = tid & 15;
   const int lr0 = tid >> 4;
+  const int kq = lane & 15;
+  const int vc = 4 * wave + (lane >> 4);
   const int ntiles = (nk + BN - 1) / BN;
   const uint32_t rs_bytes = (uint32_t)rs * 2u;
-  uint32_t voff[4];
+  uint32_t koff[4], voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    voff[i] = (uint32_t)(lr0 + 16 * i) * rs_bytes + (uint32_t)(head * D * 2 + lcc * 16);
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = (uint32_t)(lr0 + 16 * i) * rs_bytes + (uint32_t)(head * D * 2 + lcc * 16);
+    voff[i] = (uint32_t)(4 * kq + i) * rs_bytes + (uint32_t)(head * D * 2 + vc * 16);
+  }
   uint4 kreg[4], vreg[4];
   int seg = 0;  // segment holding the first key of the tile being loaded (scalar)
 
@@ -149,42 +156,55 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       const char* vb = static_cast<const char*>(segs.v[seg]) + sbase;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kreg[i] = *reinterpret_cast<const uint4*>(kb + voff[i]);
+        kreg[i] = *reinterpret_cast<const uint4*>(kb + koff[i]);
         vreg[i] = *reinterpret_cast<const uint4*>(vb + voff[i]);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = t0 + lr0 + 16 * i;
-        if (key < nk) {
-          int s = seg;
-          while (key >= segs.end[s]) ++s;
-          const int st = s ? segs.end[s - 1] : 0;
-          const int64_t off = (int64_t)(key - st) * rs + head * D + lcc * 8;
-          kreg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(segs.k[s]) + off);
-          vreg[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(segs.v[s]) + off);
-        } else {
-          kreg[i] = make_uint4(0, 0, 0, 0);
-          vreg[i] = make_uint4(0, 0, 0, 0);
-        }
-      }
+      // straddles a segment boundary or runs past the last key: per-row lookup,
+      // rows past the last key are clamped to it (their scores are masked)
+      auto row_load = [&](int r, int chunk, bool is_v) -> uint4 {
+        const int key = min(t0 + r, nk - 1);
+        int s = seg;
+        while (key >= segs.end[s]) ++s;
+        const int st = s ? segs.end[s - 1] : 0;
+        const int64_t off = (int64_t)(key - st) * rs + head * D + chunk * 8;
+        const uint16_t* base = static_cast<const uint16_t*>(is_v ? segs.v[s] : segs.k[s]);
+        return *reinterpret_cast<const uint4*>(base + off);
+      };
+      kreg[0] = row_load(lr0, lcc, false);
+      kreg[1] = row_load(lr0 + 16, lcc, false);
+      kreg[2] = row_load(lr0 + 32, lcc, false);
+      kreg[3] = row_load(lr0 + 48, lcc, false);
+      vreg[0] = row_load(4 * kq, vc, true);
+      vreg[1] = row_load(4 * kq + 1, vc, true);
+      vreg[2] = row_load(4 * kq + 2, vc, true);
+      vreg[3] = row_load(4 * kq + 3, vc, true);
     }
   };
   auto lstore = [&](int buf) {
     uint16_t* kb = lds + buf * STAGE;
-    uint16_t* vb = kb + KBUF;
+    uint16_t* vt = kb + KBUF;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = lr0 + 16 * i;
-      *reinterpret_cast<uint4*>(kb + row * KP + lcc * 8) = kreg[i];
-      *reinterpret_cast<uint4*>(vb + row * VP + lcc * 8) = vreg[i];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(kb + (lr0 + 16 * i) * KP + lcc * 8) = kreg[i];
+    // V^T[8 vc + j][4 kq .. 4 kq + 3]: pairs of keys packed per dword
+    const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
+                              {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
+                              {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
+                              {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // dims 8 vc + 2 m (low halves) and 8 vc + 2 m + 1 (high halves)
+      const uint2 even = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
+                                    __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
+      const uint2 odd = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
+                                   __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
+      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m) * VTP + 4 * kq) = even;
+      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m + 1) * VTP + 4 * kq) = odd;
     }
   };
 
   const int krow_a = k_row_perm(l32);
-  // transpose-read address pieces for V^T fragments
-  const int vrow_a = 8 * hh + ((lane & 15) >> 2);
-  const int vcol_a = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
   const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -194,7 +214,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     if (j + 1 < ntiles) gload(j + 1);
     __syncthreads();
     const uint16_t* kb = lds + (j & 1) * STAGE;
-    const uint16_t* vb = kb + KBUF;
+    const uint16_t* vt = kb + KBUF + l32 * VTP + 8 * hh;
 
     // S^T[key][query] for two 32-key blocks, chains interleaved.
     f32x16_t st[2];
@@ -253,17 +273,13 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
         pf[2 * b + half] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       }
 
-    // O^T[d][query] += V^T P^T
+    // O^T[d][query] += V^T P^T: A operand = V^T[32 db + lane % 32][16 ks + 8 hh .. +7]
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* vp0 = vb + (16 * ks + vrow_a) * VP + 32 * db + vcol_a;
-        const s16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp0));
-        const s16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp0 + 4 * VP));
-        const s16x8_t a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pf[ks],
-                                                       o[db], 0, 0, 0);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + 32 * db * VTP + 16 * ks);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
       }
     }
   }
@@ -293,7 +309,7 @@ hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs
   const float c2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attn_bf16_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
-                     nk, heads, c2, qtiles);
+                     nk, heads, c2, qtiles, qtiles * heads);
   return hipGetLastError();
 }
 

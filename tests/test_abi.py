@@ -170,3 +170,11 @@ def test_rope_and_euler_argument_checks():
     assert lib.la_fm_euler_step(p, p, 0, -0.25, None) == _lib.LA_OK  # n == 0: nothing to do
     assert lib.la_fm_euler_step(p, p, -1, -0.25, None) == _lib.LA_ERR_INVALID_ARG
     assert lib.la_fm_euler_step(ctypes.c_void_p(0x70000), ctypes.c_void_p(0x70004), 16, -0.25, None) == _lib.LA_ERR_INVALID_ARG
+
+
+def test_single_hip_runtime_shared_with_torch():
+    """The library must run on PyTorch's HIP runtime (it takes PyTorch's pointers,
+    streams and events): after loading, exactly one libamdhip64 is mapped."""
+    L.lib()
+    mapped = _lib._hip_runtimes_mapped()
+    assert len(mapped) == 1, mapped
