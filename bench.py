@@ -15,7 +15,8 @@ goes to stderr.
 
 Other workloads (--workload): c2 (one 40x128 layer, attention timed alone),
 c5 (720p-shaped layer, 44x80 tokens per frame, streamed for 1000 blocks:
-sustained blocks/s and cache-update GB/s).
+sustained blocks/s and cache-update GB/s), chain (a complete 4-step denoise of
+each block on one GPU: 4 timestep-forcing stages x 40 layers, la_denoise_chain).
 """
 
 from __future__ import annotations
@@ -158,6 +159,84 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
     return res
 
 
+def gpu_chain_bench(args, Hl, Wl, W, H, d, n_layers, n_stages=4):
+    """One block through n_stages timestep-forcing stages on one GPU (la_denoise_chain):
+    every stage has its own n_layers rings at its own noise level (1.0, 0.75, ...)."""
+    import torch
+    import streaming_causal_video_amd as L
+
+    L.lib()
+    dev = "cuda"
+    bt, st = FRAMES * Hl * Wl, Hl * Wl
+    nk = st + (W + 1) * bt
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4321)
+
+    def randn(shape, dtype=torch.bfloat16):
+        return torch.randn(shape, device=dev, dtype=torch.float32, generator=gen).to(dtype)
+
+    levels = [1.0 + DT * i for i in range(n_stages)]
+    log(f"setup: {n_stages} stages x {n_layers} layers, Hl={Hl} Wl={Wl} W={W} H={H} d={d}, "
+        f"Nq={bt} Nk={nk}, noise levels {levels}")
+    stacks = []
+    for i in range(n_stages):
+        stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, levels[i])
+        for l in range(n_layers):
+            stack.sink_k_raw[l].copy_(randn((st, H, d)))
+            stack.sink_v[l].copy_(randn((st, H, d)))
+        stacks.append(stack)
+    pool = 2  # input blocks shared by the stages (content does not affect timing)
+    ins = [[tuple(randn((bt, H, d)) for _ in range(3)) for _ in range(n_layers)] for _ in range(pool)]
+    outs = [torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
+    qws = torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev)
+    kws = torch.empty_like(qws)
+    sws = torch.empty((st, H, d), dtype=torch.bfloat16, device=dev)
+    table = torch.empty(L.la_rope_table_bytes(Hl, Wl, d) // 4, dtype=torch.float32, device=dev)
+    L.la_rope_table_fill(table, Hl, Wl, d, THETA)
+    lat_shape = (16, 3, 60, 104)
+    x = torch.randn(lat_shape, device=dev, generator=gen)
+    vels = [torch.randn(lat_shape, device=dev, generator=gen) for _ in range(n_stages)]
+    torch.cuda.synchronize()
+    log(f"allocated {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    def step(b):
+        e = b % pool
+        stages = []
+        for i in range(n_stages):
+            g = dict(rings=stacks[i].states, q_raw=[ins[e][l][0] for l in range(n_layers)],
+                     k_raw=[ins[e][l][1] for l in range(n_layers)],
+                     v_raw=[ins[e][l][2] for l in range(n_layers)], attn_out=outs,
+                     vel=vels[i], dt=DT)
+            if b == 1:
+                g["sink_k_new"] = [ins[e][l][1][:st] for l in range(n_layers)]
+                g["sink_v_new"] = [ins[e][l][2][:st] for l in range(n_layers)]
+            stages.append(g)
+        L.la_denoise_chain(stages, b, qws, kws, sws, table, Hl, Wl, x=x, frames_per_block=FRAMES,
+                           sink_delta=DELTA, theta=THETA)
+
+    block = 0
+    for _ in range(W + args.warmup):
+        block += 1
+        step(block)
+    torch.cuda.synchronize()
+    log(f"warm-up done ({block} blocks)")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        block += 1
+        step(block)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    log(f"timed {args.steps} blocks: {ms_step:.3f} ms/block through {n_stages} stages "
+        f"(host wall {wall / args.steps * 1e3:.3f} ms/block)")
+    return {"ms_per_step": ms_step, "blocks_per_s": 1e3 / ms_step, "nq": bt, "nk": nk,
+            "attn_flop_per_block": attn_flops(bt, nk, d, H) * n_layers * n_stages}
+
+
 # --------------------------------------------------------------------------- oracle on host cores
 def blas_threads():
     try:
@@ -225,13 +304,42 @@ def cpu_baseline(Hl, Wl, W, H, d, n_layers, budget_s=15.0):
     }
 
 
+def chain_main(args):
+    """--workload chain: blocks/s of a complete 4-step denoise on one GPU."""
+    geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
+    r = gpu_chain_bench(args, **geo)
+    out = {
+        "metric": "denoise-chain blocks/s at 1 GPU (4 timestep-forcing stages in sequence)",
+        "value": round(r["blocks_per_s"], 4),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) Q/K/V, sinks, latent and velocities resident in HBM (no trained weights)",
+        "config": {"workload": ("C4 shapes, 4 stages (noise levels 1.0/0.75/0.5/0.25) x 40 layers "
+                                "(3D Rolling RoPE + bf16 block attention 40x128, Nq 4680, Nk 24960 "
+                                "+ ring append/evict, W=4) + Euler per stage, one GPU"),
+                   "stages": 4, "layers": geo["n_layers"], "heads": geo["H"], "head_dim": geo["d"],
+                   "block_tokens": r["nq"], "nk": r["nk"],
+                   "parallelism": "none (4 stages sequential on 1 GPU)"},
+        "attn_tflop_per_block": round(r["attn_flop_per_block"] / 1e12, 3),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["c4", "c2", "c5"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c2", "c5", "chain"], default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
@@ -243,7 +351,7 @@ def main():
         print("bench.py is single-process; WORLD_SIZE > 1 is not supported.", file=sys.stderr)
         return 2
 
-    if args.workload == "c4":
+    if args.workload in ("c4", "chain"):
         geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
         name = ("C4 full denoise step: 40 layers x (3D Rolling RoPE + bf16 block attention "
                 "40x128, Nq 4680, Nk 24960 + ring append/evict, W=4, 1560-token sink) + "
@@ -257,6 +365,8 @@ def main():
                 "blocks + block), streamed blocks")
         if args.steps == 10:
             args.steps = 1000
+    if args.workload == "chain":
+        return chain_main(args)
     r = gpu_step_bench(args, **geo)
     import streaming_causal_video_amd as L
     version = L.la_version().split()[-1]

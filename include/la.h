@@ -277,6 +277,46 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           int64_t n_latent, float dt, void* const* timing_events,
                           la_stream_t stream);
 
+/*
+ * One stage of a timestep-forcing chain (la_denoise_chain): the per-layer
+ * caches and inputs of the stage that takes the latent from its noise level t
+ * to t + dt.  Field meanings are those of the la_denoise_step arguments of the
+ * same names; sink_k_new / sink_v_new are used at block 1 only (may be NULL).
+ */
+typedef struct la_stage {
+  la_kvring* rings;              /* n_layers rings, all at noise level t */
+  const void* const* q_raw;      /* n_layers device pointers each */
+  const void* const* k_raw;
+  const void* const* v_raw;
+  void* const* attn_out;
+  const void* const* sink_k_new;
+  const void* const* sink_v_new;
+  const float* vel;              /* velocity at this stage's input, n_latent floats */
+  float dt;                      /* step of this stage: t_next - t (negative) */
+} la_stage;
+
+/*
+ * la_denoise_chain - one block through n_stages timestep-forcing stages in
+ * order, all on one GPU (NEWS, 论文阅读: the framework also runs on a single
+ * 80 GB card; NOTES, Table 3: four denoise steps on one GPU before the steps are
+ * spread over GPUs; NOTES, 关键设计 4 and BLOG, 疑问 6: each stage keeps caches
+ * at its own noise level and hands only the latent on).  Stage s is la_denoise_step(stages[s].rings, ...,
+ * x, stages[s].vel, n_latent, stages[s].dt) with the shared workspaces, RoPE
+ * table and geometry; the latent x is updated in place stage after stage.
+ *
+ * Besides every la_denoise_step check for every stage, the noise levels must
+ * chain: stages[s+1].rings[*].noise_level == stages[s].rings[*].noise_level +
+ * stages[s].dt (to 1e-6), else LA_ERR_NOISE_LEVEL, since the latent handed to
+ * stage s+1 is at that level.  All stages are validated before the first
+ * launch; on an error nothing is enqueued and no ring changes.  x and every
+ * vel are required when n_latent > 0.
+ */
+la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
+                           int64_t block_id, void* q_rot_ws, void* k_rot_ws,
+                           void* sink_k_rot_ws, const void* rope_table, int32_t Hl, int32_t Wl,
+                           int32_t frames_per_block, int64_t sink_delta, double theta,
+                           float scale, float* x, int64_t n_latent, la_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

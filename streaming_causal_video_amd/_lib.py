@@ -26,7 +26,7 @@ EXPORTED = [
     "la_status_string", "la_last_hip_error", "la_version", "la_kvring_init", "la_kvring_advance",
     "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
     "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
-    "la_denoise_step",
+    "la_denoise_step", "la_denoise_chain",
 ]
 
 
@@ -48,6 +48,22 @@ class la_kvring(ctypes.Structure):
         ("sink_replaced", ctypes.c_int32),
         ("last_block", ctypes.c_int64),
         ("slot_block", ctypes.c_int64 * LA_MAX_WINDOW),
+    ]
+
+
+class la_stage(ctypes.Structure):
+    """Mirror of the C struct la_stage (include/la.h): one stage of la_denoise_chain."""
+
+    _fields_ = [
+        ("rings", ctypes.POINTER(la_kvring)),
+        ("q_raw", ctypes.POINTER(ctypes.c_void_p)),
+        ("k_raw", ctypes.POINTER(ctypes.c_void_p)),
+        ("v_raw", ctypes.POINTER(ctypes.c_void_p)),
+        ("attn_out", ctypes.POINTER(ctypes.c_void_p)),
+        ("sink_k_new", ctypes.POINTER(ctypes.c_void_p)),
+        ("sink_v_new", ctypes.POINTER(ctypes.c_void_p)),
+        ("vel", ctypes.c_void_p),
+        ("dt", ctypes.c_float),
     ]
 
 
@@ -118,6 +134,8 @@ def _load():
         "la_denoise_step": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP, VP,
                                            P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, VP,
                                            I64, F, P(VP), VP]),
+        "la_denoise_chain": (ctypes.c_int, [P(la_stage), I32, I32, I64, VP, VP, VP, VP, I32, I32,
+                                            I32, I64, D, F, VP, I64, VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -305,6 +323,45 @@ def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_w
         _ptr(k_rot_ws, "k_rot_ws"), _ptr(sink_k_rot_ws, "sink_k_rot_ws"), skn, svn,
         _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta, scale,
         _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, timing_events, _stream()), "la_denoise_step")
+
+
+def la_denoise_chain(stages, block_id: int, q_rot_ws, k_rot_ws, sink_k_rot_ws, rope_table,
+                     Hl: int, Wl: int, x=None, frames_per_block: int = 3, sink_delta: int = -1,
+                     theta: float = 10000.0, scale: Optional[float] = None) -> None:
+    """stages: list of dicts, one per stage in order, with keys rings (a KVRingStack's
+    .states array), q_raw, k_raw, v_raw, attn_out (lists of per-layer tensors), vel
+    (tensor like x, or None when x is None), dt, and optionally sink_k_new,
+    sink_v_new (lists, block 1)."""
+    n_layers = len(stages[0]["rings"])
+    arr = (la_stage * len(stages))()
+    keep = []  # pointer arrays must outlive the call
+    for i, g in enumerate(stages):
+        if len(g["rings"]) != n_layers:
+            raise ValueError("every stage needs the same number of layers")
+        st = arr[i]
+        st.rings = ctypes.cast(g["rings"], ctypes.POINTER(la_kvring))
+        for key in ("q_raw", "k_raw", "v_raw", "attn_out"):
+            a = _ptr_array(g[key], f"stages[{i}].{key}")
+            keep.append(a)
+            setattr(st, key, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
+        for key in ("sink_k_new", "sink_v_new"):
+            if g.get(key) is not None:
+                a = _ptr_array(g[key], f"stages[{i}].{key}")
+                keep.append(a)
+                setattr(st, key, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
+        if x is not None:
+            if g.get("vel") is None or g["vel"].numel() != x.numel():
+                raise ValueError(f"stages[{i}].vel must match x")
+            st.vel = _ptr(g["vel"], f"stages[{i}].vel").value
+        st.dt = float(g["dt"])
+    if scale is None:
+        scale = stages[0]["rings"][0].head_dim ** -0.5
+    n_lat = 0 if x is None else x.numel()
+    _check(_load().la_denoise_chain(
+        arr, len(stages), n_layers, block_id, _ptr(q_rot_ws, "q_rot_ws"), _ptr(k_rot_ws, "k_rot_ws"),
+        _ptr(sink_k_rot_ws, "sink_k_rot_ws"), _ptr(rope_table, "rope_table"), Hl, Wl,
+        frames_per_block, sink_delta, theta, scale, _ptr(x, "x"), n_lat, _stream()),
+        "la_denoise_chain")
 
 
 # ---------------------------------------------------------------- one layer's cache

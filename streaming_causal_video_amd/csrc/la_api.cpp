@@ -270,18 +270,17 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
   return hip_status(la::launch_euler(x, v, n, dt, static_cast<hipStream_t>(stream)));
 }
 
-la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
-                          const void* const* q_raw, const void* const* k_raw,
-                          const void* const* v_raw, void* const* attn_out, void* q_rot_ws,
-                          void* k_rot_ws, void* sink_k_rot_ws, const void* const* sink_k_new,
-                          const void* const* sink_v_new, const void* rope_table, int32_t Hl,
-                          int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
-                          double theta, float scale, float* x, const float* vel,
-                          int64_t n_latent, float dt, void* const* timing_events,
-                          la_stream_t stream) {
-  // ---- validate the whole step before enqueuing anything
-  if (!rings || n_layers < 1 || !q_raw || !k_raw || !v_raw || !attn_out || !q_rot_ws ||
-      !k_rot_ws || !sink_k_rot_ws || !rope_table)
+}  // extern "C"
+
+namespace {
+
+// Checks of one stage's arguments, shared by la_denoise_step and la_denoise_chain.
+la_status validate_stage(const la_kvring* rings, int32_t n_layers, int64_t block_id,
+                         const void* const* q_raw, const void* const* k_raw,
+                         const void* const* v_raw, void* const* attn_out,
+                         const void* const* sink_k_new, const void* const* sink_v_new,
+                         int32_t Hl, int32_t Wl, int32_t frames_per_block) {
+  if (!rings || n_layers < 1 || !q_raw || !k_raw || !v_raw || !attn_out)
     return LA_ERR_INVALID_ARG;
   if ((!sink_k_new) != (!sink_v_new)) return LA_ERR_INVALID_ARG;
   if (frames_per_block < 1 || frames_per_block > LA_MAX_BLOCK_FRAMES || Hl < 1 || Wl < 1)
@@ -302,10 +301,19 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
     if (sink_k_new && block_id == 1 && (!sink_k_new[l] || !sink_v_new[l]))
       return LA_ERR_INVALID_ARG;
   }
-  if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
-  if (timing_events)
-    for (int i = 0; i < 6 * n_layers + 2; ++i)
-      if (!timing_events[i]) return LA_ERR_INVALID_ARG;
+  return LA_OK;
+}
+
+// Enqueue one validated stage (per layer: RoPE, attention, append, sink
+// replacement at block 1; then the Euler update).
+la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
+                        const void* const* q_raw, const void* const* k_raw,
+                        const void* const* v_raw, void* const* attn_out, void* q_rot_ws,
+                        void* k_rot_ws, void* sink_k_rot_ws, const void* const* sink_k_new,
+                        const void* const* sink_v_new, const void* rope_table, int32_t Hl,
+                        int32_t Wl, int32_t frames_per_block, int64_t sink_delta, double theta,
+                        float scale, float* x, const float* vel, int64_t n_latent, float dt,
+                        void* const* timing_events, la_stream_t stream) {
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> la_status {
@@ -317,34 +325,99 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
     const la_status st_ = (expr);    \
     if (st_ != LA_OK) return st_;    \
   } while (0)
-  // ---- enqueue
   for (int l = 0; l < n_layers; ++l) {
     la_kvring* r = &rings[l];
     LA_TRY(mark(6 * l));
-    la_status st = la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
-                                     r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
-                                     r->heads, r->head_dim, (la_dtype)r->dtype, theta, stream);
-    if (st != LA_OK) return st;
+    LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
+                             r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
+                             r->heads, r->head_dim, (la_dtype)r->dtype, theta, stream));
     LA_TRY(mark(6 * l + 1));
     LA_TRY(mark(6 * l + 2));
-    st = la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot_ws, v_raw[l], r->block_tokens,
-                           attn_out[l], nullptr, scale, stream);
-    if (st != LA_OK) return st;
+    LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot_ws, v_raw[l], r->block_tokens,
+                             attn_out[l], nullptr, scale, stream));
     LA_TRY(mark(6 * l + 3));
     LA_TRY(mark(6 * l + 4));
-    st = la_kvcache_append_evict(r, k_rot_ws, v_raw[l], block_id, r->noise_level, nullptr,
-                                 stream);
-    if (st != LA_OK) return st;
-    if (block_id == 1 && sink_k_new) {
-      st = la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream);
-      if (st != LA_OK) return st;
-    }
+    LA_TRY(la_kvcache_append_evict(r, k_rot_ws, v_raw[l], block_id, r->noise_level, nullptr,
+                                   stream));
+    if (block_id == 1 && sink_k_new)
+      LA_TRY(la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream));
     LA_TRY(mark(6 * l + 5));
   }
   LA_TRY(mark(6 * n_layers));
   if (x && n_latent > 0) LA_TRY(la_fm_euler_step(x, vel, n_latent, dt, stream));
   LA_TRY(mark(6 * n_layers + 1));
 #undef LA_TRY
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
+                          const void* const* q_raw, const void* const* k_raw,
+                          const void* const* v_raw, void* const* attn_out, void* q_rot_ws,
+                          void* k_rot_ws, void* sink_k_rot_ws, const void* const* sink_k_new,
+                          const void* const* sink_v_new, const void* rope_table, int32_t Hl,
+                          int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
+                          double theta, float scale, float* x, const float* vel,
+                          int64_t n_latent, float dt, void* const* timing_events,
+                          la_stream_t stream) {
+  // ---- validate the whole step before enqueuing anything
+  if (!q_rot_ws || !k_rot_ws || !sink_k_rot_ws || !rope_table) return LA_ERR_INVALID_ARG;
+  const la_status v = validate_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out,
+                                     sink_k_new, sink_v_new, Hl, Wl, frames_per_block);
+  if (v != LA_OK) return v;
+  if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
+  if (timing_events)
+    for (int i = 0; i < 6 * n_layers + 2; ++i)
+      if (!timing_events[i]) return LA_ERR_INVALID_ARG;
+  return enqueue_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out, q_rot_ws,
+                       k_rot_ws, sink_k_rot_ws, sink_k_new, sink_v_new, rope_table, Hl, Wl,
+                       frames_per_block, sink_delta, theta, scale, x, vel, n_latent, dt,
+                       timing_events, stream);
+}
+
+la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
+                           int64_t block_id, void* q_rot_ws, void* k_rot_ws,
+                           void* sink_k_rot_ws, const void* rope_table, int32_t Hl, int32_t Wl,
+                           int32_t frames_per_block, int64_t sink_delta, double theta,
+                           float scale, float* x, int64_t n_latent, la_stream_t stream) {
+  // ---- validate every stage, and the noise-level chain, before enqueuing anything
+  if (!stages || n_stages < 1 || !q_rot_ws || !k_rot_ws || !sink_k_rot_ws || !rope_table)
+    return LA_ERR_INVALID_ARG;
+  if (n_latent < 0 || (n_latent > 0 && !x)) return LA_ERR_INVALID_ARG;
+  for (int s = 0; s < n_stages; ++s) {
+    const la_stage& g = stages[s];
+    const la_status v = validate_stage(g.rings, n_layers, block_id, g.q_raw, g.k_raw, g.v_raw,
+                                       g.attn_out, g.sink_k_new, g.sink_v_new, Hl, Wl,
+                                       frames_per_block);
+    if (v != LA_OK) return v;
+    if (!isfinite(g.dt) || (n_latent > 0 && !g.vel)) return LA_ERR_INVALID_ARG;
+    if (g.rings[0].head_dim != stages[0].rings[0].head_dim ||
+        g.rings[0].heads != stages[0].rings[0].heads ||
+        g.rings[0].dtype != stages[0].rings[0].dtype ||
+        g.rings[0].block_tokens != stages[0].rings[0].block_tokens)
+      return LA_ERR_SHAPE;
+    for (int t = 0; t < s; ++t)  // one ring belongs to one stage
+      for (int l = 0; l < n_layers; ++l)
+        for (int m = 0; m < n_layers; ++m)
+          if (&stages[t].rings[l] == &g.rings[m]) return LA_ERR_INVALID_ARG;
+    if (s > 0) {
+      const double expect = (double)stages[s - 1].rings[0].noise_level + stages[s - 1].dt;
+      if (fabs((double)g.rings[0].noise_level - expect) > 1e-6) return LA_ERR_NOISE_LEVEL;
+    }
+  }
+  for (int s = 0; s < n_stages; ++s) {
+    const la_stage& g = stages[s];
+    const la_status st = enqueue_stage(g.rings, n_layers, block_id, g.q_raw, g.k_raw, g.v_raw,
+                                       g.attn_out, q_rot_ws, k_rot_ws, sink_k_rot_ws,
+                                       g.sink_k_new, g.sink_v_new, rope_table, Hl, Wl,
+                                       frames_per_block, sink_delta, theta, scale,
+                                       n_latent > 0 ? x : nullptr, g.vel, n_latent, g.dt,
+                                       nullptr, stream);
+    if (st != LA_OK) return st;
+  }
   return LA_OK;
 }
 

@@ -38,16 +38,18 @@ def test_exported_dynamic_symbols():
         assert n in syms, n
 
 
-def test_struct_layout_matches_c(tmp_path):
+@pytest.mark.parametrize("struct", ["la_kvring", "la_stage"])
+def test_struct_layout_matches_c(tmp_path, struct):
     """Compile a probe against include/la.h with gcc and compare the layout with ctypes."""
     src = tmp_path / "probe.c"
-    fields = [f[0] for f in _lib.la_kvring._fields_]
-    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(la_kvring, {f}));' for f in fields)
+    cls = getattr(_lib, struct)
+    fields = [f[0] for f in cls._fields_]
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields)
     src.write_text(f"""#include <stdio.h>
 #include <stddef.h>
 #include "la.h"
 int main(void) {{
-  printf("sizeof %zu\\n", sizeof(la_kvring));
+  printf("sizeof %zu\\n", sizeof({struct}));
 {body}
   return 0;
 }}
@@ -57,9 +59,9 @@ int main(void) {{
                    check=True)
     out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
                                                       check=True).stdout.splitlines())
-    assert int(out["sizeof"]) == ctypes.sizeof(_lib.la_kvring)
+    assert int(out["sizeof"]) == ctypes.sizeof(cls)
     for f in fields:
-        assert int(out[f]) == getattr(_lib.la_kvring, f).offset, f
+        assert int(out[f]) == getattr(cls, f).offset, f
 
 
 def make_ring(W=4, dtype=L.LA_BF16, noise=0.75):
@@ -178,3 +180,64 @@ def test_single_hip_runtime_shared_with_torch():
     L.lib()
     mapped = _lib._hip_runtimes_mapped()
     assert len(mapped) == 1, mapped
+
+
+def _fake_stage(rings, dt, base):
+    """A la_stage whose device pointers are never dereferenced (refused before launch)."""
+    n = len(rings)
+    st = _lib.la_stage()
+    st.rings = ctypes.cast(rings, ctypes.POINTER(_lib.la_kvring))
+    arrs = []
+    for i, key in enumerate(("q_raw", "k_raw", "v_raw", "attn_out")):
+        a = (ctypes.c_void_p * n)(*[base + 0x100000 * i + 0x1000 * l for l in range(n)])
+        arrs.append(a)
+        setattr(st, key, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
+    st.vel = base + 0x900000
+    st.dt = dt
+    return st, arrs
+
+
+def _fake_rings(n, noise, Hl=4, Wl=4, heads=2, d=128):
+    rings = (_lib.la_kvring * n)()
+    for l in range(n):
+        L.la_kvring_init(rings[l], 0x10000, 0x20000, 0x30000, 0x40000, 2, 3 * Hl * Wl, Hl * Wl,
+                         heads, d, L.LA_BF16, noise)
+    return rings
+
+
+def test_chain_refusals_change_nothing():
+    """la_denoise_chain validates every stage and the noise-level chain before any launch."""
+    lib = L.lib()
+    p = ctypes.c_void_p(0x7000000)
+    x = ctypes.c_void_p(0x8000000)
+    # stage noise levels 1.0 -> 0.75 -> 0.5 with dt -0.25 chain correctly ...
+    r0, r1, r2 = _fake_rings(2, 1.0), _fake_rings(2, 0.75), _fake_rings(2, 0.4)
+    before = [bytes(r) for r in (r0, r1, r2)]
+    s0, a0 = _fake_stage(r0, -0.25, 0x1000000)
+    s1, a1 = _fake_stage(r1, -0.25, 0x2000000)
+    s2, a2 = _fake_stage(r2, -0.25, 0x3000000)
+    # ... but 0.75 + (-0.25) != 0.4: refused
+    stages = (_lib.la_stage * 3)(s0, s1, s2)
+    st = lib.la_denoise_chain(stages, 3, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64, None)
+    assert st == _lib.LA_ERR_NOISE_LEVEL
+    # the same rings in two stages: refused
+    s1b, a1b = _fake_stage(r0, -0.25, 0x2000000)
+    r0b = _fake_rings(2, 0.75)
+    stages = (_lib.la_stage * 2)(s0, s1b)
+    assert lib.la_denoise_chain(stages, 2, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64,
+                                None) == _lib.LA_ERR_INVALID_ARG
+    # out-of-order block: refused
+    stages = (_lib.la_stage * 2)(s0, s1)
+    assert lib.la_denoise_chain(stages, 2, 2, 2, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64,
+                                None) == _lib.LA_ERR_STATE
+    # latent without a velocity: refused
+    s1.vel = None
+    stages = (_lib.la_stage * 2)(s0, s1)
+    assert lib.la_denoise_chain(stages, 2, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64,
+                                None) == _lib.LA_ERR_INVALID_ARG
+    # shape mismatch inside a stage
+    stages = (_lib.la_stage * 1)(s0)
+    assert lib.la_denoise_chain(stages, 1, 2, 1, p, p, p, p, 5, 4, 3, -1, 1e4, 0.1, x, 64,
+                                None) == _lib.LA_ERR_SHAPE
+    assert [bytes(r) for r in (r0, r1, r2)] == before
+    del a0, a1, a2, a1b, r0b

@@ -154,3 +154,60 @@ def test_checkpoint_restore_continues_bit_identically(L):
     t.cuda.synchronize()
     assert t.equal(bstream.out.view(t.int16), ref_out.view(t.int16))
     assert t.equal(bstream.ring.k_slots.view(t.int16), ref_slots.view(t.int16))
+
+
+def test_denoise_chain_four_stages_matches_oracle(L):
+    """la_denoise_chain: one block through four timestep-forcing stages (noise levels
+    1.0, 0.75, 0.5, 0.25, each stage with its own per-layer rings and inputs), five
+    blocks.  Every stage's attention matches the float64 oracle of that stage's stream,
+    and the latent equals four sequential float32 Euler steps bit for bit."""
+    t = torch()
+    s = si.SMALL_BF16
+    n_layers, n_stages = 2, 4
+    levels = [1.0 - 0.25 * i for i in range(n_stages)]
+    stacks = []
+    for i in range(n_stages):
+        st = L.KVRingStack(n_layers, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim,
+                           t.bfloat16, levels[i])
+        for l in range(n_layers):
+            sk, sv = s.initial_sink(i * n_layers + l)
+            st.sink_k_raw[l].copy_(to_dev(sk))
+            st.sink_v[l].copy_(to_dev(sv))
+        stacks.append(st)
+    table = t.empty(L.la_rope_table_bytes(s.Hl, s.Wl, s.head_dim) // 4, dtype=t.float32,
+                    device="cuda")
+    L.la_rope_table_fill(table, s.Hl, s.Wl, s.head_dim, THETA)
+    blk = (s.block_tokens, s.heads, s.head_dim)
+    outs = [[t.empty(blk, dtype=t.bfloat16, device="cuda") for _ in range(n_layers)]
+            for _ in range(n_stages)]
+    qws, kws = t.empty(blk, dtype=t.bfloat16, device="cuda"), t.empty(blk, dtype=t.bfloat16, device="cuda")
+    sws = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+    oracles = [[StreamOracle(s, layer=i * n_layers + l, noise_level=levels[i])
+                for l in range(n_layers)] for i in range(n_stages)]
+    lat = si.latent(s.cfg_id, 0, si.TID_X, (16, 3, 8, 8))
+    x = to_dev(lat)
+    x_ref = lat.values.copy()
+    for b in range(1, 6):
+        stages, vels = [], []
+        for i in range(n_stages):
+            dev = [tuple(to_dev(z) for z in s.block_inputs(i * n_layers + l, b))
+                   for l in range(n_layers)]
+            vel = si.latent(s.cfg_id, 100 * b + i, si.TID_VEL, (16, 3, 8, 8))
+            vels.append(vel)
+            g = dict(rings=stacks[i].states, q_raw=[d[0] for d in dev], k_raw=[d[1] for d in dev],
+                     v_raw=[d[2] for d in dev], attn_out=outs[i], vel=to_dev(vel), dt=-0.25)
+            if b == 1:
+                g["sink_k_new"] = [d[1][:s.sink_tokens] for d in dev]
+                g["sink_v_new"] = [d[2][:s.sink_tokens] for d in dev]
+            stages.append(g)
+        L.la_denoise_chain(stages, b, qws, kws, sws, table, s.Hl, s.Wl, x=x,
+                           frames_per_block=FRAMES_PER_BLOCK, sink_delta=SINK_DELTA, theta=THETA)
+        t.cuda.synchronize()
+        for i in range(n_stages):
+            x_ref = euler_step(x_ref, vels[i].values, -0.25).astype(np.float32).astype(np.float64)
+            for l in range(n_layers):
+                check_attention(to_f64(outs[i][l]), oracles[i][l].block_output(b),
+                                f"stage {i} layer {l} block {b}")
+                r = stacks[i].states[l]
+                assert r.last_block == b and r.sink_replaced == 1 and r.noise_level == levels[i]
+        np.testing.assert_array_equal(x.cpu().numpy(), x_ref.astype(np.float32))
