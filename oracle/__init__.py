@@ -13,6 +13,10 @@ the rest supports.  Every step reaches a result with a plain definition
 oracle *is* that definition written out in float64 numpy with no blocking,
 fusion or reordering.
 
+FP8 (``fp8.py``): e4m3 encoding (nearest, ties to even, saturating at 448)
+and the attention of decoded tensors; the pages name FP8 quantisation without
+its format, so the OCP E4M3 format is the reading taken.
+
 Pinned by the ``-m "not gpu"`` tests against library routines, closed forms,
 invariants and brute force (see tests/test_oracle_*.py).  Parity unpinned:
 fidelity to the real trained model's choices (RoPE theta and band split, the
@@ -25,6 +29,7 @@ from .attention import attention, attention_lse
 from .cache import Ring, Sink, RingStateError
 from .flow import euler_step, linear_path_point, uniform_grid
 from .stream import StreamOracle, block_f0, SINK_DELTA
+from .fp8 import E4M3_MAX, attention_fp8, dequantize, e4m3_decode, e4m3_encode, quantize
 
 __all__ = [
     "band_split", "band_frequencies", "rope3d", "token_positions",
@@ -32,4 +37,5 @@ __all__ = [
     "Ring", "Sink", "RingStateError",
     "euler_step", "linear_path_point", "uniform_grid",
     "StreamOracle", "block_f0", "SINK_DELTA",
+    "E4M3_MAX", "attention_fp8", "dequantize", "e4m3_decode", "e4m3_encode", "quantize",
 ]

@@ -1,0 +1,137 @@
+"""Pins of the e4m3 quantisation oracle (oracle/fp8.py) against the format's
+definition: closed-form code values, exhaustive round trips, brute-force nearest
+value with ties to even, saturation, and attention of decoded tensors against a
+pure-Python softmax on a tiny case."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle.fp8 import E4M3_MAX, attention_fp8, dequantize, e4m3_decode, e4m3_encode, quantize
+
+ALL = np.arange(256, dtype=np.uint8)
+
+
+def finite_codes():
+    v = e4m3_decode(ALL)
+    return ALL[~np.isnan(v)], v[~np.isnan(v)]
+
+
+def test_closed_form_codes():
+    # one = exponent field 7, mantissa 0; largest = 1.75 * 2^8; subnormal quantum 2^-9
+    table = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x44: 3.0, 0x3C: 1.5, 0x7E: 448.0, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0xB8: -1.0, 0xFE: -448.0, 0x30: 0.5}
+    for c, v in table.items():
+        assert e4m3_decode([c])[0] == v, hex(c)
+        assert e4m3_encode([v])[0] == c, hex(c)
+    assert np.isnan(e4m3_decode([0x7F, 0xFF])).all()
+    assert E4M3_MAX == 448.0
+
+
+def test_value_set_is_the_format():
+    codes, vals = finite_codes()
+    assert len(codes) == 254
+    pos = np.sort(vals[vals > 0])
+    assert len(pos) == 126  # 7 subnormals + 15 binades * 8 - 1 (NaN slot)
+    # spacing: 2^-9 below 2^-6, then 8 values per binade
+    assert np.allclose(pos[:7], np.arange(1, 8) * 2.0 ** -9)
+    for e in range(-6, 9):
+        binade = pos[(pos >= 2.0 ** e) & (pos < 2.0 ** (e + 1))]
+        want = 8 if e < 8 else 7
+        assert len(binade) == want, e
+        assert np.allclose(np.diff(binade), 2.0 ** (e - 3))
+
+
+def test_round_trip_every_code():
+    codes, vals = finite_codes()
+    back = e4m3_encode(vals)
+    assert np.array_equal(back, codes)
+
+
+def test_monotone_over_the_code_order():
+    pos = e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+
+
+def _brute_nearest(x):
+    codes, vals = finite_codes()
+    if abs(x) >= E4M3_MAX:
+        return 0x7E | (0x80 if x < 0 else 0)
+    d = np.abs(vals - x)
+    best = np.nonzero(d == d.min())[0]
+    cands = [int(codes[i]) for i in best]
+    if len(cands) > 1:
+        # a tie between neighbours: the even mantissa wins; +-0 ties go by the sign of x
+        even = [c for c in cands if (c & 1) == 0]
+        cands = even if even else cands
+        if len(cands) > 1:
+            cands = [c for c in cands if bool(c & 0x80) == (math.copysign(1, x) < 0)]
+    c = cands[0]
+    if e4m3_decode([c])[0] == 0:
+        c = 0x80 if math.copysign(1, x) < 0 else 0x00
+    return c
+
+
+def test_nearest_value_by_brute_force():
+    rng = np.random.default_rng(3)
+    xs = np.concatenate([rng.standard_normal(3000) * np.exp2(rng.integers(-14, 10, 3000)),
+                         [0.0, -0.0, 1e-30, -1e-30, 447.9, 448.0, 463.9, 464.0, 500.0, -1e9]])
+    got = e4m3_encode(xs)
+    for x, c in zip(xs, got):
+        assert c == _brute_nearest(x), (x, hex(c))
+
+
+def test_ties_go_to_even_mantissa():
+    # midpoints between neighbours in [1, 2): 1 + (2m+1)/16
+    for m in range(7):
+        x = 1.0 + (2 * m + 1) / 16.0
+        c = e4m3_encode([x])[0]
+        assert (c & 7) % 2 == 0 and abs(e4m3_decode([c])[0] - x) == 1 / 16.0
+    # midpoint between the two smallest subnormals and between 0 and the smallest
+    assert e4m3_encode([1.5 * 2.0 ** -9])[0] == 0x02
+    assert e4m3_encode([0.5 * 2.0 ** -9])[0] == 0x00
+    assert e4m3_encode([-0.5 * 2.0 ** -9])[0] == 0x80
+
+
+def test_saturation_and_sign():
+    assert list(e4m3_encode([448.0, 449.0, 464.0, 480.0, 1e30])) == [0x7E] * 5
+    assert list(e4m3_encode([-448.0, -1e30])) == [0xFE] * 2
+    assert e4m3_encode([-0.0])[0] == 0x80 and e4m3_decode([0x80])[0] == 0.0
+    with pytest.raises(ValueError):
+        e4m3_encode([np.nan])
+
+
+def test_quantize_rounds_the_float32_product():
+    # the division by the scale is a float32 multiplication by the float32 reciprocal
+    x = np.array([0.1, 1.7, -3.3, 100.0], dtype=np.float32)
+    s = 0.0123
+    inv = np.float32(1) / np.float32(s)
+    want = e4m3_encode((x * inv).astype(np.float64))
+    assert np.array_equal(quantize(x, s), want)
+    # dequantize(quantize(x)) is within half a spacing of x for values inside the range
+    rng = np.random.default_rng(1)
+    y = rng.standard_normal(1000).astype(np.float32)
+    sc = float(np.abs(y).max()) / 448.0
+    back = dequantize(quantize(y, sc), sc)
+    rel = np.abs(back - y) / np.maximum(np.abs(y), 2.0 ** -6 * sc)
+    assert rel.max() <= 2.0 ** -4 + 1e-6
+
+
+def test_attention_of_decoded_tensors_tiny_case():
+    """Integer-valued codes, unit scales: attention_fp8 equals a pure-Python softmax."""
+    rng = np.random.default_rng(8)
+    ints = [-3, -2, -1, 0, 1, 2, 3]
+    q = rng.choice(ints, size=(3, 1, 4)).astype(float)
+    k = rng.choice(ints, size=(5, 1, 4)).astype(float)
+    v = rng.choice(ints, size=(5, 1, 4)).astype(float)
+    q8, k8, v8 = e4m3_encode(q), e4m3_encode(k), e4m3_encode(v)
+    out, lse = attention_fp8(q8, k8, v8, 1.0, 1.0, 1.0, 0.5)
+    for i in range(3):
+        logits = [0.5 * sum(q[i, 0, t] * k[j, 0, t] for t in range(4)) for j in range(5)]
+        mx = max(logits)
+        w = [math.exp(z - mx) for z in logits]
+        tot = sum(w)
+        for t in range(4):
+            assert abs(out[i, 0, t] - sum(w[j] * v[j, 0, t] for j in range(5)) / tot) < 1e-12
+        assert abs(lse[0, i] - (mx + math.log(tot))) < 1e-12
