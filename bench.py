@@ -16,7 +16,8 @@ goes to stderr.
 Other workloads (--workload): c2 (one 40x128 layer, attention timed alone),
 c5 (720p-shaped layer, 44x80 tokens per frame, streamed for 1000 blocks:
 sustained blocks/s and cache-update GB/s), chain (a complete 4-step denoise of
-each block on one GPU: 4 timestep-forcing stages x 40 layers, la_denoise_chain).
+each block on one GPU: 4 timestep-forcing stages x 40 layers, la_denoise_chain),
+c2fp8 (the e4m3 attention kernel alone at the C2 shape).
 """
 
 from __future__ import annotations
@@ -32,6 +33,7 @@ import numpy as np
 
 METRIC = "block-attn TFLOP/s + denoise-step blocks/s at 1 GPU; % bf16 MFMA / HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 FRAMES = 3
 DELTA = -1
@@ -304,6 +306,81 @@ def cpu_baseline(Hl, Wl, W, H, d, n_layers, budget_s=15.0):
     }
 
 
+def gpu_fp8_attn_bench(args, Hl, Wl, W, H, d):
+    """e4m3 block attention at the C2 shape (ring full, Nk = sink + (W+1) blocks), timed
+    alone: la_block_attn_fwd_fp8 on e4m3 Q/K/V quantised once before the timed region."""
+    import torch
+    import streaming_causal_video_amd as L
+
+    L.lib()
+    dev = "cuda"
+    bt, st = FRAMES * Hl * Wl, Hl * Wl
+    nk = st + (W + 1) * bt
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+    sc = 5.0 / 448.0
+    inv = float(np.float32(1.0) / np.float32(sc))
+
+    def q8(n):
+        x = torch.randn((n, H, d), device=dev, dtype=torch.float32, generator=gen).to(torch.bfloat16)
+        out = torch.empty((n, H, d), dtype=torch.uint8, device=dev)
+        L.la_quantize_fp8(x, out, inv)
+        return out
+
+    ring = L.KVRing(W, bt, st, H, d, torch.uint8, NOISE)
+    for b in range(1, W + 1):
+        L.la_kvcache_append_evict(ring.state, q8(bt), q8(bt), b, NOISE)
+    q, k, v, sk, sv = q8(bt), q8(bt), q8(bt), q8(st), q8(st)
+    out = torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        L.la_block_attn_fwd_fp8(ring.state, q, sk, sv, k, v, out, sc, sc, sc)
+
+    for _ in range(args.warmup + 3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    for _ in range(5):
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1) / args.steps)
+    ms = sorted(reps)[2]
+    fl = attn_flops(bt, nk, d, H)
+    log(f"fp8 attention Nq={bt} Nk={nk}: {ms:.3f} ms ({fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s)")
+    return {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "flop": fl, "nq": bt, "nk": nk}
+
+
+def fp8_main(args):
+    """--workload c2fp8: the e4m3 attention kernel at the C2 shape."""
+    geo = dict(Hl=30, Wl=52, W=4, H=40, d=128)
+    r = gpu_fp8_attn_bench(args, **geo)
+    out = {
+        "metric": "block-attn TFLOP/s at 1 GPU, e4m3 operands; % fp8 MFMA peak",
+        "value": round(r["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3",
+        "data": "synthetic N(0,1) Q/K/V quantised to e4m3 (per-tensor scale 5/448), resident in HBM",
+        "config": {"workload": "C2 e4m3 block attention 40x128, Nq 4680, Nk 24960 (W=4 e4m3 ring)",
+                   "heads": geo["H"], "head_dim": geo["d"], "nq": r["nq"], "nk": r["nk"]},
+        "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fp8_kernel", "flop_per_launch": r["flop"]},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def chain_main(args):
     """--workload chain: blocks/s of a complete 4-step denoise on one GPU."""
     geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
@@ -339,7 +416,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["c4", "c2", "c5", "chain"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c2", "c5", "chain", "c2fp8"], default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
@@ -367,6 +444,8 @@ def main():
             args.steps = 1000
     if args.workload == "chain":
         return chain_main(args)
+    if args.workload == "c2fp8":
+        return fp8_main(args)
     r = gpu_step_bench(args, **geo)
     import streaming_causal_video_amd as L
     version = L.la_version().split()[-1]

@@ -54,7 +54,14 @@ typedef enum la_status {
   LA_ERR_HIP = -6           /* a HIP runtime call or launch failed                  */
 } la_status;
 
-typedef enum la_dtype { LA_BF16 = 0, LA_F32 = 1 } la_dtype;
+/*
+ * Element types.  LA_FP8_E4M3 is an 8-bit float (OCP E4M3: bias 7, 3 mantissa
+ * bits, largest finite 448, no infinities) used for quantised attention
+ * operands (NOTES, Table 3: FP8 quantisation); a la_kvring of this dtype keeps
+ * its K/V slots in e4m3 and its sink (raw K and V) in bf16, because the sink
+ * is re-rotated at every block from its raw values.
+ */
+typedef enum la_dtype { LA_BF16 = 0, LA_F32 = 1, LA_FP8_E4M3 = 2 } la_dtype;
 
 typedef void* la_stream_t; /* hipStream_t */
 
@@ -66,6 +73,7 @@ typedef void* la_stream_t; /* hipStream_t */
  * A plain host struct owned by the caller; it only points at device memory.
  *
  *   k_slots, v_slots : device, [W][block_tokens][heads][head_dim] of dtype.
+ *                      (dtype LA_FP8_E4M3: e4m3 codes; the sink stays bf16.)
  *                      Slot s holds block b with (b - 1) mod W == s.
  *   sink_k_raw       : device, [sink_tokens][heads][head_dim], the sink's
  *                      unrotated K (it is re-rotated at every block).
@@ -276,6 +284,47 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           double theta, float scale, float* x, const float* vel,
                           int64_t n_latent, float dt, void* const* timing_events,
                           la_stream_t stream);
+
+/*
+ * la_quantize_fp8 - per-tensor FP8 quantisation (NOTES, Table 3: FP8
+ * quantisation).  out[i] = E4M3(in[i] * inv_scale) for 0 <= i < n, where the
+ * product is one float32 multiplication and E4M3 rounds to the nearest
+ * representable value (ties to even mantissa), keeps the sign of zero and
+ * saturates magnitudes beyond 448 to 448.  The dequantised value of a code c is
+ * decode(c) / inv_scale.
+ *   in        : device, n elements of in_dtype (LA_BF16 or LA_F32), 16-byte aligned.
+ *   out       : device, n bytes, 16-byte aligned, not overlapping in.
+ *   inv_scale : > 0 and finite.
+ * n == 0 is a no-op.  NaN inputs give unspecified codes.
+ */
+la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t n,
+                          float inv_scale, la_stream_t stream);
+
+/*
+ * la_block_attn_fwd_fp8 - la_block_attn_fwd on e4m3 operands: out =
+ * softmax(scale * (dq Q)(dk K_all)^T) (dv V_all) with Q, K, V given as e4m3
+ * codes and one dequantisation factor per tensor (dq, dk, dv; a code's value
+ * is decode(code) * factor).  Key set and order as in la_block_attn_fwd:
+ * [sink ; cached slots oldest first ; the block itself], no mask.
+ *   r            : ring of dtype LA_FP8_E4M3, head_dim 128; its slots hold e4m3
+ *                  K (rotated) and V quantised with the same dk, dv.
+ *   q8           : [n_q][heads][128] e4m3, n_q == r->block_tokens.
+ *   sink_k8/_v8  : [sink_tokens][heads][128] e4m3, the rotated sink K and the
+ *                  sink V for this block (the ring's bf16 sink, rotated and
+ *                  quantised by the caller with la_rope3d_rolling and
+ *                  la_quantize_fp8).
+ *   k8_cur/v8_cur: [n_q][heads][128] e4m3, this block's rotated K and its V.
+ *   out          : [n_q][heads][128] bf16 (not aliasing an input).
+ *   lse_or_null  : NULL or [heads][n_q] float32 natural-log sum of exp of the
+ *                  dequantised logits.
+ * The probabilities are rounded to e4m3 for the P V product (relative error
+ * <= 2^-4 per probability); the row sum uses them before rounding.
+ * Pointers 16-byte aligned (lse 4-byte); factors and scale > 0 and finite.
+ */
+la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* sink_k8,
+                                const void* sink_v8, const void* k8_cur, const void* v8_cur,
+                                int32_t n_q, void* out, float* lse_or_null, float scale,
+                                float dq, float dk, float dv, la_stream_t stream);
 
 /*
  * One stage of a timestep-forcing chain (la_denoise_chain): the per-layer

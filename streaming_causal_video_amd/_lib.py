@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG_DIR, "liblahip.so")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_STATE, LA_ERR_NOISE_LEVEL, \
     LA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
-LA_BF16, LA_F32 = 0, 1
+LA_BF16, LA_F32, LA_FP8_E4M3 = 0, 1, 2
 LA_MAX_WINDOW = 64
 LA_MAX_BLOCK_FRAMES = 4
 
@@ -26,7 +26,7 @@ EXPORTED = [
     "la_status_string", "la_last_hip_error", "la_version", "la_kvring_init", "la_kvring_advance",
     "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
     "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
-    "la_denoise_step", "la_denoise_chain",
+    "la_denoise_step", "la_denoise_chain", "la_quantize_fp8", "la_block_attn_fwd_fp8",
 ]
 
 
@@ -134,6 +134,9 @@ def _load():
         "la_denoise_step": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP, VP,
                                            P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, VP,
                                            I64, F, P(VP), VP]),
+        "la_quantize_fp8": (ctypes.c_int, [VP, ctypes.c_int, VP, I64, F, VP]),
+        "la_block_attn_fwd_fp8": (ctypes.c_int, [R, VP, VP, VP, VP, VP, I32, VP, VP, F, F, F, F,
+                                                 VP]),
         "la_denoise_chain": (ctypes.c_int, [P(la_stage), I32, I32, I64, VP, VP, VP, VP, I32, I32,
                                             I32, I64, D, F, VP, I64, VP]),
     }
@@ -266,10 +269,51 @@ def la_block_attn_fwd(ring: "la_kvring", q_rot, sink_k_rot, k_cur_rot, v_cur, ou
         "la_block_attn_fwd")
 
 
+def _slot_dtype(ring: "la_kvring"):
+    torch = _torch()
+    return {LA_BF16: torch.bfloat16, LA_F32: torch.float32, LA_FP8_E4M3: torch.uint8}[ring.dtype]
+
+
+def _sink_dtype(ring: "la_kvring"):
+    torch = _torch()
+    return torch.bfloat16 if ring.dtype == LA_FP8_E4M3 else _slot_dtype(ring)
+
+
+def la_quantize_fp8(x, out, inv_scale: float) -> None:
+    """out (uint8 tensor of x.numel() codes) = e4m3(x * inv_scale); x bf16 or float32."""
+    torch = _torch()
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bf16 or float32")
+    if out.dtype != torch.uint8 or out.numel() != x.numel():
+        raise ValueError("out must be a uint8 tensor with x.numel() elements")
+    _check(_load().la_quantize_fp8(_ptr(x, "x"), LA_BF16 if x.dtype == torch.bfloat16 else LA_F32,
+                                   _ptr(out, "out"), x.numel(), inv_scale, _stream()),
+           "la_quantize_fp8")
+
+
+def la_block_attn_fwd_fp8(ring: "la_kvring", q8, sink_k8, sink_v8, k8_cur, v8_cur, out, dq: float,
+                          dk: float, dv: float, lse: Optional[object] = None,
+                          scale: Optional[float] = None) -> None:
+    """e4m3 attention: q8, sink_k8, sink_v8, k8_cur, v8_cur are uint8 code tensors, out bf16."""
+    torch = _torch()
+    blk = (ring.block_tokens, ring.heads, ring.head_dim)
+    snk = (ring.sink_tokens, ring.heads, ring.head_dim)
+    u8 = torch.uint8
+    if scale is None:
+        scale = ring.head_dim ** -0.5
+    lse_p = None
+    if lse is not None:
+        lse_p = _ptr(lse, "lse", (ring.heads, ring.block_tokens), torch.float32)
+    _check(_load().la_block_attn_fwd_fp8(
+        ctypes.byref(ring), _ptr(q8, "q8", blk, u8), _ptr(sink_k8, "sink_k8", snk, u8),
+        _ptr(sink_v8, "sink_v8", snk, u8), _ptr(k8_cur, "k8_cur", blk, u8),
+        _ptr(v8_cur, "v8_cur", blk, u8), ring.block_tokens, _ptr(out, "out", blk, torch.bfloat16),
+        lse_p, scale, dq, dk, dv, _stream()), "la_block_attn_fwd_fp8")
+
+
 def la_kvcache_append_evict(ring: "la_kvring", k_rot, v, block_id: int, noise_level: float) -> int:
     """Returns the evicted block id (0 if none)."""
-    torch = _torch()
-    dtype = torch.bfloat16 if ring.dtype == LA_BF16 else torch.float32
+    dtype = _slot_dtype(ring)
     blk = (ring.block_tokens, ring.heads, ring.head_dim)
     ev = ctypes.c_int64()
     _check(_load().la_kvcache_append_evict(ctypes.byref(ring), _ptr(k_rot, "k_rot", blk, dtype),
@@ -279,8 +323,7 @@ def la_kvcache_append_evict(ring: "la_kvring", k_rot, v, block_id: int, noise_le
 
 
 def la_sink_replace(ring: "la_kvring", k_new_raw, v_new) -> None:
-    torch = _torch()
-    dtype = torch.bfloat16 if ring.dtype == LA_BF16 else torch.float32
+    dtype = _sink_dtype(ring)
     snk = (ring.sink_tokens, ring.heads, ring.head_dim)
     _check(_load().la_sink_replace(ctypes.byref(ring), _ptr(k_new_raw, "k_new_raw", snk, dtype),
                                    _ptr(v_new, "v_new", snk, dtype), _stream()), "la_sink_replace")
@@ -370,15 +413,19 @@ class KVRing:
 
     def __init__(self, W: int, block_tokens: int, sink_tokens: int, heads: int, head_dim: int,
                  dtype, noise_level: float, device="cuda"):
+        """dtype: torch.bfloat16, torch.float32, or torch.uint8 for e4m3 slots (the
+        sink of an e4m3 ring is bf16)."""
         torch = _torch()
+        code = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.uint8: LA_FP8_E4M3}[dtype]
+        sink_dtype = torch.bfloat16 if code == LA_FP8_E4M3 else dtype
         self.k_slots = torch.empty((W, block_tokens, heads, head_dim), dtype=dtype, device=device)
         self.v_slots = torch.empty_like(self.k_slots)
-        self.sink_k_raw = torch.empty((sink_tokens, heads, head_dim), dtype=dtype, device=device)
+        self.sink_k_raw = torch.empty((sink_tokens, heads, head_dim), dtype=sink_dtype,
+                                      device=device)
         self.sink_v = torch.empty_like(self.sink_k_raw)
         self.state = la_kvring()
         la_kvring_init(self.state, self.k_slots, self.v_slots, self.sink_k_raw, self.sink_v, W,
-                       block_tokens, sink_tokens, heads, head_dim,
-                       LA_BF16 if dtype == torch.bfloat16 else LA_F32, noise_level)
+                       block_tokens, sink_tokens, heads, head_dim, code, noise_level)
 
     @property
     def count(self) -> int:

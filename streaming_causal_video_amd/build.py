@@ -23,12 +23,14 @@ LIB_NAME = "liblahip.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["la_api.cpp", "rope.hip", "stream_ops.hip", "attn_bf16.hip", "attn_f32.hip"]
+SOURCES = ["la_api.cpp", "rope.hip", "stream_ops.hip", "attn_bf16.hip", "attn_fp8.hip",
+           "attn_f32.hip"]
 
-# Per-source extra flags.  The bf16 attention never sees NaN inputs, so it is
+# Per-source extra flags.  The attention kernels never see NaN inputs, so they are
 # built without NaN-quieting semantics: fmaxf then maps to bare v_max/v_max3
 # instead of canonicalising every operand first.
-EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+         "attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 # hipcc flags.  Packed-fp32 instruction selection is switched off for device code.
 CFLAGS = [

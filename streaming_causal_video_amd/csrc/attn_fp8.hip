@@ -1,0 +1,308 @@
+// Block attention on FP8 (e4m3) Q, K and V, head_dim 128, for gfx950 (CDNA4).
+//
+// out = softmax(scale * (dq Q8)(dk K8)^T) (dv V8) per head over the keys of a
+// segment table {sink, cached blocks, the block itself}, no mask: the block
+// attention of papernotes.org "Live Avatar: Streaming Real-time Audio-Driven
+// Avatar Generation with Infinite Length" (整体框架, 关键设计 2) on tensors
+// quantised to 8 bits per element with one scale per tensor (the same notes,
+// Table 3: FP8 quantisation is part of the operator-level optimisation).
+//
+// Design (gfx950-native; shares the workgroup shape of the bf16 kernel):
+//  * 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in LDS,
+//    one barrier per tile, Q fragments and the output accumulator in registers.
+//  * Both products run on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, float32
+//    accumulate): S^T = K Q^T is 4 MFMAs per tile, O^T += V^T P^T another 4.
+//  * The MFMA takes A[i][k] and B[k][j] from lane bytes under one fixed (lane,
+//    byte) -> k assignment; any assignment shared by A and B gives the same
+//    product, so the kernel picks its own: for S, lane l holds dims
+//    64 ks + 32 (l / 32) + j of its row; for P V, keys 32 (l / 32) + j.
+//  * K rows are fed to the score MFMA in the order that makes accumulator row
+//    i of key block b hold key 32 ((i / 4) % 2) + 16 b + 4 (i / 8) + i % 4.
+//    Then lane l's 32 scores are keys 32 (l / 32) .. +31 in byte order, so P
+//    packs straight into the B operand of the second product, and V^T is
+//    stored in LDS in natural key order (one 16-byte row piece per read).
+//  * V is transposed by the loader threads in registers (v_perm_b32 on
+//    4-key x 8-dim byte blocks) and stored as V^T rows of 64 bytes.
+//  * Softmax in float32 with scale * dq * dk * log2(e) folded into the exponent;
+//    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
+//    of the subnormal range; P <= 2^8 < 448 because the reference max is raised
+//    whenever a tile exceeds it by more than 2^2).  The row sum adds the float32
+//    P before rounding.  The output is multiplied by dv and divided by the sum.
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;  // head_dim = bytes per row
+constexpr int BM = 128;  // query rows per workgroup
+constexpr int BN = 64;   // keys per tile
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int KP = 144;  // K row pitch in LDS (bytes): 16 rows hit 16 disjoint bank quads
+constexpr int VTP = 80;  // V^T row pitch in LDS (bytes): 16 rows hit 16 disjoint bank quads
+constexpr int KBUF = BN * KP;
+constexpr int VBUF = D * VTP;
+constexpr int STAGE = KBUF + VBUF;
+constexpr float kRescaleSlack = 2.f;  // log2 units: P <= 2^(2 + 6) between rescales
+constexpr float kPLift = 6.f;         // P is computed as exp2(s - m + 6)
+constexpr float kE4M3Max = 448.f;
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS row of the K tile that holds key kk (inverse of the feed order above).
+__device__ __forceinline__ int k_lds_row(int kk) {
+  const int h = (kk >> 5) & 1, b = (kk >> 4) & 1, g = (kk >> 2) & 3, t = kk & 3;
+  return 32 * b + 8 * g + 4 * h + t;
+}
+
+// 32 bytes from a 16-byte aligned address (two 16-byte reads)
+__device__ __forceinline__ i32x8_t ld32(const uint8_t* p) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
+  return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+__device__ __forceinline__ f32x16_t mma(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
+                          amdgpu_waves_per_eu(2, 2))) void
+attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
+                float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
+                float c2, float dv, float ln_scale, int qtiles, int nwg) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+
+  // XCD-aware renumbering: consecutive logical ids on one XCD.
+  const int pid = __builtin_amdgcn_workgroup_id_x();
+  const int per = (nwg + 7) / 8;
+  const int tall = (nwg % 8) == 0 ? 8 : (nwg % 8);
+  const int xcd = pid % 8, loc = pid / 8;
+  const int lin = xcd < tall ? xcd * per + loc : tall * per + (xcd - tall) * (per - 1) + loc;
+  const int head = lin / qtiles;
+  const int qt = lin - head * qtiles;
+
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t rs = (int64_t)heads * D;  // row stride in bytes
+
+  // Q^T B-operand fragments: lane holds bytes 64 ks + 32 hh .. +31 of its query row.
+  const int qrow = qt * BM + wave * 32 + l32;
+  i32x8_t qf[2];
+  if (qrow < nq) {
+    const uint8_t* qp = q + qrow * rs + head * D + 32 * hh;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qf[ks] = ld32(qp + 64 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qf[ks] = i32x8_t{};
+  }
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
+  float m_run = -INFINITY;  // running reference max (exp2 units)
+  float l_run = 0.f;        // this lane's half of the running row sum (of lifted P)
+
+  // Loader.  K: thread covers 16-byte chunk kc of key rows kr0 and kr0 + 32 (8 lanes
+  // read one 128-byte row).  V: thread covers dims 8 vc .. 8 vc + 7 of keys
+  // 4 kq .. 4 kq + 3 (8 bytes each) and writes them transposed, one dword per dim.
+  const int kc = tid & 7;
+  const int kr0 = tid >> 3;
+  const int kq = tid & 15;
+  const int vc = tid >> 4;
+  const int ntiles = (nk + BN - 1) / BN;
+  const uint32_t rs32 = (uint32_t)rs;
+  uint32_t koff[2], voff[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    koff[i] = (uint32_t)(kr0 + 32 * i) * rs32 + (uint32_t)(head * D + kc * 16);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    voff[t] = (uint32_t)(4 * kq + t) * rs32 + (uint32_t)(head * D + vc * 8);
+  uint4 kreg[2];
+  uint2 vreg[4];
+  int seg = 0;  // segment holding the first key of the tile being loaded (scalar)
+
+  auto gload = [&](int tile) {
+    const int t0 = tile * BN;
+    while (t0 >= segs.end[seg]) ++seg;
+    const int start = seg ? segs.end[seg - 1] : 0;
+    if (t0 + BN <= segs.end[seg]) {
+      // whole tile inside one segment: scalar base + precomputed 32-bit offsets
+      const uint32_t sbase = (uint32_t)(t0 - start) * rs32;
+      const uint8_t* kb = static_cast<const uint8_t*>(segs.k[seg]) + sbase;
+      const uint8_t* vb = static_cast<const uint8_t*>(segs.v[seg]) + sbase;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) kreg[i] = *reinterpret_cast<const uint4*>(kb + koff[i]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vreg[t] = *reinterpret_cast<const uint2*>(vb + voff[t]);
+    } else {
+      // straddles a segment boundary or runs past the last key: per-row lookup,
+      // rows past the last key are clamped to it (their scores are masked)
+      auto row_base = [&](int r, bool is_v) -> const uint8_t* {
+        const int key = min(t0 + r, nk - 1);
+        int s = seg;
+        while (key >= segs.end[s]) ++s;
+        const int st = s ? segs.end[s - 1] : 0;
+        return static_cast<const uint8_t*>(is_v ? segs.v[s] : segs.k[s]) +
+               (int64_t)(key - st) * rs + head * D;
+      };
+      kreg[0] = *reinterpret_cast<const uint4*>(row_base(kr0, false) + kc * 16);
+      kreg[1] = *reinterpret_cast<const uint4*>(row_base(kr0 + 32, false) + kc * 16);
+      vreg[0] = *reinterpret_cast<const uint2*>(row_base(4 * kq, true) + vc * 8);
+      vreg[1] = *reinterpret_cast<const uint2*>(row_base(4 * kq + 1, true) + vc * 8);
+      vreg[2] = *reinterpret_cast<const uint2*>(row_base(4 * kq + 2, true) + vc * 8);
+      vreg[3] = *reinterpret_cast<const uint2*>(row_base(4 * kq + 3, true) + vc * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* kb = lds + buf * STAGE;
+    uint8_t* vt = kb + KBUF;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(kb + k_lds_row(kr0 + 32 * i) * KP + kc * 16) = kreg[i];
+    // V^T[8 vc + e][4 kq .. 4 kq + 3] = byte e of the four keys' 8-byte pieces
+    const uint32_t w[2][4] = {{vreg[0].x, vreg[1].x, vreg[2].x, vreg[3].x},
+                              {vreg[0].y, vreg[1].y, vreg[2].y, vreg[3].y}};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t* x = w[half];
+      // bytes 0,1 (and 2,3) of keys 0,1 and of keys 2,3 interleaved
+      const uint32_t a01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+      const uint32_t a23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+      const uint32_t b01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+      const uint32_t b23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+      const uint32_t d0 = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+      const uint32_t d1 = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+      const uint32_t d2 = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+      const uint32_t d3 = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
+      uint8_t* col = vt + (8 * vc + 4 * half) * VTP + 4 * kq;
+      *reinterpret_cast<uint32_t*>(col) = d0;
+      *reinterpret_cast<uint32_t*>(col + VTP) = d1;
+      *reinterpret_cast<uint32_t*>(col + 2 * VTP) = d2;
+      *reinterpret_cast<uint32_t*>(col + 3 * VTP) = d3;
+    }
+  };
+
+  gload(0);
+  for (int j = 0; j < ntiles; ++j) {
+    lstore(j & 1);
+    if (j + 1 < ntiles) gload(j + 1);
+    __syncthreads();
+    const uint8_t* kb = lds + (j & 1) * STAGE;
+    const uint8_t* vt = kb + KBUF + l32 * VTP + 32 * hh;
+
+    // S^T for the two 32-row key blocks: A = LDS row 32 b + lane % 32, bytes 64 ks + 32 hh ..
+    f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const i32x8_t a = ld32(kb + (32 * b + l32) * KP + 64 * ks + 32 * hh);
+        st[b] = mma(a, qf[ks], st[b]);
+      }
+    if ((j + 1) * BN > nk) {
+      // last tile: mask keys past the end (st[b][r] holds key 32 hh + 16 b + r)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (j * BN + 32 * hh + 16 * b + r >= nk) st[b][r] = -INFINITY;
+    }
+
+    float mx = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
+    mx = swap_halves_max(mx) * c2;
+    // raise the reference max only when this tile would push P above 2^(2+6)
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    }
+
+    // P^T fragment: byte 16 b + r = key 32 hh + 16 b + r; four partial row sums
+    i32x8_t pf;
+    const float nm = kPLift - m_run;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float p[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          p[t] = __builtin_amdgcn_exp2f(fmaf(st[b][4 * g + t], c2, nm));
+          ls[t] += p[t];
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p[0], kE4M3Max), fminf(p[1], kE4M3Max), 0,
+                                                false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p[2], kE4M3Max), fminf(p[3], kE4M3Max), w, true);
+        pf[4 * b + g] = w;
+      }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+    // O^T[d][query] += V^T P^T: A = V^T row 32 db + lane % 32, keys 32 hh .. +31
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const i32x8_t a = ld32(vt + 32 * db * VTP);
+      o[db] = mma(a, pf, o[db]);
+    }
+  }
+
+  const float lt = swap_halves_sum(l_run);
+  if (qrow < nq) {
+    const float f = dv / lt;
+    uint16_t* op = out + (qrow * (int64_t)heads + head) * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t w0 = pack_bf16(o[db][4 * g] * f, o[db][4 * g + 1] * f);
+        const uint32_t w1 = pack_bf16(o[db][4 * g + 2] * f, o[db][4 * g + 3] * f);
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * g) = make_uint2(w0, w1);
+      }
+    if (lse != nullptr && hh == 0)
+      lse[(int64_t)head * nq + qrow] = (m_run - kPLift + __log2f(lt)) * ln_scale;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
+                           int nk, int heads, float scale, float dq, float dk, float dv,
+                           hipStream_t s) {
+  const int qtiles = (nq + BM - 1) / BM;
+  const float c2 = scale * dq * dk * 1.4426950408889634f;
+  hipLaunchKernelGGL(attn_fp8_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
+                     static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
+                     nk, heads, c2, dv, 0.69314718055994531f, qtiles, qtiles * heads);
+  return hipGetLastError();
+}
+
+}  // namespace la

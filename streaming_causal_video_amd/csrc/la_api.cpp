@@ -24,9 +24,13 @@ la_status hip_status(hipError_t e) {
   return LA_ERR_HIP;
 }
 
-size_t elem_size(int dt) { return dt == LA_BF16 ? 2 : 4; }
+// bytes per element of a ring's K/V slots, and of its sink (bf16 for e4m3 rings)
+size_t elem_size(int dt) { return dt == LA_FP8_E4M3 ? 1 : (dt == LA_BF16 ? 2 : 4); }
+size_t sink_elem_size(int dt) { return dt == LA_FP8_E4M3 ? 2 : elem_size(dt); }
 
+// compute dtypes of the RoPE / bf16-f32 attention calls
 bool valid_dtype(int dt) { return dt == LA_BF16 || dt == LA_F32; }
+bool valid_ring_dtype(int dt) { return valid_dtype(dt) || dt == LA_FP8_E4M3; }
 
 // Frame band width d - 4*floor(d/6); spatial bands 2*floor(d/6) each.
 void bands(int d, int* t, int* hw) {
@@ -41,7 +45,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.2 (gfx950) attn-v4"; }
+const char* la_version(void) { return "liblahip 0.3 (gfx950) attn-v4"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -62,7 +66,7 @@ la_status la_kvring_init(la_kvring* r, void* k_slots, void* v_slots, void* sink_
                          void* sink_v, int32_t W, int32_t block_tokens, int32_t sink_tokens,
                          int32_t heads, int32_t head_dim, la_dtype dtype, float noise_level) {
   if (!r || !k_slots || !v_slots || !sink_k_raw || !sink_v) return LA_ERR_INVALID_ARG;
-  if (!valid_dtype(dtype)) return LA_ERR_DTYPE;
+  if (!valid_ring_dtype(dtype)) return LA_ERR_DTYPE;
   if (W < 1 || W > LA_MAX_WINDOW || block_tokens < 1 || sink_tokens < 1 || heads < 1 ||
       head_dim < 8 || head_dim % 8 != 0 || head_dim > 256)
     return LA_ERR_SHAPE;
@@ -223,6 +227,69 @@ la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* s
   return hip_status(e);
 }
 
+la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t n,
+                          float inv_scale, la_stream_t stream) {
+  if (n < 0) return LA_ERR_INVALID_ARG;
+  if (n == 0) return LA_OK;
+  if (!in || !out) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype)) return LA_ERR_DTYPE;
+  if (!(inv_scale > 0.f) || !isfinite(inv_scale)) return LA_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+  const uintptr_t ia = (uintptr_t)in, oa = (uintptr_t)out;
+  const uintptr_t ib = (uintptr_t)n * elem_size(in_dtype), ob = (uintptr_t)n;
+  if (ia < oa + ob && oa < ia + ib) return LA_ERR_INVALID_ARG;
+  return hip_status(la::launch_quantize_fp8(in, in_dtype, out, n, inv_scale,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* sink_k8,
+                                const void* sink_v8, const void* k8_cur, const void* v8_cur,
+                                int32_t n_q, void* out, float* lse_or_null, float scale,
+                                float dq, float dk, float dv, la_stream_t stream) {
+  if (!r || !q8 || !sink_k8 || !sink_v8 || !k8_cur || !v8_cur || !out) return LA_ERR_INVALID_ARG;
+  const float f[4] = {scale, dq, dk, dv};
+  for (float x : f)
+    if (!(x > 0.f) || !isfinite(x)) return LA_ERR_INVALID_ARG;
+  if (r->dtype != LA_FP8_E4M3) return LA_ERR_DTYPE;
+  if (n_q != r->block_tokens || n_q < 1 || r->head_dim != 128) return LA_ERR_SHAPE;
+  const void* ptrs[6] = {q8, sink_k8, sink_v8, k8_cur, v8_cur, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return LA_ERR_INVALID_ARG;
+  if (lse_or_null && ((uintptr_t)lse_or_null % 4)) return LA_ERR_INVALID_ARG;
+  if (out == q8 || out == k8_cur || out == v8_cur || out == sink_k8 || out == sink_v8)
+    return LA_ERR_INVALID_ARG;
+  const int count = la_kvring_count(r);
+  const int64_t nk64 = (int64_t)r->sink_tokens + (int64_t)(count + 1) * r->block_tokens;
+  if (nk64 > INT32_MAX / 2 || (int64_t)n_q * r->heads * r->head_dim > ((int64_t)1 << 40))
+    return LA_ERR_SHAPE;
+  // the kernel addresses a segment with 32-bit byte offsets
+  const int64_t seg_rows = (r->sink_tokens > r->block_tokens ? r->sink_tokens : r->block_tokens) + 64;
+  if (seg_rows * r->heads * r->head_dim >= ((int64_t)1 << 32)) return LA_ERR_SHAPE;
+
+  la::AttnSegs segs;
+  memset(&segs, 0, sizeof(segs));
+  const size_t slot_bytes = (size_t)r->block_tokens * r->heads * r->head_dim;
+  int n = 0, end = 0;
+  segs.k[n] = sink_k8;
+  segs.v[n] = sink_v8;
+  end += r->sink_tokens;
+  segs.end[n++] = end;
+  for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b) {
+    const int slot = (int)((b - 1) % r->W);
+    segs.k[n] = static_cast<const char*>(r->k_slots) + slot * slot_bytes;
+    segs.v[n] = static_cast<const char*>(r->v_slots) + slot * slot_bytes;
+    end += r->block_tokens;
+    segs.end[n++] = end;
+  }
+  segs.k[n] = k8_cur;
+  segs.v[n] = v8_cur;
+  end += r->block_tokens;
+  segs.end[n++] = end;
+  segs.nseg = n;
+  return hip_status(la::launch_attn_fp8(q8, out, lse_or_null, segs, n_q, end, r->heads, scale,
+                                        dq, dk, dv, static_cast<hipStream_t>(stream)));
+}
+
 la_status la_kvcache_append_evict(la_kvring* r, const void* k_rot, const void* v,
                                   int64_t block_id, float noise_level,
                                   int64_t* evicted_or_null, la_stream_t stream) {
@@ -251,7 +318,8 @@ la_status la_sink_replace(la_kvring* r, const void* k_new_raw, const void* v_new
   if (!r || !k_new_raw || !v_new) return LA_ERR_INVALID_ARG;
   if (!aligned16(k_new_raw) || !aligned16(v_new)) return LA_ERR_INVALID_ARG;
   if (r->sink_replaced || r->last_block < 1) return LA_ERR_STATE;
-  const size_t bytes = (size_t)r->sink_tokens * r->heads * r->head_dim * elem_size(r->dtype);
+  const size_t bytes =
+      (size_t)r->sink_tokens * r->heads * r->head_dim * sink_elem_size(r->dtype);
   const hipError_t e = la::launch_copy2(r->sink_k_raw, k_new_raw, r->sink_v, v_new, bytes,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e);
@@ -286,6 +354,7 @@ la_status validate_stage(const la_kvring* rings, int32_t n_layers, int64_t block
   if (frames_per_block < 1 || frames_per_block > LA_MAX_BLOCK_FRAMES || Hl < 1 || Wl < 1)
     return LA_ERR_SHAPE;
   const la_kvring& r0 = rings[0];
+  if (!valid_dtype(r0.dtype)) return LA_ERR_DTYPE;  // the step runs bf16 / f32 rings
   if ((int64_t)r0.block_tokens != (int64_t)frames_per_block * Hl * Wl ||
       (int64_t)r0.sink_tokens != (int64_t)Hl * Wl)
     return LA_ERR_SHAPE;

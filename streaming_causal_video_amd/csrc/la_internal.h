@@ -47,6 +47,11 @@ hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size
 hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream_t s);
 hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                             int nk, int heads, float scale, hipStream_t s);
+hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
+                           int nk, int heads, float scale, float dq, float dk, float dv,
+                           hipStream_t s);
+hipError_t launch_quantize_fp8(const void* in, int in_dtype, void* out, int64_t n, float inv_scale,
+                               hipStream_t s);
 hipError_t launch_attn_f32(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, int head_dim, float scale, hipStream_t s);
 

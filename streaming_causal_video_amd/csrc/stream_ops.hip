@@ -11,6 +11,10 @@
 //
 // Both kernels move 16-byte vectors, several per thread with all loads issued
 // before the first store, so each wave keeps 4 KiB in flight.
+//
+// FP8 quantisation (papernotes.org notes, Table 3: FP8 quantisation among the
+// operator-level optimisations): one per-tensor scale, e4m3 codes rounded to
+// nearest even and saturated at +-448.
 #include "la_internal.h"
 
 namespace la {
@@ -82,6 +86,59 @@ __global__ __launch_bounds__(kThreads) void euler_scalar_kernel(float* __restric
     x[i] = fmaf(dt, v[i], x[i]);
 }
 
+// e4m3 code of each float, round to nearest even (v_cvt_pk_fp8_f32) after
+// clamping to +-448: the conversion instruction maps magnitudes that round past
+// 448 to NaN, the quantisation saturates them.
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+  return (uint32_t)w;
+}
+
+// out[i] = e4m3(in[i] * inv): 16 elements per thread (two or four 16-byte loads,
+// one 16-byte store); the last n % 16 elements by the thread after the last chunk.
+template <bool kBF16>
+__global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const void* __restrict__ in,
+                                                             uint8_t* __restrict__ out,
+                                                             int64_t n16, int64_t n, float inv) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float x[16];
+  if (i < n16) {
+    if constexpr (kBF16) {
+      const uint4* p = static_cast<const uint4*>(in) + 2 * i;
+      const uint4 a = p[0], b = p[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[2 * k] = __uint_as_float(w[k] << 16) * inv;
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * inv;
+      }
+    } else {
+      const float4* p = static_cast<const float4*>(in) + 4 * i;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = p[k];
+        x[4 * k] = v.x * inv;
+        x[4 * k + 1] = v.y * inv;
+        x[4 * k + 2] = v.z * inv;
+        x[4 * k + 3] = v.w * inv;
+      }
+    }
+    reinterpret_cast<uint4*>(out)[i] = make_uint4(e4m3x4(x[0], x[1], x[2], x[3]),
+                                                  e4m3x4(x[4], x[5], x[6], x[7]),
+                                                  e4m3x4(x[8], x[9], x[10], x[11]),
+                                                  e4m3x4(x[12], x[13], x[14], x[15]));
+  } else if (i == n16) {
+    for (int64_t e = 16 * n16; e < n; ++e) {
+      const float v = kBF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(in)[e] << 16)
+                            : static_cast<const float*>(in)[e];
+      out[e] = (uint8_t)(e4m3x4(v * inv, 0.f, 0.f, 0.f) & 0xffu);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size_t bytes,
@@ -93,6 +150,20 @@ hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size
   hipLaunchKernelGGL(copy2_kernel, grid, dim3(kThreads), 0, s, static_cast<u32x4_t*>(d0),
                      static_cast<const u32x4_t*>(s0), static_cast<u32x4_t*>(d1),
                      static_cast<const u32x4_t*>(s1), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const void* in, int in_dtype, void* out, int64_t n, float inv,
+                               hipStream_t s) {
+  const int64_t n16 = n / 16;
+  const int64_t threads = n16 + 1;  // one more thread for the tail
+  const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+  if (in_dtype == LA_BF16)
+    hipLaunchKernelGGL(quant_fp8_kernel<true>, grid, dim3(kThreads), 0, s, in,
+                       static_cast<uint8_t*>(out), n16, n, inv);
+  else
+    hipLaunchKernelGGL(quant_fp8_kernel<false>, grid, dim3(kThreads), 0, s, in,
+                       static_cast<uint8_t*>(out), n16, n, inv);
   return hipGetLastError();
 }
 

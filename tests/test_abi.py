@@ -241,3 +241,41 @@ def test_chain_refusals_change_nothing():
                                 None) == _lib.LA_ERR_SHAPE
     assert [bytes(r) for r in (r0, r1, r2)] == before
     del a0, a1, a2, a1b, r0b
+
+
+def test_fp8_ring_and_entry_point_refusals():
+    lib = L.lib()
+    p = ctypes.c_void_p(0x70000)
+    out = ctypes.c_void_p(0x80000)
+    # e4m3 rings initialise; the bf16/f32 attention and the step refuse them
+    r8 = L.la_kvring()
+    L.la_kvring_init(r8, 0x10000, 0x20000, 0x30000, 0x40000, 2, 48, 16, 2, 128, L.LA_FP8_E4M3, 0.5)
+    assert r8.dtype == L.LA_FP8_E4M3
+    assert lib.la_block_attn_fwd(ctypes.byref(r8), p, p, p, p, 48, out, None, 0.1, None) == _lib.LA_ERR_DTYPE
+    qarr = (ctypes.c_void_p * 1)(0x50000)
+    assert lib.la_denoise_step(ctypes.byref(r8), 1, 1, qarr, qarr, qarr, qarr, p, p, p, None, None,
+                               p, 4, 4, 3, -1, 1e4, 0.1, None, None, 0, -0.25, None,
+                               None) == _lib.LA_ERR_DTYPE
+    # la_block_attn_fwd_fp8: wrong ring dtype, head_dim, factors, alignment, aliasing
+    rb = make_ring(2)
+    args = lambda r, **kw: [ctypes.byref(r), kw.get("q", p), p, p, p, p, kw.get("nq", 48),
+                            kw.get("out", out), None, 0.1, kw.get("dq", 0.01), 0.01, 0.01, None]
+    assert lib.la_block_attn_fwd_fp8(*args(rb)) == _lib.LA_ERR_DTYPE
+    assert lib.la_block_attn_fwd_fp8(*args(r8, nq=47)) == _lib.LA_ERR_SHAPE
+    assert lib.la_block_attn_fwd_fp8(*args(r8, dq=0.0)) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_block_attn_fwd_fp8(*args(r8, dq=float("inf"))) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_block_attn_fwd_fp8(*args(r8, q=ctypes.c_void_p(0x70008))) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_block_attn_fwd_fp8(*args(r8, out=p)) == _lib.LA_ERR_INVALID_ARG
+    r64 = L.la_kvring()
+    L.la_kvring_init(r64, 0x10000, 0x20000, 0x30000, 0x40000, 2, 48, 16, 2, 64, L.LA_FP8_E4M3, 0.5)
+    assert lib.la_block_attn_fwd_fp8(*args(r64)) == _lib.LA_ERR_SHAPE
+    # la_quantize_fp8
+    q = lib.la_quantize_fp8
+    assert q(p, L.LA_BF16, out, 0, 1.0, None) == _lib.LA_OK  # n == 0: nothing to do
+    assert q(p, L.LA_BF16, out, -1, 1.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert q(p, L.LA_FP8_E4M3, out, 16, 1.0, None) == _lib.LA_ERR_DTYPE
+    assert q(p, L.LA_BF16, out, 16, 0.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert q(p, L.LA_BF16, out, 16, float("nan"), None) == _lib.LA_ERR_INVALID_ARG
+    assert q(ctypes.c_void_p(0x70002), L.LA_BF16, out, 16, 1.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert q(p, L.LA_F32, ctypes.c_void_p(0x70010), 16, 1.0, None) == _lib.LA_ERR_INVALID_ARG  # overlap
+    assert q(None, L.LA_BF16, out, 16, 1.0, None) == _lib.LA_ERR_INVALID_ARG

@@ -1,0 +1,169 @@
+"""FP8 (e4m3) path on the GPU against the float64 oracle: bit-exact quantisation,
+and attention over e4m3 Q/K/V (streamed through an e4m3 ring) against the exact
+attention of the decoded tensors.
+
+Tolerance of the FP8 attention (derived in the design doc): the kernel rounds each
+probability to e4m3 for the P V product (relative error <= 2^-4), so per
+element |out - ref| <= 2^-4 * A + 2^-8 |ref| + 2^-12 max|v|, where A is the
+same attention applied to |V| (the bf16 output rounding is the 2^-8 term, the
+last term covers probabilities in the e4m3 subnormal range); and over a tensor
+the relative L2 error stays near the rms relative rounding error of e4m3
+(about 0.026): bar 0.06."""
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import attention_fp8, dequantize, e4m3_encode, quantize
+
+from gpu_helpers import rel_l2, say, to_dev, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+FP8_REL_L2 = 0.06
+SCALE_QKV = 5.0 / 448.0  # per-tensor scale: |x| = 5 maps to the largest e4m3 value
+
+
+@pytest.fixture(scope="module")
+def L():
+    import streaming_causal_video_amd as lib
+    lib.lib()
+    return lib
+
+
+def inv32(scale):
+    return float(np.float32(1.0) / np.float32(scale))
+
+
+def gpu_quant(L, x_dev, scale):
+    t = torch()
+    out = t.empty(x_dev.shape, dtype=t.uint8, device="cuda")
+    L.la_quantize_fp8(x_dev, out, inv32(scale))
+    return out
+
+
+# ------------------------------------------------------------------ quantisation
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 1000, 64 * 1024 + 5])
+def test_quantize_bf16_bit_exact(L, n):
+    t = torch()
+    st = si.SMALL_BF16.block_inputs(0, 1)[0]  # bf16, N(0,1)
+    vals = st.values.reshape(-1)
+    reps = -(-n // vals.size)
+    vals = np.tile(vals, reps)[:n] * 1.0
+    bits = np.tile(np.array(st.storage).reshape(-1), reps)[:n]
+    x = t.from_numpy(bits.view(np.int16).copy()).cuda().view(t.bfloat16)
+    for scale in (SCALE_QKV, 1.0 / 448.0, 3.0):  # |x| up to ~5: the 2nd saturates many values
+        got = gpu_quant(L, x, scale).cpu().numpy()
+        want = quantize(vals.astype(np.float32), scale)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"n={n} scale={scale}: {bad.size} codes differ, e.g. x={vals[bad[0]]} got {got[bad[0]]:#x} want {want[bad[0]]:#x}"
+
+
+def test_quantize_f32_special_values(L):
+    t = torch()
+    sp = [0.0, -0.0, 1.0, -1.0, 448.0, -448.0, 449.0, 463.9, 464.0, 465.0, 480.0, 1e30, -1e30,
+          2.0 ** -9, -(2.0 ** -9), 2.0 ** -10, -(2.0 ** -10), 1.5 * 2.0 ** -9, 2.0 ** -6,
+          1.0625, 1.1875, 1.3125, 3e-45, -3e-45, 240.0, 232.0, 248.0]
+    rng = np.random.default_rng(11)
+    more = (rng.standard_normal(5000) * np.exp2(rng.integers(-14, 10, 5000))).tolist()
+    x = np.array(sp + more, dtype=np.float32)
+    xd = t.from_numpy(x).cuda()
+    got = gpu_quant(L, xd, 1.0).cpu().numpy()
+    want = e4m3_encode(x.astype(np.float64))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+# ------------------------------------------------------------------ attention
+class Fp8Stream:
+    """One layer streamed through an e4m3 ring: per block, Q/K/V (bf16 stand-ins for the
+    rotated projections) are quantised on the GPU with fixed per-tensor scales, the block
+    attends to [sink ; window ; itself], then its K/V codes are appended."""
+
+    def __init__(self, L, shape, layer=0):
+        t = torch()
+        self.L, self.s, self.layer = L, shape, layer
+        s = shape
+        self.ring = L.KVRing(s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, t.uint8, 0.75)
+        sk, sv = s.initial_sink(layer)
+        self.sink_k8 = gpu_quant(L, to_dev(sk), SCALE_QKV)
+        self.sink_v8 = gpu_quant(L, to_dev(sv), SCALE_QKV)
+        self.codes = {"sink": (quantize(sk.values.astype(np.float32), SCALE_QKV),
+                               quantize(sv.values.astype(np.float32), SCALE_QKV))}
+        self.out = t.empty((s.block_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+        self.lse = t.empty((s.heads, s.block_tokens), dtype=t.float32, device="cuda")
+
+    def step(self, b):
+        L, s = self.L, self.s
+        q, k, v = s.block_inputs(self.layer, b)
+        q8, k8, v8 = (gpu_quant(L, to_dev(x), SCALE_QKV) for x in (q, k, v))
+        self.codes[b] = tuple(quantize(x.values.astype(np.float32), SCALE_QKV) for x in (q, k, v))
+        for dev, ref in zip((q8, k8, v8), self.codes[b]):
+            assert np.array_equal(dev.cpu().numpy(), ref), f"block {b}: codes differ"
+        L.la_block_attn_fwd_fp8(self.ring.state, q8, self.sink_k8, self.sink_v8, k8, v8, self.out,
+                                SCALE_QKV, SCALE_QKV, SCALE_QKV, lse=self.lse)
+        L.la_kvcache_append_evict(self.ring.state, k8, v8, b, 0.75)
+
+    def reference(self, b, rows=None, heads=None):
+        s = self.s
+        ids = list(range(max(1, b - s.W), b))
+        ks = [self.codes["sink"][0]] + [self.codes[i][1] for i in ids] + [self.codes[b][1]]
+        vs = [self.codes["sink"][1]] + [self.codes[i][2] for i in ids] + [self.codes[b][2]]
+        q8 = self.codes[b][0]
+        hs = slice(None) if heads is None else heads
+        K8, V8 = np.concatenate(ks)[:, hs], np.concatenate(vs)[:, hs]
+        Q8 = q8[:, hs] if rows is None else q8[rows][:, hs]
+        out, lse = attention_fp8(Q8, K8, V8, SCALE_QKV, SCALE_QKV, SCALE_QKV, s.head_dim ** -0.5)
+        # the same attention of |V|: bounds the effect of the probability rounding
+        absv = np.abs(dequantize(V8, SCALE_QKV))
+        from oracle import attention_lse
+        bound_a, _ = attention_lse(dequantize(Q8, SCALE_QKV), dequantize(K8, SCALE_QKV), absv,
+                                   s.head_dim ** -0.5)
+        return out, lse, bound_a, absv.max()
+
+
+def check_fp8(got, ref, bound_a, vmax, what):
+    err = np.abs(got - ref)
+    lim = 2.0 ** -4 * bound_a + 2.0 ** -8 * np.abs(ref) + 2.0 ** -12 * vmax + 1e-6
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    worst = np.argmax(err - lim)
+    assert (err <= lim).all(), f"{what}: |err| {err.flat[worst]:.3e} > bound {lim.flat[worst]:.3e}"
+    r = rel_l2(got, ref)
+    assert r <= FP8_REL_L2, f"{what}: rel-L2 {r:.3e} > {FP8_REL_L2}"
+    return r
+
+
+@pytest.mark.parametrize("shape", [si.SMALL_BF16, si.MID_BF16], ids=lambda s: f"cfg{s.cfg_id}")
+def test_fp8_attention_stream_small(L, shape):
+    t = torch()
+    fs = Fp8Stream(L, shape)
+    for b in range(1, shape.W + 3):
+        fs.step(b)
+        t.cuda.synchronize()
+        out, lse, a, vmax = fs.reference(b)
+        r = check_fp8(to_f64(fs.out), out, a, vmax, f"cfg{shape.cfg_id} block {b}")
+        got_lse = fs.lse.cpu().numpy().astype(np.float64)
+        assert np.abs(got_lse - lse).max() <= 1e-3, f"block {b}: lse"
+        say(f"fp8 cfg{shape.cfg_id} block {b}: rel-L2 {r:.4f}")
+
+
+@pytest.mark.timeout(600)
+def test_fp8_attention_c2_sampled(L):
+    """Full C2 shape (40 heads, Nk 24960 in steady state), sampled rows and heads."""
+    t = torch()
+    shape = si.C2
+    fs = Fp8Stream(L, shape)
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([[0, shape.block_tokens - 1],
+                                     rng.integers(0, shape.block_tokens, 48)]))
+    heads = [0, 17, 39]
+    for b in range(1, shape.W + 2):
+        fs.step(b)
+    t.cuda.synchronize()
+    b = shape.W + 1
+    out, lse, a, vmax = fs.reference(b, rows=rows, heads=heads)
+    got = to_f64(fs.out)[rows][:, heads]
+    r = check_fp8(got, out, a, vmax, "C2 fp8")
+    got_lse = fs.lse.cpu().numpy().astype(np.float64)[heads][:, rows]
+    assert np.abs(got_lse - lse).max() <= 1e-3
+    say(f"fp8 C2 block {b}: rel-L2 {r:.4f}")
