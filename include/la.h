@@ -315,10 +315,13 @@ la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t 
  *                  la_quantize_fp8).
  *   k8_cur/v8_cur: [n_q][heads][128] e4m3, this block's rotated K and its V.
  *   out          : [n_q][heads][128] bf16 (not aliasing an input).
- *   lse_or_null  : NULL or [heads][n_q] float32 natural-log sum of exp of the
- *                  dequantised logits.
+ *   lse_or_null  : NULL or [heads][n_q] float32: the natural log of the sum of
+ *                  the rounded probabilities (see below) times exp(max logit),
+ *                  i.e. the exact log-sum-exp of the dequantised logits to
+ *                  within log(1 + 2^-4).
  * The probabilities are rounded to e4m3 for the P V product (relative error
- * <= 2^-4 per probability); the row sum uses them before rounding.
+ * <= 2^-4 per probability); the row sum that normalises the output is taken
+ * from the same rounded probabilities.
  * Pointers 16-byte aligned (lse 4-byte); factors and scale > 0 and finite.
  */
 la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* sink_k8,

@@ -26,8 +26,11 @@
 //  * Softmax in float32 with scale * dq * dk * log2(e) folded into the exponent;
 //    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
 //    of the subnormal range; P <= 2^8 < 448 because the reference max is raised
-//    whenever a tile exceeds it by more than 2^2).  The row sum adds the float32
-//    P before rounding.  The output is multiplied by dv and divided by the sum.
+//    whenever a tile exceeds it by more than 2^2, so no clamp is needed).
+//  * The row sum is one more MFMA per tile, of an all-ones A operand with the
+//    same e4m3 P: it moves 32 additions per lane off the VALU, which bounds
+//    this kernel, and numerator and denominator use the same rounded P.
+//    The output is multiplied by dv and divided by the sum.
 #include "la_internal.h"
 
 namespace la {
@@ -50,7 +53,6 @@ constexpr int VBUF = D * VTP;
 constexpr int STAGE = KBUF + VBUF;
 constexpr float kRescaleSlack = 2.f;  // log2 units: P <= 2^(2 + 6) between rescales
 constexpr float kPLift = 6.f;         // P is computed as exp2(s - m + 6)
-constexpr float kE4M3Max = 448.f;
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2_t f = {lo, hi};
@@ -60,11 +62,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float swap_halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float swap_halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // LDS row of the K tile that holds key kk (inverse of the feed order above).
@@ -123,7 +120,9 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
   float m_run = -INFINITY;  // running reference max (exp2 units)
-  float l_run = 0.f;        // this lane's half of the running row sum (of lifted P)
+  f32x16_t lsum = f32x16_t{};  // every row: the running sum of lifted, rounded P
+  const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
   // Loader.  K: thread covers 16-byte chunk kc of key rows kr0 and kr0 + 32 (8 lanes
   // read one 128-byte row).  V: thread covers dims 8 vc .. 8 vc + 7 of keys
@@ -241,31 +240,26 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      l_run *= alpha;
+      lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
     }
 
-    // P^T fragment: byte 16 b + r = key 32 hh + 16 b + r; four partial row sums
+    // P^T fragment: byte 16 b + r = key 32 hh + 16 b + r
     i32x8_t pf;
     const float nm = kPLift - m_run;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float p[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          p[t] = __builtin_amdgcn_exp2f(fmaf(st[b][4 * g + t], c2, nm));
-          ls[t] += p[t];
-        }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p[0], kE4M3Max), fminf(p[1], kE4M3Max), 0,
-                                                false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p[2], kE4M3Max), fminf(p[3], kE4M3Max), w, true);
+        for (int t = 0; t < 4; ++t) p[t] = __builtin_amdgcn_exp2f(fmaf(st[b][4 * g + t], c2, nm));
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pf[4 * b + g] = w;
       }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    lsum = mma(ones, pf, lsum);
 
     // O^T[d][query] += V^T P^T: A = V^T row 32 db + lane % 32, keys 32 hh .. +31
 #pragma unroll
@@ -275,7 +269,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     }
   }
 
-  const float lt = swap_halves_sum(l_run);
+  const float lt = lsum[0];  // the full row sum: MFMA rows all hold it
   if (qrow < nq) {
     const float f = dv / lt;
     uint16_t* op = out + (qrow * (int64_t)heads + head) * D + 4 * hh;

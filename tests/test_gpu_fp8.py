@@ -8,7 +8,8 @@ element |out - ref| <= 2^-4 * A + 2^-8 |ref| + 2^-12 max|v|, where A is the
 same attention applied to |V| (the bf16 output rounding is the 2^-8 term, the
 last term covers probabilities in the e4m3 subnormal range); and over a tensor
 the relative L2 error stays near the rms relative rounding error of e4m3
-(about 0.026): bar 0.06."""
+(about 0.026): bar 0.06.  The log-sum-exp is that of the rounded probabilities
+(the normaliser of the output), within log(1 + 2^-4) < 0.0625 of the exact one."""
 
 import numpy as np
 import pytest
@@ -21,6 +22,7 @@ from gpu_helpers import rel_l2, say, to_dev, to_f64, torch
 pytestmark = pytest.mark.gpu
 
 FP8_REL_L2 = 0.06
+FP8_LSE = 0.0625
 SCALE_QKV = 5.0 / 448.0  # per-tensor scale: |x| = 5 maps to the largest e4m3 value
 
 
@@ -143,7 +145,7 @@ def test_fp8_attention_stream_small(L, shape):
         out, lse, a, vmax = fs.reference(b)
         r = check_fp8(to_f64(fs.out), out, a, vmax, f"cfg{shape.cfg_id} block {b}")
         got_lse = fs.lse.cpu().numpy().astype(np.float64)
-        assert np.abs(got_lse - lse).max() <= 1e-3, f"block {b}: lse"
+        assert np.abs(got_lse - lse).max() <= FP8_LSE, f"block {b}: lse"
         say(f"fp8 cfg{shape.cfg_id} block {b}: rel-L2 {r:.4f}")
 
 
@@ -165,5 +167,5 @@ def test_fp8_attention_c2_sampled(L):
     got = to_f64(fs.out)[rows][:, heads]
     r = check_fp8(got, out, a, vmax, "C2 fp8")
     got_lse = fs.lse.cpu().numpy().astype(np.float64)[heads][:, rows]
-    assert np.abs(got_lse - lse).max() <= 1e-3
+    assert np.abs(got_lse - lse).max() <= FP8_LSE
     say(f"fp8 C2 block {b}: rel-L2 {r:.4f}")
