@@ -28,7 +28,7 @@ from .rope import band_split, band_frequencies, rope3d, token_positions
 from .attention import attention, attention_lse
 from .cache import Ring, Sink, RingStateError
 from .flow import euler_step, linear_path_point, uniform_grid
-from .stream import StreamOracle, block_f0, SINK_DELTA
+from .stream import StreamOracle, block_f0, SINK_DELTA, SINK_FIXED_POSITION
 from .fp8 import E4M3_MAX, attention_fp8, dequantize, e4m3_decode, e4m3_encode, quantize
 
 __all__ = [
@@ -36,6 +36,6 @@ __all__ = [
     "attention", "attention_lse",
     "Ring", "Sink", "RingStateError",
     "euler_step", "linear_path_point", "uniform_grid",
-    "StreamOracle", "block_f0", "SINK_DELTA",
+    "StreamOracle", "block_f0", "SINK_DELTA", "SINK_FIXED_POSITION",
     "E4M3_MAX", "attention_fp8", "dequantize", "e4m3_decode", "e4m3_encode", "quantize",
 ]

@@ -18,6 +18,14 @@ Per block b (1-based) on one stage t_i -> t_{i-1}, for one attention layer:
      input, to the window (BLOG 疑问 4; NEWS 方法概述; no clean refresh);
   4. after block 1 only: replace the sink once (NOTES 关键设计 3; BLOG 疑问 5).
 
+Variants for the pages' ablations (NOTES, Table 4 and the Table 6 finding):
+  rolling=False : the sink K keeps one fixed position, frame 0 (where the
+                  reference frame sits), instead of following the block;
+  aas=False     : the sink is never replaced (the input image stays the sink);
+  cache_layer=c : the window's K/V and the sink belong to another stream c that
+                  writes the cache (a clean-refresh pass, or the one stage of a
+                  fixed-noise cache); this stream only attends to it.
+
 Readings taken where the pages are silent: f0(b) = 3 (b - 1); delta = -1 (the
 sink sits one latent frame before the block's first frame, where the
 reference frame sits at block 1 if it is frame 0 of the video, and it stays
@@ -37,6 +45,7 @@ from .cache import Ring, Sink
 from .rope import DEFAULT_THETA, rope3d
 
 SINK_DELTA = -1
+SINK_FIXED_POSITION = 0  # the sink's own frame when Rolling RoPE is off
 
 
 def block_f0(block: int, frames_per_block: int = 3) -> int:
@@ -54,9 +63,13 @@ class StreamOracle:
 
     def __init__(self, shape, layer: int = 0, heads: Optional[Sequence[int]] = None,
                  theta: float = DEFAULT_THETA, delta: int = SINK_DELTA,
-                 noise_level: float = 0.75):
+                 noise_level: float = 0.75, rolling: bool = True, aas: bool = True,
+                 cache_layer: Optional[int] = None):
         self.shape = shape
         self.layer = layer
+        self.rolling = rolling
+        self.aas = aas
+        self.cache_layer = layer if cache_layer is None else cache_layer
         self.heads = list(range(shape.heads)) if heads is None else list(heads)
         self.theta = theta
         self.delta = delta
@@ -64,18 +77,19 @@ class StreamOracle:
         self.scale = 1.0 / np.sqrt(shape.head_dim)
 
     # ---- inputs (float64 values of the stored bits), restricted to self.heads
-    def raw_block(self, block: int):
-        q, k, v = self.shape.block_inputs(self.layer, block)
+    def raw_block(self, block: int, layer: Optional[int] = None):
+        q, k, v = self.shape.block_inputs(self.layer if layer is None else layer, block)
         hs = self.heads
         return q.values[:, hs, :], k.values[:, hs, :], v.values[:, hs, :]
 
     def initial_sink(self):
-        sk, sv = self.shape.initial_sink(self.layer)
+        """The sink of the stream that owns the cache."""
+        sk, sv = self.shape.initial_sink(self.cache_layer)
         return sk.values[:, self.heads, :], sv.values[:, self.heads, :]
 
     def replacement_sink(self):
-        """Block 1's first latent frame of raw K and V (the AAS stand-in)."""
-        _, k, v = self.raw_block(1)
+        """Block 1's first latent frame of raw K and V of the cache owner (the AAS stand-in)."""
+        _, k, v = self.raw_block(1, self.cache_layer)
         n = self.shape.sink_tokens
         return k[:n].copy(), v[:n].copy()
 
@@ -85,10 +99,14 @@ class StreamOracle:
         return rope3d(x, s.frames_per_block, s.Hl, s.Wl, block_f0(block, s.frames_per_block),
                       self.theta)
 
+    def sink_position(self, block: int) -> int:
+        if not self.rolling:
+            return SINK_FIXED_POSITION
+        return block_f0(block, self.shape.frames_per_block) + self.delta
+
     def rot_sink(self, k_raw: np.ndarray, block: int) -> np.ndarray:
         s = self.shape
-        return rope3d(k_raw, 1, s.Hl, s.Wl,
-                      block_f0(block, s.frames_per_block) + self.delta, self.theta)
+        return rope3d(k_raw, 1, s.Hl, s.Wl, self.sink_position(block), self.theta)
 
     # ---- the window a block sees, straight from its definition
     def window_ids(self, block: int):
@@ -96,7 +114,9 @@ class StreamOracle:
         return list(range(max(1, block - self.shape.W), block))
 
     def sink_for(self, block: int):
-        return self.initial_sink() if block == 1 else self.replacement_sink()
+        if block == 1 or not self.aas:
+            return self.initial_sink()
+        return self.replacement_sink()
 
     def block_output(self, block: int, rows: Optional[np.ndarray] = None, with_lse=False):
         """Attention output of block ``block`` (optionally only some query rows)."""
@@ -107,7 +127,7 @@ class StreamOracle:
         keys = [self.rot_sink(sk_raw, block)]
         vals = [sv]
         for b2 in self.window_ids(block):
-            _, k2, v2 = self.raw_block(b2)
+            _, k2, v2 = self.raw_block(b2, self.cache_layer)
             keys.append(self.rot_block(k2, b2))
             vals.append(v2)
         keys.append(k_rot)
@@ -118,7 +138,10 @@ class StreamOracle:
 
     # ---- the same stream run step by step with the Ring and Sink models
     def run(self, n_blocks: int, record: Iterable[int] = ()):
-        """Process blocks 1..n_blocks in order; returns ({block: output}, ring, sink)."""
+        """Process blocks 1..n_blocks in order; returns ({block: output}, ring, sink).
+        Only for a stream that writes its own cache."""
+        if self.cache_layer != self.layer:
+            raise ValueError("run() models a stream that writes its own cache")
         record = set(record)
         ring = Ring(self.shape.W, self.noise_level)
         sink = Sink(*self.initial_sink())
@@ -133,7 +156,7 @@ class StreamOracle:
             if b in record:
                 outs[b] = attention_lse(q_rot, keys, vals, self.scale)[0]
             ring.append(b, k_rot, v, self.noise_level)
-            if b == 1:
+            if b == 1 and self.aas:
                 n = self.shape.sink_tokens
                 sink.replace(k_raw[:n], v[:n])
         return outs, ring, sink

@@ -114,3 +114,73 @@ def test_euler_fp32_rounding_is_single():
     v = rng.standard_normal(100000).astype(np.float32)
     ref = euler_step(x, v, -0.25).astype(np.float32)
     np.testing.assert_array_equal(ref, x + np.float32(-0.25) * v)
+
+
+# ---- ablation variants (NOTES Table 4: no Rolling RoPE, no AAS; clean / fixed-noise caches)
+def _assemble(shape, own, owner, b, sink_pos, sink_kv):
+    """Block b's attention assembled directly from the oracle's pinned pieces: own Q/K/V,
+    the cache owner's window blocks, and the given raw sink rotated at sink_pos."""
+    from oracle import attention_lse, rope3d
+    f0 = lambda blk: 3 * (blk - 1)
+    q, k, v = own.raw_block(b)
+    keys = [rope3d(sink_kv[0], 1, shape.Hl, shape.Wl, sink_pos, own.theta)]
+    vals = [sink_kv[1]]
+    for b2 in range(max(1, b - shape.W), b):
+        _, k2, v2 = owner.raw_block(b2)
+        keys.append(rope3d(k2, 3, shape.Hl, shape.Wl, f0(b2), own.theta))
+        vals.append(v2)
+    keys.append(rope3d(k, 3, shape.Hl, shape.Wl, f0(b), own.theta))
+    vals.append(v)
+    qr = rope3d(q, 3, shape.Hl, shape.Wl, f0(b), own.theta)
+    return attention_lse(qr, np.concatenate(keys), np.concatenate(vals), own.scale)[0]
+
+
+@pytest.mark.parametrize("rolling,aas", [(False, True), (True, False), (False, False)])
+def test_variant_state_machine_equals_window_definition(rolling, aas):
+    shape = SMALL_F32
+    orc = StreamOracle(shape, rolling=rolling, aas=aas)
+    n = shape.W + 3
+    outs, _, sink = orc.run(n, record=range(1, n + 1))
+    for b in range(1, n + 1):
+        np.testing.assert_allclose(outs[b], orc.block_output(b), atol=1e-12)
+    assert sink.replaced == aas
+
+
+def test_variant_outputs_from_their_definition():
+    shape = SMALL_F32
+    base = StreamOracle(shape)
+    init = base.initial_sink()
+    repl = base.replacement_sink()
+    for b in (1, 2, shape.W + 2):
+        # no Rolling RoPE: the sink stays at frame 0
+        got = StreamOracle(shape, rolling=False).block_output(b)
+        want = _assemble(shape, base, base, b, 0, init if b == 1 else repl)
+        np.testing.assert_allclose(got, want, atol=1e-12)
+        # no AAS: the initial sink at every block, rolling position
+        got = StreamOracle(shape, aas=False).block_output(b)
+        want = _assemble(shape, base, base, b, 3 * (b - 1) - 1, init)
+        np.testing.assert_allclose(got, want, atol=1e-12)
+
+
+def test_no_rolling_changes_outputs_after_block_1_negative_control():
+    shape = SMALL_F32
+    a, b_ = StreamOracle(shape), StreamOracle(shape, rolling=False)
+    for blk in (2, 5):
+        assert np.max(np.abs(a.block_output(blk) - b_.block_output(blk))) > 1e-4
+
+
+def test_shared_cache_stream_reads_the_owner_cache_and_sink():
+    """An attend-only stream (cache_layer = the writer's stream) sees the writer's window
+    blocks and sink, and its own Q/K/V for the block itself."""
+    shape = SMALL_F32
+    writer = StreamOracle(shape, layer=7)
+    reader = StreamOracle(shape, layer=3, cache_layer=7)
+    for b in (1, 2, shape.W + 2):
+        sink = writer.initial_sink() if b == 1 else writer.replacement_sink()
+        want = _assemble(shape, StreamOracle(shape, layer=3), writer, b, 3 * (b - 1) - 1, sink)
+        np.testing.assert_allclose(reader.block_output(b), want, atol=1e-12)
+    with pytest.raises(ValueError):
+        reader.run(2)
+    # its own stream (cache_layer == layer) is the default stream
+    np.testing.assert_allclose(StreamOracle(shape, layer=3, cache_layer=3).block_output(3),
+                               StreamOracle(shape, layer=3).block_output(3), atol=0)
