@@ -17,7 +17,8 @@ Other workloads (--workload): c2 (one 40x128 layer, attention timed alone),
 c5 (720p-shaped layer, 44x80 tokens per frame, streamed for 1000 blocks:
 sustained blocks/s and cache-update GB/s), chain (a complete 4-step denoise of
 each block on one GPU: 4 timestep-forcing stages x 40 layers, la_denoise_chain),
-c2fp8 (the e4m3 attention kernel alone at the C2 shape).
+c2fp8 (the e4m3 attention kernel alone at the C2 shape), refresh (the NFE-5
+clean-cache baseline: 4 attend-only passes and a refresh pass per block).
 """
 
 from __future__ import annotations
@@ -48,8 +49,11 @@ DT = -0.25
 ATTN_TRAFFIC_BYTES = {"attn-v4": 1.089e9}
 
 
+_T0 = time.perf_counter()
+
+
 def log(msg):
-    print(msg, file=sys.stderr, flush=True)
+    print(f"[{time.perf_counter() - _T0:7.1f}s] {msg}", file=sys.stderr, flush=True)
 
 
 def attn_flops(nq, nk, d, h):
@@ -381,9 +385,93 @@ def fp8_main(args):
     return 0
 
 
+def gpu_refresh_bench(args, Hl, Wl, W, H, d, n_layers, n_steps=4):
+    """The clean-cache baseline the pipeline replaces (NFE 5): per block, n_steps denoise
+    passes attend to one shared clean cache without writing it (LA_STEP_ATTEND_ONLY), then a
+    refresh pass at noise level 0 writes the block's K/V into it."""
+    import torch
+    import streaming_causal_video_amd as L
+
+    L.lib()
+    dev = "cuda"
+    bt, st = FRAMES * Hl * Wl, Hl * Wl
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(777)
+
+    def randn(shape, dtype=torch.bfloat16):
+        return torch.randn(shape, device=dev, dtype=torch.float32, generator=gen).to(dtype)
+
+    log(f"setup: clean-cache baseline, {n_layers} layers, {n_steps} attend-only passes + refresh")
+    stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, 0.0)
+    for l in range(n_layers):
+        stack.sink_k_raw[l].copy_(randn((st, H, d)))
+        stack.sink_v[l].copy_(randn((st, H, d)))
+    pool = 2
+    ins = [[tuple(randn((bt, H, d)) for _ in range(3)) for _ in range(n_layers)] for _ in range(pool)]
+    log("inputs ready")
+    outs = [torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
+    qws = torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev)
+    kws = torch.empty_like(qws)
+    sws = torch.empty((st, H, d), dtype=torch.bfloat16, device=dev)
+    table = torch.empty(L.la_rope_table_bytes(Hl, Wl, d) // 4, dtype=torch.float32, device=dev)
+    L.la_rope_table_fill(table, Hl, Wl, d, THETA)
+    lat_shape = (16, 3, 60, 104)
+    x = torch.randn(lat_shape, device=dev, generator=gen)
+    vels = [torch.randn(lat_shape, device=dev, generator=gen) for _ in range(n_steps)]
+    torch.cuda.synchronize()
+
+    def step(b):
+        e = b % pool
+        q = [ins[e][l][0] for l in range(n_layers)]
+        k = [ins[e][l][1] for l in range(n_layers)]
+        v = [ins[e][l][2] for l in range(n_layers)]
+        for i in range(n_steps):
+            L.la_denoise_step(stack.states, b, q, k, v, outs, qws, kws, sws, table, Hl, Wl, FRAMES,
+                              DELTA, THETA, x=x, vel=vels[i], dt=DT, flags=L.LA_STEP_ATTEND_ONLY)
+        L.la_denoise_step(stack.states, b, q, k, v, outs, qws, kws, sws, table, Hl, Wl, FRAMES,
+                          DELTA, THETA, sink_k_new=[t[:st] for t in k] if b == 1 else None,
+                          sink_v_new=[t[:st] for t in v] if b == 1 else None)
+
+    block = 0
+    for _ in range(W + args.warmup):
+        block += 1
+        step(block)
+        torch.cuda.synchronize()
+        log(f"warm-up block {block} done")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        block += 1
+        step(block)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    log(f"clean-cache baseline: {ms:.3f} ms/block ({n_steps} attend-only passes + 1 refresh)")
+    return {"ms_per_step": ms, "blocks_per_s": 1e3 / ms}
+
+
+def refresh_main(args):
+    """--workload refresh: blocks/s of the NFE-5 clean-cache baseline on one GPU."""
+    geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=args.layers or 40)
+    r = gpu_refresh_bench(args, **geo)
+    out = {
+        "metric": "clean-cache baseline blocks/s at 1 GPU (4 attend-only passes + 1 refresh, NFE 5)",
+        "value": round(r["blocks_per_s"], 4), "unit": "blocks/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0,1) Q/K/V, sinks, latent and velocities resident in HBM (no trained weights)",
+        "config": {"workload": ("C4 shapes, 40 layers: 4 denoise passes attending to a shared clean "
+                                "cache (W=4) + 1 refresh pass writing it, per block"),
+                   "layers": geo["n_layers"], "nfe": 5, "parallelism": "none"},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def chain_main(args):
     """--workload chain: blocks/s of a complete 4-step denoise on one GPU."""
-    geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
+    geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=args.layers or 40)
     r = gpu_chain_bench(args, **geo)
     out = {
         "metric": "denoise-chain blocks/s at 1 GPU (4 timestep-forcing stages in sequence)",
@@ -416,8 +504,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["c4", "c2", "c5", "chain", "c2fp8"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c2", "c5", "chain", "c2fp8", "refresh"],
+                    default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers per stage for the chain / refresh workloads (default 40)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -428,7 +519,14 @@ def main():
         print("bench.py is single-process; WORLD_SIZE > 1 is not supported.", file=sys.stderr)
         return 2
 
-    if args.workload in ("c4", "chain"):
+    # workloads with their own driver (they take --steps as given)
+    if args.workload == "chain":
+        return chain_main(args)
+    if args.workload == "c2fp8":
+        return fp8_main(args)
+    if args.workload == "refresh":
+        return refresh_main(args)
+    if args.workload == "c4":
         geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
         name = ("C4 full denoise step: 40 layers x (3D Rolling RoPE + bf16 block attention "
                 "40x128, Nq 4680, Nk 24960 + ring append/evict, W=4, 1560-token sink) + "
@@ -436,16 +534,14 @@ def main():
     elif args.workload == "c2":
         geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=1)
         name = "C2 one layer: bf16 block attention 40x128, Nq 4680, Nk 24960 (+RoPE, append, Euler)"
-    else:
+    elif args.workload == "c5":
         geo = dict(Hl=44, Wl=80, W=4, H=40, d=128, n_layers=1)
         name = ("C5 720p-shaped layer: 44x80 tokens/frame, Nq 10560, Nk 56320 (sink + 4 cached "
                 "blocks + block), streamed blocks")
         if args.steps == 10:
             args.steps = 1000
-    if args.workload == "chain":
-        return chain_main(args)
-    if args.workload == "c2fp8":
-        return fp8_main(args)
+    else:
+        raise AssertionError(args.workload)
     r = gpu_step_bench(args, **geo)
     import streaming_causal_video_amd as L
     version = L.la_version().split()[-1]

@@ -255,6 +255,17 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *      (sink_k_new[l], sink_v_new[l]) (Adaptive Attention Sink, NOTES 关键设计 3);
  * then la_fm_euler_step(x, vel, n_latent, dt) if x != NULL.
  *
+ * flags (bitwise or):
+ *   LA_STEP_ATTEND_ONLY : skip steps 3 and 4 (no append, no sink replacement);
+ *       the rings are read, not written.  For the pages' cache ablations (NOTES,
+ *       Table 4: a clean cache instead of the step's own noisy one; NOTES,
+ *       关键发现 on Table 6: a fixed-noise cache): the denoise stages attend to a
+ *       shared cache that one other pass writes (a clean refresh pass at noise
+ *       level 0, NFE 5, or the stage at the fixed level).  sink_k_new must be NULL.
+ * The other ablations need no flag: Rolling RoPE off = pass sink_delta =
+ * p_sink - f0 (the sink stays at p_sink, e.g. frame 0); AAS off = never pass a
+ * replacement sink.
+ *
  *   rings[n_layers]        : one la_kvring per layer, identical geometry and
  *                            noise level, all at last_block == block_id - 1.
  *   q_raw/k_raw/v_raw/attn_out : arrays of n_layers device pointers, each
@@ -282,8 +293,10 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                           int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
                           double theta, float scale, float* x, const float* vel,
-                          int64_t n_latent, float dt, void* const* timing_events,
-                          la_stream_t stream);
+                          int64_t n_latent, float dt, uint32_t flags,
+                          void* const* timing_events, la_stream_t stream);
+
+#define LA_STEP_ATTEND_ONLY 1u
 
 /*
  * la_quantize_fp8 - per-tensor FP8 quantisation (NOTES, Table 3: FP8

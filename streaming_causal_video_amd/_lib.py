@@ -20,6 +20,7 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_STATE, LA_ERR_NOIS
     LA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 LA_BF16, LA_F32, LA_FP8_E4M3 = 0, 1, 2
 LA_MAX_WINDOW = 64
+LA_STEP_ATTEND_ONLY = 1
 LA_MAX_BLOCK_FRAMES = 4
 
 EXPORTED = [
@@ -133,7 +134,7 @@ def _load():
         "la_fm_euler_step": (ctypes.c_int, [VP, VP, I64, F, VP]),
         "la_denoise_step": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP, VP,
                                            P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, VP,
-                                           I64, F, P(VP), VP]),
+                                           I64, F, ctypes.c_uint32, P(VP), VP]),
         "la_quantize_fp8": (ctypes.c_int, [VP, ctypes.c_int, VP, I64, F, VP]),
         "la_block_attn_fwd_fp8": (ctypes.c_int, [R, VP, VP, VP, VP, VP, I32, VP, VP, F, F, F, F,
                                                  VP]),
@@ -348,10 +349,10 @@ def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_w
                     sink_k_rot_ws, rope_table, Hl: int, Wl: int, frames_per_block: int = 3,
                     sink_delta: int = -1, theta: float = 10000.0, scale: Optional[float] = None,
                     sink_k_new=None, sink_v_new=None, x=None, vel=None, dt: float = -0.25,
-                    timing_events=None) -> None:
+                    timing_events=None, flags: int = 0) -> None:
     """rings: a ctypes array of la_kvring (see KVRingStack); the other per-layer
     arguments are lists of tensors.  timing_events: None or a ctypes array of
-    6*len(rings)+2 raw hipEvent_t handles."""
+    6*len(rings)+2 raw hipEvent_t handles.  flags: LA_STEP_ATTEND_ONLY or 0."""
     n = len(rings)
     if scale is None:
         scale = rings[0].head_dim ** -0.5
@@ -365,7 +366,8 @@ def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_w
         _ptr_array(v_raw, "v_raw"), _ptr_array(attn_out, "attn_out"), _ptr(q_rot_ws, "q_rot_ws"),
         _ptr(k_rot_ws, "k_rot_ws"), _ptr(sink_k_rot_ws, "sink_k_rot_ws"), skn, svn,
         _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta, scale,
-        _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, timing_events, _stream()), "la_denoise_step")
+        _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, flags, timing_events, _stream()),
+        "la_denoise_step")
 
 
 def la_denoise_chain(stages, block_id: int, q_rot_ws, k_rot_ws, sink_k_rot_ws, rope_table,

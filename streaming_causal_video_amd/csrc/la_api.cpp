@@ -347,10 +347,12 @@ la_status validate_stage(const la_kvring* rings, int32_t n_layers, int64_t block
                          const void* const* q_raw, const void* const* k_raw,
                          const void* const* v_raw, void* const* attn_out,
                          const void* const* sink_k_new, const void* const* sink_v_new,
-                         int32_t Hl, int32_t Wl, int32_t frames_per_block) {
+                         int32_t Hl, int32_t Wl, int32_t frames_per_block, uint32_t flags) {
   if (!rings || n_layers < 1 || !q_raw || !k_raw || !v_raw || !attn_out)
     return LA_ERR_INVALID_ARG;
   if ((!sink_k_new) != (!sink_v_new)) return LA_ERR_INVALID_ARG;
+  if (flags & ~LA_STEP_ATTEND_ONLY) return LA_ERR_INVALID_ARG;
+  if ((flags & LA_STEP_ATTEND_ONLY) && sink_k_new) return LA_ERR_INVALID_ARG;
   if (frames_per_block < 1 || frames_per_block > LA_MAX_BLOCK_FRAMES || Hl < 1 || Wl < 1)
     return LA_ERR_SHAPE;
   const la_kvring& r0 = rings[0];
@@ -382,7 +384,8 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
                         const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                         int32_t Wl, int32_t frames_per_block, int64_t sink_delta, double theta,
                         float scale, float* x, const float* vel, int64_t n_latent, float dt,
-                        void* const* timing_events, la_stream_t stream) {
+                        uint32_t flags, void* const* timing_events, la_stream_t stream) {
+  const bool append = !(flags & LA_STEP_ATTEND_ONLY);
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> la_status {
@@ -406,9 +409,10 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
                              attn_out[l], nullptr, scale, stream));
     LA_TRY(mark(6 * l + 3));
     LA_TRY(mark(6 * l + 4));
-    LA_TRY(la_kvcache_append_evict(r, k_rot_ws, v_raw[l], block_id, r->noise_level, nullptr,
-                                   stream));
-    if (block_id == 1 && sink_k_new)
+    if (append)
+      LA_TRY(la_kvcache_append_evict(r, k_rot_ws, v_raw[l], block_id, r->noise_level, nullptr,
+                                     stream));
+    if (append && block_id == 1 && sink_k_new)
       LA_TRY(la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream));
     LA_TRY(mark(6 * l + 5));
   }
@@ -430,12 +434,12 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                           int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
                           double theta, float scale, float* x, const float* vel,
-                          int64_t n_latent, float dt, void* const* timing_events,
-                          la_stream_t stream) {
+                          int64_t n_latent, float dt, uint32_t flags,
+                          void* const* timing_events, la_stream_t stream) {
   // ---- validate the whole step before enqueuing anything
   if (!q_rot_ws || !k_rot_ws || !sink_k_rot_ws || !rope_table) return LA_ERR_INVALID_ARG;
   const la_status v = validate_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out,
-                                     sink_k_new, sink_v_new, Hl, Wl, frames_per_block);
+                                     sink_k_new, sink_v_new, Hl, Wl, frames_per_block, flags);
   if (v != LA_OK) return v;
   if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
   if (timing_events)
@@ -444,7 +448,7 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
   return enqueue_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out, q_rot_ws,
                        k_rot_ws, sink_k_rot_ws, sink_k_new, sink_v_new, rope_table, Hl, Wl,
                        frames_per_block, sink_delta, theta, scale, x, vel, n_latent, dt,
-                       timing_events, stream);
+                       flags, timing_events, stream);
 }
 
 la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
@@ -460,7 +464,7 @@ la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
     const la_stage& g = stages[s];
     const la_status v = validate_stage(g.rings, n_layers, block_id, g.q_raw, g.k_raw, g.v_raw,
                                        g.attn_out, g.sink_k_new, g.sink_v_new, Hl, Wl,
-                                       frames_per_block);
+                                       frames_per_block, 0u);
     if (v != LA_OK) return v;
     if (!isfinite(g.dt) || (n_latent > 0 && !g.vel)) return LA_ERR_INVALID_ARG;
     if (g.rings[0].head_dim != stages[0].rings[0].head_dim ||
@@ -484,7 +488,7 @@ la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
                                        g.sink_k_new, g.sink_v_new, rope_table, Hl, Wl,
                                        frames_per_block, sink_delta, theta, scale,
                                        n_latent > 0 ? x : nullptr, g.vel, n_latent, g.dt,
-                                       nullptr, stream);
+                                       0u, nullptr, stream);
     if (st != LA_OK) return st;
   }
   return LA_OK;

@@ -254,7 +254,7 @@ def test_fp8_ring_and_entry_point_refusals():
     assert lib.la_block_attn_fwd(ctypes.byref(r8), p, p, p, p, 48, out, None, 0.1, None) == _lib.LA_ERR_DTYPE
     qarr = (ctypes.c_void_p * 1)(0x50000)
     assert lib.la_denoise_step(ctypes.byref(r8), 1, 1, qarr, qarr, qarr, qarr, p, p, p, None, None,
-                               p, 4, 4, 3, -1, 1e4, 0.1, None, None, 0, -0.25, None,
+                               p, 4, 4, 3, -1, 1e4, 0.1, None, None, 0, -0.25, 0, None,
                                None) == _lib.LA_ERR_DTYPE
     # la_block_attn_fwd_fp8: wrong ring dtype, head_dim, factors, alignment, aliasing
     rb = make_ring(2)
@@ -279,3 +279,19 @@ def test_fp8_ring_and_entry_point_refusals():
     assert q(ctypes.c_void_p(0x70002), L.LA_BF16, out, 16, 1.0, None) == _lib.LA_ERR_INVALID_ARG
     assert q(p, L.LA_F32, ctypes.c_void_p(0x70010), 16, 1.0, None) == _lib.LA_ERR_INVALID_ARG  # overlap
     assert q(None, L.LA_BF16, out, 16, 1.0, None) == _lib.LA_ERR_INVALID_ARG
+
+
+def test_denoise_step_flag_refusals():
+    """Unknown flag bits, and a replacement sink with LA_STEP_ATTEND_ONLY, are refused."""
+    lib = L.lib()
+    p = ctypes.c_void_p(0x70000)
+    rings = (_lib.la_kvring * 1)()
+    L.la_kvring_init(rings[0], 0x10000, 0x20000, 0x30000, 0x40000, 2, 48, 16, 2, 128, L.LA_BF16, 0.5)
+    arr = (ctypes.c_void_p * 1)(0x50000)
+    before = bytes(rings[0])
+    call = lambda flags, sink: lib.la_denoise_step(rings, 1, 1, arr, arr, arr, arr, p, p, p, sink,
+                                                   sink, p, 4, 4, 3, -1, 1e4, 0.1, None, None, 0,
+                                                   -0.25, flags, None, None)
+    assert call(2, None) == _lib.LA_ERR_INVALID_ARG
+    assert call(L.LA_STEP_ATTEND_ONLY, arr) == _lib.LA_ERR_INVALID_ARG
+    assert bytes(rings[0]) == before
