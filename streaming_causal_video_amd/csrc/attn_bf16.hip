@@ -7,14 +7,18 @@
 // block attends to the sink frame and to the sliding noisy KV cache).
 //
 // Design (MI355X-first, not a port of the pages' FlashAttention):
-//  * One workgroup = 4 waves = 128 query rows of one head; each wave owns 32
-//    query rows for the whole key range and keeps its Q fragments, the running
-//    row max / row sum and the output accumulator in registers.
+//  * One workgroup = 8 waves (two per SIMD) = 256 query rows of one head; each
+//    wave owns 32 query rows for the whole key range and keeps its Q fragments,
+//    the running row max / row sum and the output accumulator in registers.
+//    The K/V tile a workgroup stages in LDS serves 256 queries: the global
+//    loads per query (measured to cost a quarter of the kernel's time at 128
+//    queries per workgroup, whether they hit L2 or not) are halved.
 //  * Keys are walked as one virtual range over the segment table, 64 keys per
 //    tile, so tiles straddle segment boundaries and only the very last tile
 //    can be partial.  K and V tiles are staged global -> registers -> LDS,
 //    double buffered, one barrier per tile; the next tile's global loads are in
-//    flight while the current tile is computed.
+//    flight while the current tile is computed.  Waves 0-3 load V, waves 4-7 K
+//    (four 16-byte loads per thread per tile).
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: in the 32x32 result each lane holds one query
 //    (lane % 32) and half of the tile's keys, so the row max needs one
@@ -54,9 +58,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
-constexpr int BM = 128;  // query rows per workgroup
+constexpr int BM = 256;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int KP = 136;  // K row pitch in LDS (bf16): 272 B, 16 rows hit 16 disjoint bank quads
 constexpr int VTP = 72;  // V^T row pitch in LDS (bf16): 144 B, 16 rows hit 16 disjoint bank quads
@@ -126,23 +130,24 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   float m_run = -INFINITY;  // running max of scale*log2(e)*score
   float l_run = 0.f;        // this lane's half of the running row sum
 
-  // Loader.  K: thread covers 16-byte chunk lcc of tile rows lr0 + 16 i (16 lanes
-  // read one 256-byte row).  V: thread covers 16-byte chunk vc (dims 8 vc .. 8 vc + 7)
-  // of tile rows 4 kq + i (a wave reads 64 contiguous bytes of every row) and
-  // writes it transposed.
-  const int lcc = tid & 15;
-  const int lr0 = tid >> 4;
+  // Loader.  Waves 4-7 load K: thread covers 16-byte chunk lcc of tile rows
+  // lr0 + 16 i (16 lanes read one 256-byte row).  Waves 0-3 load V: thread covers
+  // 16-byte chunk vc (dims 8 vc .. +7) of tile rows 4 kq + i (a wave reads 64
+  // contiguous bytes of every row) and writes it transposed.
+  const bool kloader = __builtin_amdgcn_readfirstlane(wave) >= 4;
+  const int ltid = tid & 255;
+  const int lcc = ltid & 15;
+  const int lr0 = ltid >> 4;
   const int kq = lane & 15;
-  const int vc = 4 * wave + (lane >> 4);
+  const int vc = 4 * (wave & 3) + (lane >> 4);
   const int ntiles = (nk + BN - 1) / BN;
   const uint32_t rs_bytes = (uint32_t)rs * 2u;
-  uint32_t koff[4], voff[4];
+  uint32_t off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    koff[i] = (uint32_t)(lr0 + 16 * i) * rs_bytes + (uint32_t)(head * D * 2 + lcc * 16);
-    voff[i] = (uint32_t)(4 * kq + i) * rs_bytes + (uint32_t)(head * D * 2 + vc * 16);
-  }
-  uint4 kreg[4], vreg[4];
+  for (int i = 0; i < 4; ++i)
+    off[i] = kloader ? (uint32_t)(lr0 + 16 * i) * rs_bytes + (uint32_t)(head * D * 2 + lcc * 16)
+                     : (uint32_t)(4 * kq + i) * rs_bytes + (uint32_t)(head * D * 2 + vc * 16);
+  uint4 reg[4];
   int seg = 0;  // segment holding the first key of the tile being loaded (scalar)
 
   auto gload = [&](int tile) {
@@ -152,13 +157,9 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     if (t0 + BN <= segs.end[seg]) {
       // whole tile inside one segment: scalar base + precomputed 32-bit offsets
       const uint32_t sbase = (uint32_t)(t0 - start) * rs_bytes;
-      const char* kb = static_cast<const char*>(segs.k[seg]) + sbase;
-      const char* vb = static_cast<const char*>(segs.v[seg]) + sbase;
+      const char* b = static_cast<const char*>(kloader ? segs.k[seg] : segs.v[seg]) + sbase;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kreg[i] = *reinterpret_cast<const uint4*>(kb + koff[i]);
-        vreg[i] = *reinterpret_cast<const uint4*>(vb + voff[i]);
-      }
+      for (int i = 0; i < 4; ++i) reg[i] = *reinterpret_cast<const uint4*>(b + off[i]);
     } else {
       // straddles a segment boundary or runs past the last key: per-row lookup,
       // rows past the last key are clamped to it (their scores are masked)
@@ -167,40 +168,45 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
         int s = seg;
         while (key >= segs.end[s]) ++s;
         const int st = s ? segs.end[s - 1] : 0;
-        const int64_t off = (int64_t)(key - st) * rs + head * D + chunk * 8;
+        const int64_t o = (int64_t)(key - st) * rs + head * D + chunk * 8;
         const uint16_t* base = static_cast<const uint16_t*>(is_v ? segs.v[s] : segs.k[s]);
-        return *reinterpret_cast<const uint4*>(base + off);
+        return *reinterpret_cast<const uint4*>(base + o);
       };
-      kreg[0] = row_load(lr0, lcc, false);
-      kreg[1] = row_load(lr0 + 16, lcc, false);
-      kreg[2] = row_load(lr0 + 32, lcc, false);
-      kreg[3] = row_load(lr0 + 48, lcc, false);
-      vreg[0] = row_load(4 * kq, vc, true);
-      vreg[1] = row_load(4 * kq + 1, vc, true);
-      vreg[2] = row_load(4 * kq + 2, vc, true);
-      vreg[3] = row_load(4 * kq + 3, vc, true);
+      if (kloader) {
+        reg[0] = row_load(lr0, lcc, false);
+        reg[1] = row_load(lr0 + 16, lcc, false);
+        reg[2] = row_load(lr0 + 32, lcc, false);
+        reg[3] = row_load(lr0 + 48, lcc, false);
+      } else {
+        reg[0] = row_load(4 * kq, vc, true);
+        reg[1] = row_load(4 * kq + 1, vc, true);
+        reg[2] = row_load(4 * kq + 2, vc, true);
+        reg[3] = row_load(4 * kq + 3, vc, true);
+      }
     }
   };
   auto lstore = [&](int buf) {
     uint16_t* kb = lds + buf * STAGE;
     uint16_t* vt = kb + KBUF;
+    if (kloader) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(kb + (lr0 + 16 * i) * KP + lcc * 8) = kreg[i];
-    // V^T[8 vc + j][4 kq .. 4 kq + 3]: pairs of keys packed per dword
-    const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
-                              {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
-                              {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
-                              {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(kb + (lr0 + 16 * i) * KP + lcc * 8) = reg[i];
+    } else {
+      // V^T[8 vc + j][4 kq .. 4 kq + 3]: pairs of keys packed per dword
+      const uint32_t w[4][4] = {{reg[0].x, reg[0].y, reg[0].z, reg[0].w},
+                                {reg[1].x, reg[1].y, reg[1].z, reg[1].w},
+                                {reg[2].x, reg[2].y, reg[2].z, reg[2].w},
+                                {reg[3].x, reg[3].y, reg[3].z, reg[3].w}};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // dims 8 vc + 2 m (low halves) and 8 vc + 2 m + 1 (high halves)
-      const uint2 even = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
-                                    __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
-      const uint2 odd = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
-                                   __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
-      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m) * VTP + 4 * kq) = even;
-      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m + 1) * VTP + 4 * kq) = odd;
+      for (int m = 0; m < 4; ++m) {
+        const uint2 even = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
+                                      __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
+        const uint2 odd = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
+                                     __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
+        *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m) * VTP + 4 * kq) = even;
+        *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m + 1) * VTP + 4 * kq) = odd;
+      }
     }
   };
 
