@@ -10,6 +10,10 @@
 // Design (gfx950-native; shares the workgroup shape of the bf16 kernel):
 //  * 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in LDS,
 //    one barrier per tile, Q fragments and the output accumulator in registers.
+//    Three waves per SIMD (<= 168 registers, 39 KB of LDS per workgroup): this
+//    kernel is bound by its softmax VALU work, which more resident waves hide
+//    better (measured 1.85 ms vs 1.94 ms with two; a 256-query workgroup, which
+//    halves the K/V loads per query, was slower here: 2.20 ms).
 //  * Both products run on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, float32
 //    accumulate): S^T = K Q^T is 4 MFMAs per tile, O^T += V^T P^T another 4.
 //  * The MFMA takes A[i][k] and B[k][j] from lane bytes under one fixed (lane,
@@ -82,7 +86,7 @@ __device__ __forceinline__ f32x16_t mma(const i32x8_t& a, const i32x8_t& b, cons
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
-                          amdgpu_waves_per_eu(2, 2))) void
+                          amdgpu_waves_per_eu(3, 3))) void
 attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
                 float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
                 float c2, float dv, float ln_scale, int qtiles, int nwg) {
