@@ -42,8 +42,11 @@
 //    a handful of tiles instead of every tile.  Exact: numerator and
 //    denominator use the same reference max; P stays <= 256.
 //  * Loader: per-thread 32-bit row offsets are computed once; per tile only a
-//    scalar segment base changes.  Tiles that straddle a segment boundary or
-//    run past the last key take a slower per-row path with zero fill.
+//    scalar segment base changes, and the current segment's key range and
+//    base pointers stay in scalar registers (the segment table in kernel
+//    arguments is read only when a tile enters the next segment: a scalar load
+//    would also wait for all LDS reads in flight).  Tiles that straddle a
+//    segment boundary or run past the last key take a slower per-row path.
 //  * Workgroups are renumbered so that all query tiles of a head run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 while
 //    they stream the head's K/V.
@@ -148,16 +151,27 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     off[i] = kloader ? (uint32_t)(lr0 + 16 * i) * rs_bytes + (uint32_t)(head * D * 2 + lcc * 16)
                      : (uint32_t)(4 * kq + i) * rs_bytes + (uint32_t)(head * D * 2 + vc * 16);
   uint4 reg[4];
-  int seg = 0;  // segment holding the first key of the tile being loaded (scalar)
+  // Segment holding the first key of the tile being loaded, with its key range
+  // and base pointers kept in scalar registers: the segment table is read only
+  // when a tile crosses into the next segment (a scalar load would also wait
+  // for every LDS read in flight).
+  int seg = 0, seg_start = 0, seg_end = segs.end[0];
+  const char* seg_k = static_cast<const char*>(segs.k[0]);
+  const char* seg_v = static_cast<const char*>(segs.v[0]);
 
-  auto gload = [&](int tile) {
+  auto gload = [&](int tile) __attribute__((always_inline)) {
     const int t0 = tile * BN;
-    while (t0 >= segs.end[seg]) ++seg;
-    const int start = seg ? segs.end[seg - 1] : 0;
-    if (t0 + BN <= segs.end[seg]) {
+    while (t0 >= seg_end) {
+      ++seg;
+      seg_start = seg_end;
+      seg_end = segs.end[seg];
+      seg_k = static_cast<const char*>(segs.k[seg]);
+      seg_v = static_cast<const char*>(segs.v[seg]);
+    }
+    if (t0 + BN <= seg_end) {
       // whole tile inside one segment: scalar base + precomputed 32-bit offsets
-      const uint32_t sbase = (uint32_t)(t0 - start) * rs_bytes;
-      const char* b = static_cast<const char*>(kloader ? segs.k[seg] : segs.v[seg]) + sbase;
+      const uint32_t sbase = (uint32_t)(t0 - seg_start) * rs_bytes;
+      const char* b = (kloader ? seg_k : seg_v) + sbase;
 #pragma unroll
       for (int i = 0; i < 4; ++i) reg[i] = *reinterpret_cast<const uint4*>(b + off[i]);
     } else {

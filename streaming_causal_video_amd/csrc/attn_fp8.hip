@@ -146,17 +146,28 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     voff[t] = (uint32_t)(4 * kq + t) * rs32 + (uint32_t)(head * D + vc * 8);
   uint4 kreg[2];
   uint2 vreg[4];
-  int seg = 0;  // segment holding the first key of the tile being loaded (scalar)
+  // Segment holding the first key of the tile being loaded, with its key range
+  // and base pointers kept in scalar registers: the segment table is read only
+  // when a tile crosses into the next segment (a scalar load would also wait
+  // for every LDS read in flight).
+  int seg = 0, seg_start = 0, seg_end = segs.end[0];
+  const uint8_t* seg_k = static_cast<const uint8_t*>(segs.k[0]);
+  const uint8_t* seg_v = static_cast<const uint8_t*>(segs.v[0]);
 
   auto gload = [&](int tile) {
     const int t0 = tile * BN;
-    while (t0 >= segs.end[seg]) ++seg;
-    const int start = seg ? segs.end[seg - 1] : 0;
-    if (t0 + BN <= segs.end[seg]) {
+    while (t0 >= seg_end) {
+      ++seg;
+      seg_start = seg_end;
+      seg_end = segs.end[seg];
+      seg_k = static_cast<const uint8_t*>(segs.k[seg]);
+      seg_v = static_cast<const uint8_t*>(segs.v[seg]);
+    }
+    if (t0 + BN <= seg_end) {
       // whole tile inside one segment: scalar base + precomputed 32-bit offsets
-      const uint32_t sbase = (uint32_t)(t0 - start) * rs32;
-      const uint8_t* kb = static_cast<const uint8_t*>(segs.k[seg]) + sbase;
-      const uint8_t* vb = static_cast<const uint8_t*>(segs.v[seg]) + sbase;
+      const uint32_t sbase = (uint32_t)(t0 - seg_start) * rs32;
+      const uint8_t* kb = seg_k + sbase;
+      const uint8_t* vb = seg_v + sbase;
 #pragma unroll
       for (int i = 0; i < 2; ++i) kreg[i] = *reinterpret_cast<const uint4*>(kb + koff[i]);
 #pragma unroll
