@@ -46,7 +46,7 @@ DT = -0.25
 # from rocprofv3 FETCH_SIZE/WRITE_SIZE runs scaled by a copy kernel of known size,
 # keyed by the attention kernel version the library reports; any other version
 # reports null (the counters were taken on a different kernel).
-ATTN_TRAFFIC_BYTES = {"attn-v5": 8.117e8}
+ATTN_TRAFFIC_BYTES = {"attn-v5s": 8.118e8}
 
 
 _T0 = time.perf_counter()
