@@ -10,10 +10,15 @@
 // Design (gfx950-native; shares the workgroup shape of the bf16 kernel):
 //  * 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in LDS,
 //    one barrier per tile, Q fragments and the output accumulator in registers.
-//    Three waves per SIMD (<= 168 registers, 39 KB of LDS per workgroup): this
-//    kernel is bound by its softmax VALU work, which more resident waves hide
-//    better (measured 1.85 ms vs 1.94 ms with two; a 256-query workgroup, which
-//    halves the K/V loads per query, was slower here: 2.20 ms).
+//    Two waves per SIMD (<= 256 registers, 39 KB of LDS per workgroup).  At
+//    three per SIMD (168 registers) the loop-invariant addresses spilled to
+//    scratch, and the reload after each barrier waited (one in-order counter)
+//    for the next tile's prefetch as well: 1.82 ms against 1.58 ms here.
+//  * Tile loads are buffer loads from a scalar descriptor (segment base + tile
+//    row + head, record count = the segment's remaining bytes) with one lane
+//    offset for K and one for V; the other rows of a thread differ by uniform
+//    multiples of the row stride, passed as the scalar offset.  No 64-bit
+//    address registers, and a wrong offset reads zeros instead of faulting.
 //  * Both products run on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, float32
 //    accumulate): S^T = K Q^T is 4 MFMAs per tile, O^T += V^T P^T another 4.
 //  * The MFMA takes A[i][k] and B[k][j] from lane bytes under one fixed (lane,
@@ -47,6 +52,9 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;  // head_dim = bytes per row
 constexpr int BM = 128;  // query rows per workgroup
+// Third descriptor word of a raw buffer resource on gfx9 (32-bit data format,
+// no swizzle): the same value the ROCm libraries use for gfx90a/gfx942/gfx950.
+constexpr int kBufWord3 = 0x00020000;
 constexpr int BN = 64;   // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
@@ -86,7 +94,7 @@ __device__ __forceinline__ f32x16_t mma(const i32x8_t& a, const i32x8_t& b, cons
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
-                          amdgpu_waves_per_eu(3, 3))) void
+                          amdgpu_waves_per_eu(2, 2))) void
 attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
                 float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
                 float c2, float dv, float ln_scale, int qtiles, int nwg) {
@@ -137,13 +145,11 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
   const int vc = tid >> 4;
   const int ntiles = (nk + BN - 1) / BN;
   const uint32_t rs32 = (uint32_t)rs;
-  uint32_t koff[2], voff[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    koff[i] = (uint32_t)(kr0 + 32 * i) * rs32 + (uint32_t)(head * D + kc * 16);
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    voff[t] = (uint32_t)(4 * kq + t) * rs32 + (uint32_t)(head * D + vc * 8);
+  // Lane offsets of the tile loads relative to the tile's first row of this
+  // head; the other rows of a thread are uniform multiples of the row stride
+  // (passed as the buffer loads' scalar offset).
+  const uint32_t koff = (uint32_t)kr0 * rs32 + (uint32_t)(kc * 16);
+  const uint32_t voff = (uint32_t)(4 * kq) * rs32 + (uint32_t)(vc * 8);
   uint4 kreg[2];
   uint2 vreg[4];
   // Segment holding the first key of the tile being loaded, with its key range
@@ -164,14 +170,25 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
       seg_v = static_cast<const uint8_t*>(segs.v[seg]);
     }
     if (t0 + BN <= seg_end) {
-      // whole tile inside one segment: scalar base + precomputed 32-bit offsets
-      const uint32_t sbase = (uint32_t)(t0 - seg_start) * rs32;
-      const uint8_t* kb = seg_k + sbase;
-      const uint8_t* vb = seg_v + sbase;
+      // whole tile inside one segment: buffer loads from a scalar base with the
+      // precomputed 32-bit offsets (no 64-bit address registers); the record
+      // count ends the descriptor at the segment's end
+      const uint32_t sbase = (uint32_t)(t0 - seg_start) * rs32 + (uint32_t)(head * D);
+      const uint32_t nbytes = (uint32_t)(seg_end - t0) * rs32 - (uint32_t)(head * D);
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) kreg[i] = *reinterpret_cast<const uint4*>(kb + koff[i]);
+      for (int i = 0; i < 2; ++i) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 32 * i * rs32, 0);
+        kreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) vreg[t] = *reinterpret_cast<const uint2*>(vb + voff[t]);
+      for (int t = 0; t < 4; ++t) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(vr, voff, t * rs32, 0);
+        vreg[t] = make_uint2(x[0], x[1]);
+      }
     } else {
       // straddles a segment boundary or runs past the last key: per-row lookup,
       // rows past the last key are clamped to it (their scores are masked)
