@@ -82,28 +82,35 @@ class Fp8Stream:
     rotated projections) are quantised on the GPU with fixed per-tensor scales, the block
     attends to [sink ; window ; itself], then its K/V codes are appended."""
 
-    def __init__(self, L, shape, layer=0):
+    def __init__(self, L, shape, layer=0, scale=SCALE_QKV, qk_mult=1.0):
         t = torch()
         self.L, self.s, self.layer = L, shape, layer
+        self.scale, self.qk_mult = scale, qk_mult
         s = shape
         self.ring = L.KVRing(s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, t.uint8, 0.75)
         sk, sv = s.initial_sink(layer)
-        self.sink_k8 = gpu_quant(L, to_dev(sk), SCALE_QKV)
-        self.sink_v8 = gpu_quant(L, to_dev(sv), SCALE_QKV)
-        self.codes = {"sink": (quantize(sk.values.astype(np.float32), SCALE_QKV),
-                               quantize(sv.values.astype(np.float32), SCALE_QKV))}
+        sk = self._mult(sk)
+        self.sink_k8 = gpu_quant(L, to_dev(sk), scale)
+        self.sink_v8 = gpu_quant(L, to_dev(sv), scale)
+        self.codes = {"sink": (quantize(sk.values.astype(np.float32), scale),
+                               quantize(sv.values.astype(np.float32), scale))}
         self.out = t.empty((s.block_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
         self.lse = t.empty((s.heads, s.block_tokens), dtype=t.float32, device="cuda")
 
+    def _mult(self, x):
+        # Q and K times a power of two (exact in bf16): larger, peakier logits
+        return x if self.qk_mult == 1.0 else si.make_stored(x.values * self.qk_mult, "bf16")
+
     def step(self, b):
-        L, s = self.L, self.s
+        L, s, sc = self.L, self.s, self.scale
         q, k, v = s.block_inputs(self.layer, b)
-        q8, k8, v8 = (gpu_quant(L, to_dev(x), SCALE_QKV) for x in (q, k, v))
-        self.codes[b] = tuple(quantize(x.values.astype(np.float32), SCALE_QKV) for x in (q, k, v))
+        q, k = self._mult(q), self._mult(k)
+        q8, k8, v8 = (gpu_quant(L, to_dev(x), sc) for x in (q, k, v))
+        self.codes[b] = tuple(quantize(x.values.astype(np.float32), sc) for x in (q, k, v))
         for dev, ref in zip((q8, k8, v8), self.codes[b]):
             assert np.array_equal(dev.cpu().numpy(), ref), f"block {b}: codes differ"
         L.la_block_attn_fwd_fp8(self.ring.state, q8, self.sink_k8, self.sink_v8, k8, v8, self.out,
-                                SCALE_QKV, SCALE_QKV, SCALE_QKV, lse=self.lse)
+                                sc, sc, sc, lse=self.lse)
         L.la_kvcache_append_evict(self.ring.state, k8, v8, b, 0.75)
 
     def reference(self, b, rows=None, heads=None):
@@ -115,12 +122,12 @@ class Fp8Stream:
         hs = slice(None) if heads is None else heads
         K8, V8 = np.concatenate(ks)[:, hs], np.concatenate(vs)[:, hs]
         Q8 = q8[:, hs] if rows is None else q8[rows][:, hs]
-        out, lse = attention_fp8(Q8, K8, V8, SCALE_QKV, SCALE_QKV, SCALE_QKV, s.head_dim ** -0.5)
+        sc = self.scale
+        out, lse = attention_fp8(Q8, K8, V8, sc, sc, sc, s.head_dim ** -0.5)
         # the same attention of |V|: bounds the effect of the probability rounding
-        absv = np.abs(dequantize(V8, SCALE_QKV))
+        absv = np.abs(dequantize(V8, sc))
         from oracle import attention_lse
-        bound_a, _ = attention_lse(dequantize(Q8, SCALE_QKV), dequantize(K8, SCALE_QKV), absv,
-                                   s.head_dim ** -0.5)
+        bound_a, _ = attention_lse(dequantize(Q8, sc), dequantize(K8, sc), absv, s.head_dim ** -0.5)
         return out, lse, bound_a, absv.max()
 
 
@@ -169,3 +176,50 @@ def test_fp8_attention_c2_sampled(L):
     got_lse = fs.lse.cpu().numpy().astype(np.float64)[heads][:, rows]
     assert np.abs(got_lse - lse).max() <= FP8_LSE
     say(f"fp8 C2 block {b}: rel-L2 {r:.4f}")
+
+
+def test_fp8_window_of_one_block(L):
+    shape = si.LayerShape(107, "bf16", heads=2, head_dim=128, Hl=6, Wl=11, W=1)
+    fs = Fp8Stream(L, shape)
+    for b in range(1, 5):
+        fs.step(b)
+        torch().cuda.synchronize()
+        out, lse, a, vmax = fs.reference(b)
+        check_fp8(to_f64(fs.out), out, a, vmax, f"W=1 block {b}")
+        assert np.abs(fs.lse.cpu().numpy().astype(np.float64) - lse).max() <= FP8_LSE
+
+
+def test_fp8_peaked_logits(L):
+    """Q and K times 4 (logit std ~16 after quantisation, scale 20/448 so nothing
+    saturates): the row max moves between tiles and segments, so the kernel raises its
+    reference max during the stream."""
+    shape = si.LayerShape(108, "bf16", heads=3, head_dim=128, Hl=10, Wl=13, W=2)
+    fs = Fp8Stream(L, shape, scale=20.0 / 448.0, qk_mult=4.0)
+    for b in range(1, shape.W + 3):
+        fs.step(b)
+        torch().cuda.synchronize()
+        out, lse, a, vmax = fs.reference(b)
+        r = check_fp8(to_f64(fs.out), out, a, vmax, f"peaked block {b}")
+        assert np.abs(fs.lse.cpu().numpy().astype(np.float64) - lse).max() <= FP8_LSE
+        say(f"fp8 peaked block {b}: rel-L2 {r:.4f}")
+
+
+@pytest.mark.timeout(900)
+def test_fp8_attention_c5_sampled(L):
+    """720p-shaped layer (Nk 56320 at block 5, eviction at 6), sampled rows of two heads."""
+    shape = si.C5
+    fs = Fp8Stream(L, shape)
+    rng = np.random.default_rng(19)
+    rows = np.unique(np.concatenate([[0, 255, 256, shape.block_tokens - 1],
+                                     rng.integers(0, shape.block_tokens, 40)]))
+    heads = [3, 38]
+    for b in range(1, shape.W + 3):
+        fs.step(b)
+        if b >= shape.W + 1:
+            torch().cuda.synchronize()
+            out, lse, a, vmax = fs.reference(b, rows=rows, heads=heads)
+            got = to_f64(fs.out)[rows][:, heads]
+            r = check_fp8(got, out, a, vmax, f"C5 fp8 block {b}")
+            got_lse = fs.lse.cpu().numpy().astype(np.float64)[heads][:, rows]
+            assert np.abs(got_lse - lse).max() <= FP8_LSE
+            say(f"fp8 C5 block {b}: rel-L2 {r:.4f}")
