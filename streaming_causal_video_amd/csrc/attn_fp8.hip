@@ -34,11 +34,16 @@
 //    4-key x 8-dim byte blocks) and stored as V^T rows of 64 bytes.
 //  * Softmax in float32 with scale * dq * dk * log2(e) folded into the exponent;
 //    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
-//    of the subnormal range; P <= 2^8 < 448 because the reference max is raised
-//    whenever a tile exceeds it by more than 2^2, so no clamp is needed).
+//    of the subnormal range).
 //  * The row sum is one more MFMA per tile, of an all-ones A operand with the
 //    same e4m3 P: it moves 32 additions per lane off the VALU, which bounds
 //    this kernel, and numerator and denominator use the same rounded P.
+//  * No per-tile max: P is computed against the current reference m, and a P
+//    past the e4m3 range converts to a NaN code, which the row-sum MFMA
+//    carries; only then (always on the first tile, whose reference starts at
+//    -1e30, and whenever a tile's max exceeds m by about 2^2.8) is m raised to
+//    the tile's max, O and the sum rescaled and the tile redone before its P V
+//    product.  This saves the 24 max instructions of every other tile.
 //    The output is multiplied by dv and divided by the sum.
 #include "la_internal.h"
 
@@ -63,7 +68,6 @@ constexpr int VTP = 80;  // V^T row pitch in LDS (bytes): 16 rows hit 16 disjoin
 constexpr int KBUF = BN * KP;
 constexpr int VBUF = D * VTP;
 constexpr int STAGE = KBUF + VBUF;
-constexpr float kRescaleSlack = 2.f;  // log2 units: P <= 2^(2 + 6) between rescales
 constexpr float kPLift = 6.f;         // P is computed as exp2(s - m + 6)
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -131,8 +135,8 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
   f32x16_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
-  float m_run = -INFINITY;  // running reference max (exp2 units)
-  f32x16_t lsum = f32x16_t{};  // every row: the running sum of lifted, rounded P
+  float m_run = -1e30f;  // reference max (exp2 units; finite: no inf - inf)
+  float l_run = 0.f;      // running sum of the lifted, rounded P of this lane's query
   const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
@@ -263,35 +267,45 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
           if (j * BN + 32 * hh + 16 * b + r >= nk) st[b][r] = -INFINITY;
     }
 
-    float mx = fmaxf(st[0][0], st[1][0]);
+    // P^T fragment against the current reference max: byte 16 b + r = key
+    // 32 hh + 16 b + r; tsum = the tile's row sum of the rounded, lifted P.
+    i32x8_t pf;
+    f32x16_t tsum;
+    auto probs = [&]() __attribute__((always_inline)) {
+      const float nm = kPLift - m_run;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
-    mx = swap_halves_max(mx) * c2;
-    // raise the reference max only when this tile would push P above 2^(2+6)
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float p[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            p[t] = __builtin_amdgcn_exp2f(fmaf(st[b][4 * g + t], c2, nm));
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+          pf[4 * b + g] = w;
+        }
+      tsum = mma(ones, pf, f32x16_t{});
+    };
+    probs();
+    // A probability past the e4m3 range converts to a NaN code, which the row
+    // sum carries: only then is the reference max raised to this tile's max
+    // (always on the first tile, whose reference starts at -1e30), O and the
+    // row sum rescaled and the tile's probabilities redone.
+    if (__builtin_amdgcn_ballot_w64((__float_as_uint(tsum[0]) & 0x7fffffffu) > 0x7f800000u) != 0) {
+      float mx = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
+      mx = swap_halves_max(mx) * c2;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      lsum *= alpha;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      probs();
     }
-
-    // P^T fragment: byte 16 b + r = key 32 hh + 16 b + r
-    i32x8_t pf;
-    const float nm = kPLift - m_run;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float p[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) p[t] = __builtin_amdgcn_exp2f(fmaf(st[b][4 * g + t], c2, nm));
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-        pf[4 * b + g] = w;
-      }
-    lsum = mma(ones, pf, lsum);
+    l_run += tsum[0];
 
     // O^T[d][query] += V^T P^T: A = V^T row 32 db + lane % 32, keys 32 hh .. +31
 #pragma unroll
@@ -301,7 +315,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     }
   }
 
-  const float lt = lsum[0];  // the full row sum: MFMA rows all hold it
+  const float lt = l_run;  // the full row sum (every row of the sum MFMA holds it)
   if (qrow < nq) {
     const float f = dv / lt;
     uint16_t* op = out + (qrow * (int64_t)heads + head) * D + 4 * hh;
