@@ -14,7 +14,7 @@ region (there are no trained weights).  One JSON line goes to stdout; progress
 goes to stderr.
 
 Other workloads (--workload): c2 (one 40x128 layer, attention timed alone),
-c5 (720p-shaped layer, 44x80 tokens per frame, streamed for 1000 blocks:
+c3 (the same layer with a window of 8 blocks, Nk 43680), c5 (720p-shaped layer, 44x80 tokens per frame, streamed for 1000 blocks:
 sustained blocks/s and cache-update GB/s), chain (a complete 4-step denoise of
 each block on one GPU: 4 timestep-forcing stages x 40 layers, la_denoise_chain),
 c2fp8 (the e4m3 attention kernel alone at the C2 shape), refresh (the NFE-5
@@ -504,7 +504,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["c4", "c2", "c5", "chain", "c2fp8", "refresh"],
+    ap.add_argument("--workload", choices=["c4", "c2", "c3", "c5", "chain", "c2fp8", "refresh"],
                     default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0,
@@ -534,6 +534,10 @@ def main():
     elif args.workload == "c2":
         geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=1)
         name = "C2 one layer: bf16 block attention 40x128, Nq 4680, Nk 24960 (+RoPE, append, Euler)"
+    elif args.workload == "c3":
+        geo = dict(Hl=30, Wl=52, W=8, H=40, d=128, n_layers=1)
+        name = ("C3 one layer, window of 8 blocks: bf16 block attention 40x128, Nq 4680, "
+                "Nk 43680 (+RoPE, append, Euler)")
     elif args.workload == "c5":
         geo = dict(Hl=44, Wl=80, W=4, H=40, d=128, n_layers=1)
         name = ("C5 720p-shaped layer: 44x80 tokens/frame, Nq 10560, Nk 56320 (sink + 4 cached "
