@@ -47,6 +47,8 @@ DT = -0.25
 # keyed by the attention kernel version the library reports; any other version
 # reports null (the counters were taken on a different kernel).
 ATTN_TRAFFIC_BYTES = {"attn-v5s": 8.118e8}
+# The same for the e4m3 attention kernel at the C2 shape (--workload c2fp8).
+FP8_TRAFFIC_BYTES = {"fp8-v4": 4.3355e+08}
 
 
 _T0 = time.perf_counter()
@@ -358,10 +360,17 @@ def gpu_fp8_attn_bench(args, Hl, Wl, W, H, d):
     return {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "flop": fl, "nq": bt, "nk": nk}
 
 
+def kernel_version(prefix):
+    """The library's version tag of one kernel family (e.g. "attn-v5s", "fp8-v4")."""
+    import streaming_causal_video_amd as L
+    return next((t for t in L.la_version().split() if t.startswith(prefix)), None)
+
+
 def fp8_main(args):
     """--workload c2fp8: the e4m3 attention kernel at the C2 shape."""
     geo = dict(Hl=30, Wl=52, W=4, H=40, d=128)
     r = gpu_fp8_attn_bench(args, **geo)
+    version = kernel_version("fp8-")
     out = {
         "metric": "block-attn TFLOP/s at 1 GPU, e4m3 operands; % fp8 MFMA peak",
         "value": round(r["tflops"], 2),
@@ -379,7 +388,8 @@ def fp8_main(args):
                    "heads": geo["H"], "head_dim": geo["d"], "nq": r["nq"], "nk": r["nk"]},
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_fp8_kernel", "flop_per_launch": r["flop"]},
+                     "traffic": FP8_TRAFFIC_BYTES.get(version), "kernel": "attn_fp8_kernel",
+                     "kernel_version": version, "flop_per_launch": r["flop"]},
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -548,7 +558,7 @@ def main():
         raise AssertionError(args.workload)
     r = gpu_step_bench(args, **geo)
     import streaming_causal_video_amd as L
-    version = L.la_version().split()[-1]
+    version = kernel_version("attn-")
     traffic = ATTN_TRAFFIC_BYTES.get(version) if args.workload in ("c4", "c2") else None
     peak_frac = r["attn_tflops"] / PEAK_BF16_TFLOPS
     out = {
