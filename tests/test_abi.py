@@ -295,3 +295,36 @@ def test_denoise_step_flag_refusals():
     assert call(2, None) == _lib.LA_ERR_INVALID_ARG
     assert call(L.LA_STEP_ATTEND_ONLY, arr) == _lib.LA_ERR_INVALID_ARG
     assert bytes(rings[0]) == before
+
+
+def test_attention_refuses_segments_beyond_32_bit_offsets():
+    """Both attention kernels address a key segment with 32-bit byte offsets (the e4m3
+    kernel's buffer descriptors hold a 32-bit record count): a segment of
+    rows x heads x 128 elements reaching 2^32 bytes is refused before any launch; one that
+    fits is not refused for its size."""
+    lib = L.lib()
+    p = ctypes.c_void_p(0x70000)
+    out = ctypes.c_void_p(0x80000)
+    fake = [0x10000, 0x20000, 0x30000, 0x40000]
+
+    def ring(block_tokens, dtype):
+        r = L.la_kvring()
+        L.la_kvring_init(r, *fake, 2, block_tokens, 16, 40, 128, dtype, 0.5)
+        return r
+
+    # bf16: (block + 64) x 40 x 128 x 2 B >= 2^32 from block = 419,367
+    big = ring(419_400, L.LA_BF16)
+    assert lib.la_block_attn_fwd(ctypes.byref(big), p, p, p, p, 419_400, out, None, 0.1,
+                                 None) == _lib.LA_ERR_SHAPE
+    # e4m3: (block + 64) x 40 x 128 B >= 2^32 from block = 838,797
+    big8 = ring(838_800, L.LA_FP8_E4M3)
+    assert lib.la_block_attn_fwd_fp8(ctypes.byref(big8), p, p, p, p, p, 838_800, out, None,
+                                     0.1, 1.0, 1.0, 1.0, None) == _lib.LA_ERR_SHAPE
+    # just below the limits the size check passes and only the (deliberately) wrong n_q is
+    # refused, so the refusal above came from the size
+    ok = ring(419_300, L.LA_BF16)
+    assert lib.la_block_attn_fwd(ctypes.byref(ok), p, p, p, p, 419_299, out, None, 0.1,
+                                 None) == _lib.LA_ERR_SHAPE
+    ok8 = ring(838_700, L.LA_FP8_E4M3)
+    assert lib.la_block_attn_fwd_fp8(ctypes.byref(ok8), p, p, p, p, p, 838_699, out, None,
+                                     0.1, 1.0, 1.0, 1.0, None) == _lib.LA_ERR_SHAPE
