@@ -7,14 +7,20 @@ them.  This checker walks the control-flow graph of every function in the
 assembly and reports:
 
   * a non-MFMA instruction that reads or writes a register of an MFMA result
-    (VGPR or AGPR) fewer than ``mfma_window`` wait states after the MFMA issued
+    (VGPR or AGPR) fewer than ``passes + 4`` wait states after the MFMA issued
     (an MFMA that accumulates into exactly the same registers is allowed: the
     hardware forwards back-to-back accumulations);
   * a non-MFMA instruction that writes a register an MFMA reads as its
-    accumulator input (srcC) fewer than ``srcc_window`` wait states after the
+    accumulator input (srcC) fewer than ``passes - 1`` wait states after the
     MFMA issued (the matrix core reads srcC over several passes);
   * an MFMA that reads a register written by a VALU instruction fewer than
     ``valu_window`` wait states earlier.
+
+``passes`` is the MFMA's number of 4-cycle passes on gfx950 (``mfma_passes``):
+4 for the 16x16x32 bf16/f16 forms, 8 for 32x32x16, 16 for the 32x32x64 fp8
+form; the windows are the figures the compiler uses for gfx950's XDL ops (12
+and 7 wait states for 8 passes).  ``mfma_window`` / ``srcc_window`` override
+them for every MFMA.
 
 Wait states are counted as the compiler does: one per instruction, N + 1 for
 ``s_nop N``.  Along control flow the count is the minimum over all paths
@@ -134,7 +140,23 @@ def _blocks(body):
     return blocks, succ
 
 
-def check(text, mfma_window=12, valu_window=2, srcc_window=8):
+_PASSES = [
+    (re.compile(r"v_mfma_f32_16x16x32_(bf16|f16)\b"), 4),
+    (re.compile(r"v_mfma_f32_32x32x16_(bf16|f16)\b"), 8),
+    (re.compile(r"v_mfma_scale_f32_16x16x128_f8f6f4\b"), 8),
+    (re.compile(r"v_mfma_scale_f32_32x32x64_f8f6f4\b"), 16),
+]
+
+
+def mfma_passes(op):
+    """Passes of an MFMA opcode on gfx950 (16, the longest, for forms not listed)."""
+    for pat, n in _PASSES:
+        if pat.match(op):
+            return n
+    return 16
+
+
+def check(text, mfma_window=None, valu_window=2, srcc_window=None):
     """Return a list of violation strings for every function in ``text``."""
     found = []
     for fname, body in _functions(text):
@@ -177,7 +199,7 @@ def check(text, mfma_window=12, valu_window=2, srcc_window=8):
                             if found_key not in reported:
                                 reported.add(found_key)
                                 found.append(f"{fname}: '{ins}' overwrites an MFMA accumulator input "
-                                             f"{srcc_window - sc[reg]} wait states after issue")
+                                             f"{sc[reg]} wait states too early")
                     touched = [reg for r in defs + uses for reg in r]
                     for reg in touched:
                         if reg in mf and mf[reg][0] > 0:
@@ -185,7 +207,7 @@ def check(text, mfma_window=12, valu_window=2, srcc_window=8):
                             if found_key not in reported:
                                 reported.add(found_key)
                                 found.append(f"{fname}: '{ins}' touches an MFMA result "
-                                             f"{mfma_window - mf[reg][0]} wait states after issue")
+                                             f"{mf[reg][0]} wait states too early")
                 # advance time, then record this instruction's own effects
                 for d in (mf, va, sc):
                     for reg in list(d):
@@ -200,11 +222,14 @@ def check(text, mfma_window=12, valu_window=2, srcc_window=8):
                             if d[reg] <= 0:
                                 del d[reg]
                 if kind == "mfma" and defs:
+                    p = mfma_passes(op)
+                    mw = mfma_window if mfma_window is not None else p + 4
+                    cw = srcc_window if srcc_window is not None else p - 1
                     for reg in defs[0]:
-                        mf[reg] = (mfma_window, defs[0])
+                        mf[reg] = (mw, defs[0])
                     if len(uses) >= 3:
                         for reg in uses[2]:
-                            sc[reg] = srcc_window
+                            sc[reg] = cw
                 if kind == "valu":
                     for r in defs:
                         for reg in r:
