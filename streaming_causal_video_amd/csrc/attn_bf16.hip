@@ -7,46 +7,52 @@
 // block attends to the sink frame and to the sliding noisy KV cache).
 //
 // Design (MI355X-first, not a port of the pages' FlashAttention):
-//  * One workgroup = 8 waves (two per SIMD) = 256 query rows of one head; each
-//    wave owns 32 query rows for the whole key range and keeps its Q fragments,
+//  * One workgroup = 4 waves = 192 query rows of one head, two workgroups per
+//    CU (two waves per SIMD, from different workgroups, so one workgroup's
+//    barrier does not stall the other's waves).  Each wave owns 48 query rows
+//    (three 16-row tiles) for the whole key range and keeps its Q fragments,
 //    the running row max / row sum and the output accumulator in registers.
-//    The K/V tile a workgroup stages in LDS serves 256 queries: the global
-//    loads per query (measured to cost a quarter of the kernel's time at 128
-//    queries per workgroup, whether they hit L2 or not) are halved.
-//  * Keys are walked as one virtual range over the segment table, 64 keys per
-//    tile, so tiles straddle segment boundaries and only the very last tile
-//    can be partial.  K and V tiles are staged global -> registers -> LDS,
-//    double buffered, one barrier per tile; the next tile's global loads are in
-//    flight while the current tile is computed.  Waves 0-3 load V, waves 4-7 K
-//    (four 16-byte loads per thread per tile).
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: in the 32x32 result each lane holds one query
-//    (lane % 32) and half of the tile's keys, so the row max needs one
-//    v_permlane32_swap per tile and the row sum none until the end.
-//  * K rows are fed to the MFMA in an order that swaps bits 2 and 3 of the row
-//    index; then the probabilities P^T come out of the score accumulator
-//    already in the B-operand layout of the second product O^T = V^T P^T, with
-//    no shuffle.
-//  * V is stored transposed in LDS (V^T: 128 rows of 64 keys, 144-byte pitch):
-//    each loader thread transposes a 4-key x 8-dim piece in registers with
-//    v_perm_b32, so the V^T operand of the second product is read with plain
-//    ds_read_b128 at immediate offsets (measured on gfx950: 16-byte LDS reads
-//    deliver ~2.4x the bytes per clock of the transposing ds_read_b64_tr_b16).
+//  * Products on v_mfma_f32_16x16x32_bf16: every K or V^T fragment read from
+//    LDS feeds three MFMAs (one per query tile), 48 flops per LDS byte; the
+//    LDS operand traffic, not the matrix core, bounded the earlier 32-row
+//    waves on 32x32x16 MFMAs.  At 4680 rows a head takes 25 workgroups
+//    (2.5 % padding), and 40 heads fill 512 CU slots in two rounds.
+//  * Scores are computed transposed, S^T = K Q^T: in each 16x16 result a lane
+//    holds one query (lane % 16) and four keys; the row max needs two lane
+//    swaps (v_permlane32_swap, v_permlane16_swap).
+//  * K rows sit in LDS in an order that moves key bit 2 to row bit 4 and key
+//    bits 3-4 to row bits 2-3 (within each 32-key half); then rows 4g .. 4g+3
+//    of the row blocks 2h and 2h+1 hold keys 32h + 8g .. 32h + 8g + 7, so the
+//    probabilities P^T come out of the score accumulators already in the
+//    B-operand layout of O^T = V^T P^T, with no shuffle.
+//  * Each 64-key tile is processed as two 32-key halves (scores, softmax,
+//    P V): 24 score and 24 output registers per half instead of 48, which
+//    keeps the kernel within the 256 registers of two waves per SIMD.
 //  * Online softmax in float32 with the scale folded into a base-2 exponent
-//    (one FMA and one v_exp_f32 per score); P is rounded to bf16 for the second
-//    product with v_cvt_pk_bf16_f32, and the row sum is taken from those same
-//    bf16 pairs with v_dot2c_f32_bf16 (two scores per instruction, consistent
-//    with the P V product it normalises).
-//  * Lazy rescaling: the running max is only raised when a tile's max exceeds
-//    it by more than 2^8 (in exp2 units), so O and the row sum are rescaled on
-//    a handful of tiles instead of every tile.  Exact: numerator and
-//    denominator use the same reference max; P stays <= 256.
-//  * Loader: per-thread 32-bit row offsets are computed once; per tile only a
-//    scalar segment base changes, and the current segment's key range and
-//    base pointers stay in scalar registers (the segment table in kernel
-//    arguments is read only when a tile enters the next segment: a scalar load
-//    would also wait for all LDS reads in flight).  Tiles that straddle a
-//    segment boundary or run past the last key take a slower per-row path.
+//    (one FMA and one v_exp_f32 per score).  Probabilities are taken against
+//    the running reference max without a per-tile max; only when a query's
+//    sum over the half leaves [0, 2^64] (always on the first tile, whose
+//    reference is -inf) is the reference raised to the half's max, O and the
+//    row sum rescaled and the half's probabilities recomputed.  Exact:
+//    numerator and denominator use the same reference, and P <= 2^64 keeps
+//    the float32 accumulators far from overflow.  P is rounded to bf16 for
+//    the second product (v_cvt_pk_bf16_f32) and the row sum is taken from
+//    those same bf16 pairs with v_dot2c_f32_bf16.
+//  * K tiles go global -> LDS by DMA (buffer_load ... lds): no staging
+//    registers, issued one tile ahead right after the barrier, so a whole
+//    tile of compute hides their latency.  A DMA writes each wave's 1 KB
+//    contiguously, so K rows have no padding (256-byte pitch) and each
+//    16-byte chunk c of row r sits at chunk c ^ (r & 15), which keeps the
+//    fragment reads free of bank conflicts.  Tiles that straddle a segment
+//    boundary or run past the last key take a synchronous per-row copy.
+//  * V is stored transposed in LDS (V^T: 128 rows of 64 keys, 144-byte pitch)
+//    for the A operand of the second product: each thread loads a 4-key x
+//    8-dim piece into registers after the first half's scores and transposes
+//    it with v_perm_b32 at the end of the tile.
+//  * Loader addressing: buffer loads from a scalar descriptor per tile with
+//    per-thread 32-bit offsets computed once; the current segment's key range
+//    and base pointers stay in scalar registers (the segment table in kernel
+//    arguments is read only when a tile enters the next segment).
 //  * Workgroups are renumbered so that all query tiles of a head run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 while
 //    they stream the head's K/V.
@@ -57,39 +63,47 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
-constexpr int BM = 256;  // query rows per workgroup
-constexpr int BN = 64;   // keys per tile
-constexpr int NWAVES = 8;
+constexpr int NQT = 3;           // 16-query tiles per wave
+constexpr int QW = 16 * NQT;     // query rows per wave
+constexpr int NWAVES = 4;
+constexpr int BM = QW * NWAVES;  // query rows per workgroup
+constexpr int BN = 64;           // keys per tile
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int KP = 136;  // K row pitch in LDS (bf16): 272 B, 16 rows hit 16 disjoint bank quads
-constexpr int VTP = 72;  // V^T row pitch in LDS (bf16): 144 B, 16 rows hit 16 disjoint bank quads
+constexpr int KP = 128;  // K row pitch in LDS (bf16): 256 B, chunks XOR-swizzled by row
+constexpr int VTP = 72;  // V^T row pitch in LDS (bf16): 144 B
 constexpr int KBUF = BN * KP;
 constexpr int VBUF = D * VTP;
 constexpr int STAGE = KBUF + VBUF;
-constexpr float kRescaleSlack = 8.f;  // log2 units: P <= 2^8 between rescales
+constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit loads
+constexpr float kSumLimit = 0x1p64f;   // a half's row sum above this raises the reference
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-__device__ __forceinline__ float swap_halves_max(float x) {
+// max / sum over the four lanes c, c + 16, c + 32, c + 48 (one query's keys)
+__device__ __forceinline__ float max4_lanes(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum4_lanes(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-__device__ __forceinline__ float swap_halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Row of the K tile that feeds MFMA row i: bits 2 and 3 of i swapped.
-__device__ __forceinline__ int k_row_perm(int i) {
-  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+// Tile key held by LDS K row r (r = 0..63): row bits (5 | 4 | 3,2 | 1,0) are
+// key bits (5 | 2 | 4,3 | 1,0).
+__device__ __forceinline__ int key_of_krow(int r) {
+  return (r & 32) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
@@ -111,55 +125,65 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
+  const int c = lane & 15;  // query (scores) / row (operands) within a 16-tile
+  const int g = lane >> 4;  // 8-element k-group of the operands
   const int64_t rs = (int64_t)heads * D;
+  const int qbase = qt * BM + wave * QW;
 
-  // Q^T B-operand fragments: lane holds Q[qrow][16 s + 8 hh .. +7].
-  const int qrow = qt * BM + wave * 32 + l32;
-  bf16x8_t qf[8];
-  if (qrow < nq) {
-    const uint16_t* qp = q + qrow * rs + head * D + 8 * hh;
+  // Q^T B-operand fragments: lane holds Q[query qbase + 16 nt + c][32 s + 8 g .. +7].
+  bf16x8_t qf[NQT][4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * s);
-  } else {
+  for (int nt = 0; nt < NQT; ++nt) {
+    const int qrow = qbase + 16 * nt + c;
+    if (qrow < nq) {
+      const uint16_t* qp = q + qrow * rs + head * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = bf16x8_t{};
+      for (int s = 0; s < 4; ++s) qf[nt][s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qf[nt][s] = bf16x8_t{};
+    }
   }
 
-  f32x16_t o[4];
+  f32x4_t o[8][NQT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
-  float m_run = -INFINITY;  // running max of scale*log2(e)*score
-  float l_run = 0.f;        // this lane's half of the running row sum
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) o[dt][nt] = f32x4_t{};
+  float m_run[NQT], l_run[NQT];  // reference max (scale*log2(e) units), this lane's row sum
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
 
-  // Loader.  Waves 4-7 load K: thread covers 16-byte chunk lcc of tile rows
-  // lr0 + 16 i (16 lanes read one 256-byte row).  Waves 0-3 load V: thread covers
-  // 16-byte chunk vc (dims 8 vc .. +7) of tile rows 4 kq + i (a wave reads 64
-  // contiguous bytes of every row) and writes it transposed.
-  const bool kloader = __builtin_amdgcn_readfirstlane(wave) >= 4;
-  const int ltid = tid & 255;
-  const int lcc = ltid & 15;
-  const int lr0 = ltid >> 4;
+  // Loader geometry.  K DMA: wave w fills LDS rows 16 w + 4 i + t (t = lane
+  // >> 4, i = 0..3), lane slot p = lane & 15 of a row receiving chunk
+  // p ^ (row & 15) of key 32 (w >> 1) + 4 (w & 1) + 8 i + t.  V: thread covers
+  // the 16-byte chunk vc (dims 8 vc .. +7) of tile rows 4 kq .. 4 kq + 3.
+  const int t4 = lane >> 4;
   const int kq = lane & 15;
-  const int vc = 4 * (wave & 3) + (lane >> 4);
+  const int vc = 4 * wave + t4;
   const int ntiles = (nk + BN - 1) / BN;
   const uint32_t rs_bytes = (uint32_t)rs * 2u;
-  uint32_t off[4];
+  const uint32_t hoff = (uint32_t)(head * D * 2);
+  const uint32_t kkey0 = (uint32_t)(32 * (wave >> 1) + 4 * (wave & 1) + t4);
+  uint32_t kdoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    off[i] = kloader ? (uint32_t)(lr0 + 16 * i) * rs_bytes + (uint32_t)(head * D * 2 + lcc * 16)
-                     : (uint32_t)(4 * kq + i) * rs_bytes + (uint32_t)(head * D * 2 + vc * 16);
-  uint4 reg[4];
-  // Segment holding the first key of the tile being loaded, with its key range
-  // and base pointers kept in scalar registers: the segment table is read only
-  // when a tile crosses into the next segment (a scalar load would also wait
-  // for every LDS read in flight).
+    kdoff[i] = kkey0 * rs_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * i + t4));
+  const uint32_t voff = (uint32_t)(4 * kq) * rs_bytes + (uint32_t)(vc * 16);
+  uint4 vreg[4];
+
+  // Segment of the tile being loaded, kept in scalar registers: the segment
+  // table is read only when a tile crosses into the next segment.
   int seg = 0, seg_start = 0, seg_end = segs.end[0];
   const char* seg_k = static_cast<const char*>(segs.k[0]);
   const char* seg_v = static_cast<const char*>(segs.v[0]);
+  bool whole = true;             // tile inside one segment
+  uint32_t sbase = 0, nbytes = 0;  // tile's byte offset in the segment, bytes left from there
 
-  auto gload = [&](int tile) __attribute__((always_inline)) {
+  auto locate = [&](int tile) __attribute__((always_inline)) {
     const int t0 = tile * BN;
     while (t0 >= seg_end) {
       ++seg;
@@ -168,156 +192,201 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       seg_k = static_cast<const char*>(segs.k[seg]);
       seg_v = static_cast<const char*>(segs.v[seg]);
     }
-    if (t0 + BN <= seg_end) {
-      // whole tile inside one segment: scalar base + precomputed 32-bit offsets
-      const uint32_t sbase = (uint32_t)(t0 - seg_start) * rs_bytes;
-      const char* b = (kloader ? seg_k : seg_v) + sbase;
+    whole = t0 + BN <= seg_end;
+    sbase = (uint32_t)(t0 - seg_start) * rs_bytes + hoff;
+    nbytes = (uint32_t)(seg_end - t0) * rs_bytes - hoff;
+  };
+  // one 16-byte chunk of tile row r; rows past the last key are clamped to it
+  // (their scores are masked)
+  auto row_load = [&](int t0, int r, int chunk, bool is_v) __attribute__((always_inline)) -> uint4 {
+    const int key = min(t0 + r, nk - 1);
+    int s = seg;
+    while (key >= segs.end[s]) ++s;
+    const int st = s ? segs.end[s - 1] : 0;
+    const int64_t o = (int64_t)(key - st) * rs + head * D + chunk * 8;
+    const uint16_t* base = static_cast<const uint16_t*>(is_v ? segs.v[s] : segs.k[s]);
+    return *reinterpret_cast<const uint4*>(base + o);
+  };
+  auto kload = [&](int tile, int buf) __attribute__((always_inline)) {
+    uint16_t* kb = lds + buf * STAGE;
+    if (whole) {
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) reg[i] = *reinterpret_cast<const uint4*>(b + off[i]);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void*)(kb + (16 * wave + 4 * i) * KP), 16,
+            kdoff[i], 8 * i * rs_bytes, 0, 0);
     } else {
-      // straddles a segment boundary or runs past the last key: per-row lookup,
-      // rows past the last key are clamped to it (their scores are masked)
-      auto row_load = [&](int r, int chunk, bool is_v) -> uint4 {
-        const int key = min(t0 + r, nk - 1);
-        int s = seg;
-        while (key >= segs.end[s]) ++s;
-        const int st = s ? segs.end[s - 1] : 0;
-        const int64_t o = (int64_t)(key - st) * rs + head * D + chunk * 8;
-        const uint16_t* base = static_cast<const uint16_t*>(is_v ? segs.v[s] : segs.k[s]);
-        return *reinterpret_cast<const uint4*>(base + o);
-      };
-      if (kloader) {
-        reg[0] = row_load(lr0, lcc, false);
-        reg[1] = row_load(lr0 + 16, lcc, false);
-        reg[2] = row_load(lr0 + 32, lcc, false);
-        reg[3] = row_load(lr0 + 48, lcc, false);
-      } else {
-        reg[0] = row_load(4 * kq, vc, true);
-        reg[1] = row_load(4 * kq + 1, vc, true);
-        reg[2] = row_load(4 * kq + 2, vc, true);
-        reg[3] = row_load(4 * kq + 3, vc, true);
+      const int t0 = tile * BN;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * i + t4;
+        const uint4 x = row_load(t0, key_of_krow(r), (lane & 15) ^ (r & 15), false);
+        *reinterpret_cast<uint4*>(kb + r * KP + (lane & 15) * 8) = x;
       }
     }
   };
-  auto lstore = [&](int buf) {
-    uint16_t* kb = lds + buf * STAGE;
-    uint16_t* vt = kb + KBUF;
-    if (kloader) {
+  auto vload = [&](int tile) __attribute__((always_inline)) {
+    if (whole) {
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(kb + (lr0 + 16 * i) * KP + lcc * 8) = reg[i];
-    } else {
-      // V^T[8 vc + j][4 kq .. 4 kq + 3]: pairs of keys packed per dword
-      const uint32_t w[4][4] = {{reg[0].x, reg[0].y, reg[0].z, reg[0].w},
-                                {reg[1].x, reg[1].y, reg[1].z, reg[1].w},
-                                {reg[2].x, reg[2].y, reg[2].z, reg[2].w},
-                                {reg[3].x, reg[3].y, reg[3].z, reg[3].w}};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint2 even = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
-                                      __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
-        const uint2 odd = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
-                                     __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
-        *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m) * VTP + 4 * kq) = even;
-        *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m + 1) * VTP + 4 * kq) = odd;
+      for (int i = 0; i < 4; ++i) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, i * rs_bytes, 0);
+        vreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
       }
+    } else {
+      const int t0 = tile * BN;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vreg[i] = row_load(t0, 4 * kq + i, vc, true);
+    }
+  };
+  auto vstore = [&](int buf) __attribute__((always_inline)) {
+    // V^T[8 vc + j][4 kq .. 4 kq + 3]: pairs of keys packed per dword
+    uint16_t* vt = lds + buf * STAGE + KBUF;
+    const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
+                              {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
+                              {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
+                              {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint2 even = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
+                                    __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
+      const uint2 odd = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
+                                   __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
+      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m) * VTP + 4 * kq) = even;
+      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m + 1) * VTP + 4 * kq) = odd;
     }
   };
 
-  const int krow_a = k_row_perm(l32);
   typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
   const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  gload(0);
+  locate(0);
+  kload(0, 0);
+  vload(0);
+  vstore(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile 0's K DMA has landed
   for (int j = 0; j < ntiles; ++j) {
-    lstore(j & 1);
-    if (j + 1 < ntiles) gload(j + 1);
     __syncthreads();
-    const uint16_t* kb = lds + (j & 1) * STAGE;
-    const uint16_t* vt = kb + KBUF + l32 * VTP + 8 * hh;
-
-    // S^T[key][query] for two 32-key blocks, chains interleaved.
-    f32x16_t st[2];
-    st[0] = f32x16_t{};
-    st[1] = f32x16_t{};
-    const uint16_t* kr0 = kb + krow_a * KP + 8 * hh;
-    const uint16_t* kr1 = kr0 + 32 * KP;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(kr0 + 16 * s);
-      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(kr1 + 16 * s);
-      st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], st[0], 0, 0, 0);
-      st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], st[1], 0, 0, 0);
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      locate(j + 1);
+      kload(j + 1, (j + 1) & 1);
     }
-    if ((j + 1) * BN > nk) {
-      // last tile: mask keys past the end (accumulator row i holds key 32 b + perm(i))
+    const uint16_t* kb = lds + (j & 1) * STAGE;
+    // K fragment: row 16 blk + c, chunk 4 s + g, stored at chunk (4 s + g) ^ c
+    const uint16_t* kr = kb + c * KP;
+    const uint16_t* vt = kb + KBUF + c * VTP + 8 * g;
+
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // S^T[key][query] for keys 32 h .. 32 h + 31: row blocks 2 h and 2 h + 1.
+      f32x4_t st[2][NQT];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j * BN + 32 * b + k_row_perm(i) >= nk) st[b][r] = -INFINITY;
+        for (int nt = 0; nt < NQT; ++nt) st[b][nt] = f32x4_t{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+              kr + 16 * (2 * h + b) * KP + (((4 * s + g) ^ c) * 8));
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt)
+            st[b][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[b][nt], 0, 0, 0);
         }
-    }
-
-    float mx = fmaxf(st[0][0], st[1][0]);
+      if (h == 0 && more) vload(j + 1);
+      if ((j + 1) * BN > nk) {
+        // last tile: row 4 g + i of block 2 h + b holds key 32 h + 8 g + 4 b + i
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
-    mx = swap_halves_max(mx) * c2;
-    // raise the reference max only when this tile would push P above 2^8
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-    }
-
-    // P^T fragments: ks = 2 b + half, elements r = 8 half .. 8 half + 7.
-    bf16x8_t pf[4];
-    const float nm = -m_run;
+          for (int i = 0; i < 4; ++i) {
+            if (j * BN + 32 * h + 8 * g + 4 * b + i >= nk) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e], c2, nm));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[b][8 * half + 2 * e + 1], c2, nm));
-          w[e] = pack_bf16(p0, p1);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[e]), ones,
-                                                  l_run, false);
-        }
-        pf[2 * b + half] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+              for (int nt = 0; nt < NQT; ++nt) st[b][nt][i] = -INFINITY;
+            }
+          }
       }
 
-    // O^T[d][query] += V^T P^T: A operand = V^T[32 db + lane % 32][16 ks + 8 hh .. +7]
+      // P^T fragment of query tile nt: keys 32 h + 8 g .. +7, i.e. rows
+      // 4 g .. 4 g + 3 of both row blocks; tsum = this lane's sum of them.
+      bf16x8_t pf[NQT];
+      float tsum[NQT];
+      auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int nt = 0; nt < NQT; ++nt) {
+          const float nm = -m_run[nt];
+          uint32_t w[4];
+          float ts = 0.f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + 32 * db * VTP + 16 * ks);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(st[e >> 1][nt][2 * (e & 1)], c2, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(st[e >> 1][nt][2 * (e & 1) + 1], c2, nm));
+            w[e] = pack_bf16(p0, p1);
+            ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[e]), ones, ts,
+                                                 false);
+          }
+          tsum[nt] = ts;
+          pf[nt] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      };
+      probs();
+      bool over = false;
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) over |= !(tsum[nt] <= kSumLimit);  // also inf / NaN
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          const float a =
+              fmaxf(fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3])),
+                    fmaxf(fmaxf(st[1][nt][0], st[1][nt][1]), fmaxf(st[1][nt][2], st[1][nt][3])));
+          const float m_new = fmaxf(m_run[nt], max4_lanes(a) * c2);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+          m_run[nt] = m_new;
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
+        }
+        probs();
       }
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) l_run[nt] += tsum[nt];
+
+      // O^T[d][query] += V^T P^T: A operand = V^T[16 dt + c][32 h + 8 g .. +7]
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + 16 * dt * VTP + 32 * h);
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt)
+          o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nt], o[dt][nt], 0, 0, 0);
+      }
+    }
+    if (more) {
+      vstore((j + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's K DMA has landed
     }
   }
 
-  const float lt = swap_halves_sum(l_run);
-  if (qrow < nq) {
-    const float inv = 1.f / lt;
-    uint16_t* op = out + qrow * rs + head * D + 4 * hh;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int nt = 0; nt < NQT; ++nt) {
+    const float lt = sum4_lanes(l_run[nt]);
+    const int qrow = qbase + 16 * nt + c;
+    if (qrow < nq) {
+      const float inv = 1.f / lt;
+      uint16_t* op = out + qrow * rs + head * D + 4 * g;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t w0 = pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        const uint32_t w1 = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * db + 8 * g) = make_uint2(w0, w1);
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint32_t w0 = pack_bf16(o[dt][nt][0] * inv, o[dt][nt][1] * inv);
+        const uint32_t w1 = pack_bf16(o[dt][nt][2] * inv, o[dt][nt][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(w0, w1);
       }
-    if (lse != nullptr && hh == 0)
-      lse[(int64_t)head * nq + qrow] = (m_run + __log2f(lt)) * 0.69314718055994531f;
+      if (lse != nullptr && g == 0)
+        lse[(int64_t)head * nq + qrow] = (m_run[nt] + __log2f(lt)) * 0.69314718055994531f;
+    }
   }
 }
 

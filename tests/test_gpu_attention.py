@@ -141,3 +141,46 @@ def test_peaked_logits_on_given_bf16_inputs(L):
     allv = np.concatenate([sv.values, *vals, vc.values])
     ref, _ = attention_lse(q.values, allk, allv, s.head_dim ** -0.5)
     check_attention(to_f64(out), ref, "peaked")
+
+
+def test_late_dominant_keys_raise_the_reference(L):
+    """Attention alone on given bf16 inputs where, late in the block's own keys, key
+    p_i is a multiple of query i chosen so that query i's logit there is ~100 binades
+    above every earlier one: the kernel must raise its running reference mid-stream
+    (probabilities against a stale reference would overflow) and rescale what it has
+    accumulated.  Query i's output is then essentially V[p_i]; the oracle decides."""
+    t = torch()
+    s = si.LayerShape(109, "bf16", heads=3, head_dim=128, Hl=10, Wl=13, W=2)
+    ring = L.KVRing(s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, t.bfloat16, 0.75)
+    keys, vals = [], []
+    sk, sv = s.initial_sink(0)
+    ring.sink_k_raw.copy_(to_dev(sk))
+    ring.sink_v.copy_(to_dev(sv))
+    for b in range(1, 3):
+        _, k, v = s.block_inputs(0, b)
+        L.la_kvcache_append_evict(ring.state, to_dev(k), to_dev(v), b, 0.75)
+        keys.append(k.values)
+        vals.append(v.values)
+    q, kc, vc = s.block_inputs(0, 3)
+    kv = kc.values.copy()
+    planted = {0: 389, 47: 300, 48: 230, 191: 150, 192: 260, 389: 388}  # query row -> key row
+    d = s.head_dim
+    for i, p in planted.items():
+        for h in range(s.heads):
+            qi = q.values[i, h]
+            alpha = 100.0 * np.sqrt(d) / (np.log2(np.e) * float(qi @ qi))
+            kv[p, h] = alpha * qi
+    kc = si.make_stored(kv, "bf16")
+    out = t.empty((s.block_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+    lse = t.empty((s.heads, s.block_tokens), dtype=t.float32, device="cuda")
+    L.la_block_attn_fwd(ring.state, to_dev(q), ring.sink_k_raw, to_dev(kc), to_dev(vc), out, lse)
+    t.cuda.synchronize()
+    allk = np.concatenate([sk.values, *keys, kc.values])
+    allv = np.concatenate([sv.values, *vals, vc.values])
+    ref, lse_ref = attention_lse(q.values, allk, allv, d ** -0.5)
+    got = to_f64(out)
+    check_attention(got, ref, "late dominant keys")
+    rows = sorted(planted)
+    assert np.abs(got[rows] - vc.values[[planted[i] for i in rows]]).max() <= 2e-2
+    gl = lse.cpu().numpy().astype(np.float64)
+    assert np.abs(gl - lse_ref).max() <= 5e-3
