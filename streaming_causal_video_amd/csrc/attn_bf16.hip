@@ -32,8 +32,8 @@
 //    (one FMA and one v_exp_f32 per score).  Probabilities are taken against
 //    the running reference max without a per-tile max; only when a query's
 //    sum over the half leaves [0, 2^64] (always on the first tile, whose
-//    reference is -inf) is the reference raised to the half's max, O and the
-//    row sum rescaled and the half's probabilities recomputed.  Exact:
+//    reference starts at -1e30) is the reference raised to the half's max, O
+//    and the row sum rescaled and the half's probabilities recomputed.  Exact:
 //    numerator and denominator use the same reference, and P <= 2^64 keeps
 //    the float32 accumulators far from overflow.  P is rounded to bf16 for
 //    the second product (v_cvt_pk_bf16_f32) and the row sum is taken from
@@ -79,7 +79,8 @@ constexpr int KBUF = BN * KP;
 constexpr int VBUF = D * VTP;
 constexpr int STAGE = KBUF + VBUF;
 constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit loads
-constexpr float kSumLimit = 0x1p64f;   // a half's row sum above this raises the reference
+constexpr uint32_t kSumLimitBits = 0x5f800000u;  // 2^64: a half's row sum above it
+                                                 // raises the reference
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2_t f = {lo, hi};
@@ -150,10 +151,13 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) o[dt][nt] = f32x4_t{};
-  float m_run[NQT], l_run[NQT];  // reference max (scale*log2(e) units), this lane's row sum
+  // Reference max (scale*log2(e) units) and this lane's row sum.  The reference
+  // starts finite, so the first tile's probabilities overflow to +inf (never
+  // NaN, even where masked keys hold -inf) and trigger the first raise.
+  float m_run[NQT], l_run[NQT];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    m_run[nt] = -INFINITY;
+    m_run[nt] = -1e30f;
     l_run[nt] = 0.f;
   }
 
@@ -337,7 +341,8 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       probs();
       bool over = false;
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) over |= !(tsum[nt] <= kSumLimit);  // also inf / NaN
+      for (int nt = 0; nt < NQT; ++nt)  // on the bits: also inf and NaN, whatever the NaN flags
+        over |= (__float_as_uint(tsum[nt]) & 0x7fffffffu) > kSumLimitBits;
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt) {

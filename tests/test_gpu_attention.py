@@ -184,3 +184,26 @@ def test_late_dominant_keys_raise_the_reference(L):
     assert np.abs(got[rows] - vc.values[[planted[i] for i in rows]]).max() <= 2e-2
     gl = lse.cpu().numpy().astype(np.float64)
     assert np.abs(gl - lse_ref).max() <= 5e-3
+
+
+@pytest.mark.parametrize("sink,block", [(2, 5), (1, 1), (3, 40)])
+def test_tiny_key_ranges(L, sink, block):
+    """First block of a ring with no cached blocks: only sink + block keys (as few
+    as 2), so the first 64-key tile is also the last and most of it is masked."""
+    t = torch()
+    heads, d = 2, 128
+    cfg = 1100 + 100 * sink + block
+    bf = lambda tid, n: si.tensor(cfg, 0, 1, tid, (n, heads, d), "bf16")
+    q, kc, vc = bf(si.TID_Q, block), bf(si.TID_K, block), bf(si.TID_V, block)
+    sk, sv = bf(si.TID_SINK_K, sink), bf(si.TID_SINK_V, sink)
+    ring = L.KVRing(1, block, sink, heads, d, t.bfloat16, 0.75)
+    ring.sink_k_raw.copy_(to_dev(sk))
+    ring.sink_v.copy_(to_dev(sv))
+    out = t.empty((block, heads, d), dtype=t.bfloat16, device="cuda")
+    lse = t.empty((heads, block), dtype=t.float32, device="cuda")
+    L.la_block_attn_fwd(ring.state, to_dev(q), ring.sink_k_raw, to_dev(kc), to_dev(vc), out, lse)
+    t.cuda.synchronize()
+    ref, lse_ref = attention_lse(q.values, np.concatenate([sk.values, kc.values]),
+                                 np.concatenate([sv.values, vc.values]), d ** -0.5)
+    check_attention(to_f64(out), ref, f"sink {sink} block {block}")
+    assert np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref).max() <= 5e-3
