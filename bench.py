@@ -46,7 +46,7 @@ DT = -0.25
 # from rocprofv3 FETCH_SIZE/WRITE_SIZE runs scaled by a copy kernel of known size,
 # keyed by the attention kernel version the library reports; any other version
 # reports null (the counters were taken on a different kernel).
-ATTN_TRAFFIC_BYTES = {"attn-v6": 9.082e8}
+ATTN_TRAFFIC_BYTES = {"attn-v6": 9.077e8}
 # The same for the e4m3 attention kernel at the C2 shape (--workload c2fp8).
 FP8_TRAFFIC_BYTES = {"fp8-v4": 4.3355e+08}
 
