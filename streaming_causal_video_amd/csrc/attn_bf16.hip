@@ -45,10 +45,17 @@
 //    16-byte chunk c of row r sits at chunk c ^ (r & 15), which keeps the
 //    fragment reads free of bank conflicts.  Tiles that straddle a segment
 //    boundary or run past the last key take a synchronous per-row copy.
-//  * V is stored transposed in LDS (V^T: 128 rows of 64 keys, 144-byte pitch)
-//    for the A operand of the second product: each thread loads a 4-key x
-//    8-dim piece into registers after the first half's scores and transposes
-//    it with v_perm_b32 at the end of the tile.
+//  * V stays key-major in LDS (64 rows of 128 dims, 288-byte pitch) and the A
+//    operand of the second product (V^T: 16 dims x 8 keys per lane) is read
+//    with two ds_read_b64_tr_b16: in each 16-lane group lane i receives, as
+//    element j, element i & 3 of the 8 bytes lane 4j + (i >> 2) addresses
+//    (measured on gfx950), so a lane that addresses key j, dims 4m .. 4m+3
+//    feeds exactly the operand layout; no v_perm transpose in the loader.
+//    Keys sit in LDS rows with key bits 2 and 3 swapped, so the 8 keys one
+//    half-wave reads are 8 consecutive rows, which the 288-byte pitch spreads
+//    over disjoint banks.  Each 16-lane group loads one 256-byte V row (four
+//    rows per thread, after the first half's scores) and stores it at the end
+//    of the tile.
 //  * Loader addressing: buffer loads from a scalar descriptor per tile with
 //    per-thread 32-bit offsets computed once; the current segment's key range
 //    and base pointers stay in scalar registers (the segment table in kernel
@@ -65,6 +72,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int D = 128;
 constexpr int NQT = 3;           // 16-query tiles per wave
@@ -74,9 +83,9 @@ constexpr int BM = QW * NWAVES;  // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int KP = 128;  // K row pitch in LDS (bf16): 256 B, chunks XOR-swizzled by row
-constexpr int VTP = 72;  // V^T row pitch in LDS (bf16): 144 B
+constexpr int VP = 144;  // V row pitch in LDS (bf16): 288 B, key-major
 constexpr int KBUF = BN * KP;
-constexpr int VBUF = D * VTP;
+constexpr int VBUF = BN * VP;
 constexpr int STAGE = KBUF + VBUF;
 constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit loads
 constexpr uint32_t kSumLimitBits = 0x5f800000u;  // 2^64: a half's row sum above it
@@ -164,10 +173,11 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   // Loader geometry.  K DMA: wave w fills LDS rows 16 w + 4 i + t (t = lane
   // >> 4, i = 0..3), lane slot p = lane & 15 of a row receiving chunk
   // p ^ (row & 15) of key 32 (w >> 1) + 4 (w & 1) + 8 i + t.  V: thread covers
-  // the 16-byte chunk vc (dims 8 vc .. +7) of tile rows 4 kq .. 4 kq + 3.
+  // the 16-byte chunk lcc of tile rows lr0 + 16 i (16 lanes read one row).
   const int t4 = lane >> 4;
-  const int kq = lane & 15;
-  const int vc = 4 * wave + t4;
+  const int lcc = tid & 15;  // V: 16-byte chunk of rows lr0 + 16 i
+  const int lr0 = tid >> 4;
+  const int vrow0 = (lr0 & ~12) | ((lr0 & 4) << 1) | ((lr0 & 8) >> 1);  // LDS row of key lr0
   const int ntiles = (nk + BN - 1) / BN;
   const uint32_t rs_bytes = (uint32_t)rs * 2u;
   const uint32_t hoff = (uint32_t)(head * D * 2);
@@ -176,7 +186,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     kdoff[i] = kkey0 * rs_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * i + t4));
-  const uint32_t voff = (uint32_t)(4 * kq) * rs_bytes + (uint32_t)(vc * 16);
+  const uint32_t voff = (uint32_t)lr0 * rs_bytes + (uint32_t)(lcc * 16);
   uint4 vreg[4];
 
   // Segment of the tile being loaded, kept in scalar registers: the segment
@@ -237,31 +247,21 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
           __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, i * rs_bytes, 0);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 16 * i * rs_bytes, 0);
         vreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
       }
     } else {
       const int t0 = tile * BN;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = row_load(t0, 4 * kq + i, vc, true);
+      for (int i = 0; i < 4; ++i) vreg[i] = row_load(t0, lr0 + 16 * i, lcc, true);
     }
   };
   auto vstore = [&](int buf) __attribute__((always_inline)) {
-    // V^T[8 vc + j][4 kq .. 4 kq + 3]: pairs of keys packed per dword
-    uint16_t* vt = lds + buf * STAGE + KBUF;
-    const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
-                              {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
-                              {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
-                              {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
+    // key lr0 + 16 i lives in LDS row 16 i + vrow0 (key bits 2 and 3 swapped)
+    uint16_t* vb = lds + buf * STAGE + KBUF;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint2 even = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
-                                    __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
-      const uint2 odd = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
-                                   __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
-      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m) * VTP + 4 * kq) = even;
-      *reinterpret_cast<uint2*>(vt + (8 * vc + 2 * m + 1) * VTP + 4 * kq) = odd;
-    }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(vb + (16 * i + vrow0) * VP + lcc * 8) = vreg[i];
   };
 
   typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -282,7 +282,10 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* kb = lds + (j & 1) * STAGE;
     // K fragment: row 16 blk + c, chunk 4 s + g, stored at chunk (4 s + g) ^ c
     const uint16_t* kr = kb + c * KP;
-    const uint16_t* vt = kb + KBUF + c * VTP + 8 * g;
+    // V operand by transposing reads (B = 0, 1 for keys + 0..3, + 4..7): this lane
+    // addresses key 32 h + 8 g + (c >> 2) + 4 B, dims 16 dt + 4 (c & 3) .. +3, which
+    // sits in LDS row 32 h + 16 (g >> 1) + 8 B + 4 (g & 1) + (c >> 2)
+    const uint16_t* vt = kb + KBUF + (16 * (g >> 1) + 4 * (g & 1) + (c >> 2)) * VP + 4 * (c & 3);
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -364,7 +367,11 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       // O^T[d][query] += V^T P^T: A operand = V^T[16 dt + c][32 h + 8 g .. +7]
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + 16 * dt * VTP + 32 * h);
+        const uint16_t* va = vt + 32 * h * VP + 16 * dt;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * VP));
+        const bf16x8_t a =
+            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt)
           o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nt], o[dt][nt], 0, 0, 0);
