@@ -134,7 +134,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
 
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
   const int c = lane & 15;  // query (scores) / row (operands) within a 16-tile
   const int g = lane >> 4;  // 8-element k-group of the operands
   const int64_t rs = (int64_t)heads * D;
@@ -272,14 +272,17 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   vload(0);
   vstore(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile 0's K DMA has landed
-  for (int j = 0; j < ntiles; ++j) {
+  // One 64-key tile j computed from LDS buffer `cur` while tile j + 1 is staged
+  // into buffer 1 - cur.  The loop below runs two tiles per trip so that both
+  // buffers are compile-time constants (LDS addresses become immediates).
+  auto tile = [&](const int j, const int cur) __attribute__((always_inline)) {
     __syncthreads();
     const bool more = j + 1 < ntiles;
     if (more) {
       locate(j + 1);
-      kload(j + 1, (j + 1) & 1);
+      kload(j + 1, 1 - cur);
     }
-    const uint16_t* kb = lds + (j & 1) * STAGE;
+    const uint16_t* kb = lds + cur * STAGE;
     // K fragment: row 16 blk + c, chunk 4 s + g, stored at chunk (4 s + g) ^ c
     const uint16_t* kr = kb + c * KP;
     // V operand by transposing reads (B = 0, 1 for keys + 0..3, + 4..7): this lane
@@ -344,8 +347,8 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       probs();
       bool over = false;
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt)  // on the bits: also inf and NaN, whatever the NaN flags
-        over |= (__float_as_uint(tsum[nt]) & 0x7fffffffu) > kSumLimitBits;
+      for (int nt = 0; nt < NQT; ++nt)  // on the bits (sums are >= +0): also inf and any NaN,
+        over |= __float_as_uint(tsum[nt]) > kSumLimitBits;  // whatever the NaN flags
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt) {
@@ -378,9 +381,13 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       }
     }
     if (more) {
-      vstore((j + 1) & 1);
+      vstore(1 - cur);
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's K DMA has landed
     }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, 0);
+    if (j + 1 < ntiles) tile(j + 1, 1);
   }
 
 #pragma unroll
