@@ -7,13 +7,13 @@
 // quantised to 8 bits per element with one scale per tensor (the same notes,
 // Table 3: FP8 quantisation is part of the operator-level optimisation).
 //
-// Design (gfx950-native; shares the workgroup shape of the bf16 kernel):
+// Design (gfx950-native):
 //  * 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in LDS,
 //    one barrier per tile, Q fragments and the output accumulator in registers.
 //    Two waves per SIMD (<= 256 registers, 39 KB of LDS per workgroup).  At
 //    three per SIMD (168 registers) the loop-invariant addresses spilled to
 //    scratch, and the reload after each barrier waited (one in-order counter)
-//    for the next tile's prefetch as well: 1.82 ms against 1.58 ms here.
+//    for the next tile's prefetch as well (1.82 ms against 1.58 ms at two per SIMD).
 //  * Tile loads are buffer loads from a scalar descriptor (segment base + tile
 //    row + head, record count = the segment's remaining bytes) with one lane
 //    offset for K and one for V; the other rows of a thread differ by uniform
@@ -28,10 +28,14 @@
 //  * K rows are fed to the score MFMA in the order that makes accumulator row
 //    i of key block b hold key 32 ((i / 4) % 2) + 16 b + 4 (i / 8) + i % 4.
 //    Then lane l's 32 scores are keys 32 (l / 32) .. +31 in byte order, so P
-//    packs straight into the B operand of the second product, and V^T is
-//    stored in LDS in natural key order (one 16-byte row piece per read).
-//  * V is transposed by the loader threads in registers (v_perm_b32 on
-//    4-key x 8-dim byte blocks) and stored as V^T rows of 64 bytes.
+//    packs straight into the B operand of the second product.
+//  * V stays key-major in LDS (64 rows of 128 bytes, 160-byte pitch: the 8
+//    consecutive keys one half-wave reads land on disjoint banks) and the A
+//    operand of the second product (32 dims x 32 keys per lane) is read with
+//    four ds_read_b64_tr_b8: in each 16-lane group lane i receives, as byte j,
+//    byte i & 7 of the 8 bytes lane 2j + (i >> 3) addresses (measured on
+//    gfx950), so lanes addressing 8 dims of one key hand every lane the 8 keys
+//    of its dim.  The loader stores V rows as it loads them (no transpose).
 //  * Softmax in float32 with scale * dq * dk * log2(e) folded into the exponent;
 //    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
 //    of the subnormal range).
@@ -51,6 +55,8 @@ namespace la {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -64,9 +70,9 @@ constexpr int BN = 64;   // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int KP = 144;  // K row pitch in LDS (bytes): 16 rows hit 16 disjoint bank quads
-constexpr int VTP = 80;  // V^T row pitch in LDS (bytes): 16 rows hit 16 disjoint bank quads
+constexpr int VP = 160;  // V row pitch in LDS (bytes), key-major: 8 consecutive rows, disjoint banks
 constexpr int KBUF = BN * KP;
-constexpr int VBUF = D * VTP;
+constexpr int VBUF = BN * VP;
 constexpr int STAGE = KBUF + VBUF;
 constexpr float kPLift = 6.f;         // P is computed as exp2(s - m + 6)
 
@@ -140,22 +146,18 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
   const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
-  // Loader.  K: thread covers 16-byte chunk kc of key rows kr0 and kr0 + 32 (8 lanes
-  // read one 128-byte row).  V: thread covers dims 8 vc .. 8 vc + 7 of keys
-  // 4 kq .. 4 kq + 3 (8 bytes each) and writes them transposed, one dword per dim.
+  // Loader.  K and V alike: thread covers 16-byte chunk kc of key rows kr0 and
+  // kr0 + 32 (8 lanes read one 128-byte row).
   const int kc = tid & 7;
   const int kr0 = tid >> 3;
-  const int kq = tid & 15;
-  const int vc = tid >> 4;
   const int ntiles = (nk + BN - 1) / BN;
   const uint32_t rs32 = (uint32_t)rs;
-  // Lane offsets of the tile loads relative to the tile's first row of this
-  // head; the other rows of a thread are uniform multiples of the row stride
-  // (passed as the buffer loads' scalar offset).
+  // Lane offset of the tile loads (K and V) relative to the tile's first row of
+  // this head; the other row of a thread is 32 row strides further (passed as the
+  // buffer loads' scalar offset).
   const uint32_t koff = (uint32_t)kr0 * rs32 + (uint32_t)(kc * 16);
-  const uint32_t voff = (uint32_t)(4 * kq) * rs32 + (uint32_t)(vc * 8);
   uint4 kreg[2];
-  uint2 vreg[4];
+  uint4 vreg[2];
   // Segment holding the first key of the tile being loaded, with its key range
   // and base pointers kept in scalar registers: the segment table is read only
   // when a tile crosses into the next segment (a scalar load would also wait
@@ -189,9 +191,9 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
         kreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(vr, voff, t * rs32, 0);
-        vreg[t] = make_uint2(x[0], x[1]);
+      for (int i = 0; i < 2; ++i) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, koff, 32 * i * rs32, 0);
+        vreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
       }
     } else {
       // straddles a segment boundary or runs past the last key: per-row lookup,
@@ -206,10 +208,8 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
       };
       kreg[0] = *reinterpret_cast<const uint4*>(row_base(kr0, false) + kc * 16);
       kreg[1] = *reinterpret_cast<const uint4*>(row_base(kr0 + 32, false) + kc * 16);
-      vreg[0] = *reinterpret_cast<const uint2*>(row_base(4 * kq, true) + vc * 8);
-      vreg[1] = *reinterpret_cast<const uint2*>(row_base(4 * kq + 1, true) + vc * 8);
-      vreg[2] = *reinterpret_cast<const uint2*>(row_base(4 * kq + 2, true) + vc * 8);
-      vreg[3] = *reinterpret_cast<const uint2*>(row_base(4 * kq + 3, true) + vc * 8);
+      vreg[0] = *reinterpret_cast<const uint4*>(row_base(kr0, true) + kc * 16);
+      vreg[1] = *reinterpret_cast<const uint4*>(row_base(kr0 + 32, true) + kc * 16);
     }
   };
   auto lstore = [&](int buf) {
@@ -218,27 +218,9 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       *reinterpret_cast<uint4*>(kb + k_lds_row(kr0 + 32 * i) * KP + kc * 16) = kreg[i];
-    // V^T[8 vc + e][4 kq .. 4 kq + 3] = byte e of the four keys' 8-byte pieces
-    const uint32_t w[2][4] = {{vreg[0].x, vreg[1].x, vreg[2].x, vreg[3].x},
-                              {vreg[0].y, vreg[1].y, vreg[2].y, vreg[3].y}};
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t* x = w[half];
-      // bytes 0,1 (and 2,3) of keys 0,1 and of keys 2,3 interleaved
-      const uint32_t a01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
-      const uint32_t a23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
-      const uint32_t b01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
-      const uint32_t b23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
-      const uint32_t d0 = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
-      const uint32_t d1 = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
-      const uint32_t d2 = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
-      const uint32_t d3 = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
-      uint8_t* col = vt + (8 * vc + 4 * half) * VTP + 4 * kq;
-      *reinterpret_cast<uint32_t*>(col) = d0;
-      *reinterpret_cast<uint32_t*>(col + VTP) = d1;
-      *reinterpret_cast<uint32_t*>(col + 2 * VTP) = d2;
-      *reinterpret_cast<uint32_t*>(col + 3 * VTP) = d3;
-    }
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(vt + (kr0 + 32 * i) * VP + kc * 16) = vreg[i];
   };
 
   gload(0);
@@ -247,7 +229,10 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     if (j + 1 < ntiles) gload(j + 1);
     __syncthreads();
     const uint8_t* kb = lds + (j & 1) * STAGE;
-    const uint8_t* vt = kb + KBUF + l32 * VTP + 32 * hh;
+    // V operand by transposing reads: in each 16-lane group lane s addresses key
+    // 32 hh + 8 r + (s >> 1), dims 32 db + 16 ((lane >> 4) & 1) + 8 (s & 1) .. +7
+    const uint8_t* vt = kb + KBUF + (32 * hh + ((lane & 15) >> 1)) * VP + 16 * ((lane >> 4) & 1) +
+                        8 * (lane & 1);
 
     // S^T for the two 32-row key blocks: A = LDS row 32 b + lane % 32, bytes 64 ks + 32 hh ..
     f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
@@ -310,7 +295,12 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     // O^T[d][query] += V^T P^T: A = V^T row 32 db + lane % 32, keys 32 hh .. +31
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const i32x8_t a = ld32(vt + 32 * db * VTP);
+      i32x2_t part[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        part[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vt + 8 * r * VP + 32 * db));
+      const i32x8_t a = {part[0][0], part[0][1], part[1][0], part[1][1],
+                         part[2][0], part[2][1], part[3][0], part[3][1]};
       o[db] = mma(a, pf, o[db]);
     }
   }
