@@ -48,7 +48,7 @@ DT = -0.25
 # reports null (the counters were taken on a different kernel).
 ATTN_TRAFFIC_BYTES = {"attn-v8": 8.755e8}
 # The same for the e4m3 attention kernel at the C2 shape (--workload c2fp8).
-FP8_TRAFFIC_BYTES = {"fp8-v5": 5.4736e+08}
+FP8_TRAFFIC_BYTES = {"fp8-v6": 5.337e+08}
 
 
 _T0 = time.perf_counter()
@@ -361,7 +361,7 @@ def gpu_fp8_attn_bench(args, Hl, Wl, W, H, d):
 
 
 def kernel_version(prefix):
-    """The library's version tag of one kernel family (e.g. "attn-v8", "fp8-v5")."""
+    """The library's version tag of one kernel family (e.g. "attn-v8", "fp8-v6")."""
     import streaming_causal_video_amd as L
     return next((t for t in L.la_version().split() if t.startswith(prefix)), None)
 

@@ -121,7 +121,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
 
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t rs = (int64_t)heads * D;  // row stride in bytes
@@ -224,11 +224,14 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
   };
 
   gload(0);
-  for (int j = 0; j < ntiles; ++j) {
-    lstore(j & 1);
+  // One 64-key tile j from LDS buffer `cur` (its K/V registers are stored there
+  // first, then tile j + 1 is loaded into registers).  The loop runs two tiles per
+  // trip so that both buffers are compile-time constants (immediate LDS offsets).
+  auto tile = [&](const int j, const int cur) __attribute__((always_inline)) {
+    lstore(cur);
     if (j + 1 < ntiles) gload(j + 1);
     __syncthreads();
-    const uint8_t* kb = lds + (j & 1) * STAGE;
+    const uint8_t* kb = lds + cur * STAGE;
     // V operand by transposing reads: in each 16-lane group lane s addresses key
     // 32 hh + 8 r + (s >> 1), dims 32 db + 16 ((lane >> 4) & 1) + 8 (s & 1) .. +7
     const uint8_t* vt = kb + KBUF + (32 * hh + ((lane & 15) >> 1)) * VP + 16 * ((lane >> 4) & 1) +
@@ -303,6 +306,10 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
                          part[2][0], part[2][1], part[3][0], part[3][1]};
       o[db] = mma(a, pf, o[db]);
     }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, 0);
+    if (j + 1 < ntiles) tile(j + 1, 1);
   }
 
   const float lt = l_run;  // the full row sum (every row of the sum MFMA holds it)

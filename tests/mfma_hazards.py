@@ -7,7 +7,7 @@ them.  This checker walks the control-flow graph of every function in the
 assembly and reports:
 
   * a non-MFMA instruction that reads or writes a register of an MFMA result
-    (VGPR or AGPR) fewer than ``passes + 4`` wait states after the MFMA issued
+    (VGPR or AGPR) fewer than ``result_window(passes)`` wait states after the MFMA issued
     (an MFMA that accumulates into exactly the same registers is allowed: the
     hardware forwards back-to-back accumulations);
   * a non-MFMA instruction that writes a register an MFMA reads as its
@@ -18,9 +18,11 @@ assembly and reports:
 
 ``passes`` is the MFMA's number of 4-cycle passes on gfx950 (``mfma_passes``):
 4 for the 16x16x32 bf16/f16 forms, 8 for 32x32x16, 16 for the 32x32x64 fp8
-form; the windows are the figures the compiler uses for gfx950's XDL ops (12
-and 7 wait states for 8 passes).  ``mfma_window`` / ``srcc_window`` override
-them for every MFMA.
+form.  The windows are the figures the compiler schedules for gfx950's XDL ops:
+a result may be read 8, 12 and 19 wait states after a 4-, 8- and 16-pass MFMA
+issued (one more than gfx940's passes + 3 for 4 and 8 passes, not for 16), and
+its accumulator input overwritten passes - 1 after.  ``mfma_window`` /
+``srcc_window`` override them for every MFMA.
 
 Wait states are counted as the compiler does: one per instruction, N + 1 for
 ``s_nop N``.  Along control flow the count is the minimum over all paths
@@ -143,9 +145,10 @@ def _blocks(body):
 _PASSES = [
     (re.compile(r"v_mfma_f32_16x16x32_(bf16|f16)\b"), 4),
     (re.compile(r"v_mfma_f32_32x32x16_(bf16|f16)\b"), 8),
-    (re.compile(r"v_mfma_scale_f32_16x16x128_f8f6f4\b"), 8),
-    (re.compile(r"v_mfma_scale_f32_32x32x64_f8f6f4\b"), 16),
+    (re.compile(r"v_mfma_(scale_)?f32_16x16x128_f8f6f4\b"), 8),
+    (re.compile(r"v_mfma_(scale_)?f32_32x32x64_f8f6f4\b"), 16),
 ]
+_RESULT_WINDOW = {4: 8, 8: 12, 16: 19}
 
 
 def mfma_passes(op):
@@ -223,7 +226,7 @@ def check(text, mfma_window=None, valu_window=2, srcc_window=None):
                                 del d[reg]
                 if kind == "mfma" and defs:
                     p = mfma_passes(op)
-                    mw = mfma_window if mfma_window is not None else p + 4
+                    mw = mfma_window if mfma_window is not None else _RESULT_WINDOW.get(p, p + 4)
                     cw = srcc_window if srcc_window is not None else p - 1
                     for reg in defs[0]:
                         mf[reg] = (mw, defs[0])

@@ -87,6 +87,7 @@ def test_checker_windows_follow_the_pass_count():
     assert mh.mfma_passes("v_mfma_f32_16x16x32_bf16") == 4
     assert mh.mfma_passes("v_mfma_f32_32x32x16_bf16") == 8
     assert mh.mfma_passes("v_mfma_scale_f32_32x32x64_f8f6f4") == 16
+    assert mh.mfma_passes("v_mfma_f32_32x32x64_f8f6f4") == 16
     short = "\tv_mfma_f32_16x16x32_bf16 v[16:19], v[0:3], v[4:7], 0\n"
     # a 4-pass result may be read 8 wait states after issue, not 7
     assert mh.check(_fn(short + "\ts_nop 7\n\tv_add_f32_e32 v40, v16, v17\n")) == []
@@ -94,3 +95,9 @@ def test_checker_windows_follow_the_pass_count():
     # the same spacing is too short for an 8-pass result
     assert len(mh.check(_fn(MFMA.format(d="v[16:31]", c="0")
                             + "\ts_nop 7\n\tv_add_f32_e32 v40, v16, v17\n"))) == 1
+
+
+def test_checker_16_pass_result_window_is_19():
+    long = "\tv_mfma_f32_32x32x64_f8f6f4 v[16:31], v[0:7], v[8:15], 0\n"
+    assert mh.check(_fn(long + "\ts_nop 15\n\ts_nop 2\n\tv_add_f32_e32 v40, v16, v17\n")) == []
+    assert len(mh.check(_fn(long + "\ts_nop 15\n\ts_nop 1\n\tv_add_f32_e32 v40, v16, v17\n"))) == 1
