@@ -522,8 +522,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs one GPU's stage only (asked for {args.gpus} GPUs); the multi-GPU "
-              "pipeline is not part of this build.", file=sys.stderr)
+        print(f"bench.py runs one GPU's stage only (asked for {args.gpus} GPUs); spreading the "
+              "denoise stages over several GPUs is not implemented.", file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py is single-process; WORLD_SIZE > 1 is not supported.", file=sys.stderr)
