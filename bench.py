@@ -46,7 +46,7 @@ DT = -0.25
 # from rocprofv3 FETCH_SIZE/WRITE_SIZE runs scaled by a copy kernel of known size,
 # keyed by the attention kernel version the library reports; any other version
 # reports null (the counters were taken on a different kernel).
-ATTN_TRAFFIC_BYTES = {"attn-v8": 8.755e8}
+ATTN_TRAFFIC_BYTES = {"attn-v9": 8.618e8}
 # The same for the e4m3 attention kernel at the C2 shape (--workload c2fp8).
 FP8_TRAFFIC_BYTES = {"fp8-v6": 5.337e+08}
 
@@ -361,7 +361,7 @@ def gpu_fp8_attn_bench(args, Hl, Wl, W, H, d):
 
 
 def kernel_version(prefix):
-    """The library's version tag of one kernel family (e.g. "attn-v8", "fp8-v6")."""
+    """The library's version tag of one kernel family (e.g. "attn-v9", "fp8-v6")."""
     import streaming_causal_video_amd as L
     return next((t for t in L.la_version().split() if t.startswith(prefix)), None)
 

@@ -45,17 +45,16 @@
 //    16-byte chunk c of row r sits at chunk c ^ (r & 15), which keeps the
 //    fragment reads free of bank conflicts.  Tiles that straddle a segment
 //    boundary or run past the last key take a synchronous per-row copy.
-//  * V stays key-major in LDS (64 rows of 128 dims, 288-byte pitch) and the A
+//  * V stays key-major in LDS (64 rows of 128 dims, 256-byte pitch) and the A
 //    operand of the second product (V^T: 16 dims x 8 keys per lane) is read
 //    with two ds_read_b64_tr_b16: in each 16-lane group lane i receives, as
 //    element j, element i & 3 of the 8 bytes lane 4j + (i >> 2) addresses
 //    (measured on gfx950), so a lane that addresses key j, dims 4m .. 4m+3
 //    feeds exactly the operand layout; no v_perm transpose in the loader.
-//    Keys sit in LDS rows with key bits 2 and 3 swapped, so the 8 keys one
-//    half-wave reads are 8 consecutive rows, which the 288-byte pitch spreads
-//    over disjoint banks.  Each 16-lane group loads one 256-byte V row (four
-//    rows per thread, after the first half's scores) and stores it at the end
-//    of the tile.
+//    V tiles also arrive by DMA (issued after the first half's scores), with
+//    16-byte chunk c of key k at chunk c ^ (2 (k & 3) + 8 (bit 3 of k)): the
+//    8 keys and two chunks a half-wave reads then fill all 64 banks once, and
+//    the d-tile of a read is an XOR of one per-lane address with 32 dt.
 //  * Loader addressing: buffer loads from a scalar descriptor per tile with
 //    per-thread 32-bit offsets computed once; the current segment's key range
 //    and base pointers stay in scalar registers (the segment table in kernel
@@ -83,7 +82,7 @@ constexpr int BM = QW * NWAVES;  // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int KP = 128;  // K row pitch in LDS (bf16): 256 B, chunks XOR-swizzled by row
-constexpr int VP = 144;  // V row pitch in LDS (bf16): 288 B, key-major
+constexpr int VP = 128;  // V row pitch in LDS (bf16): 256 B, key-major, chunks XOR-swizzled
 constexpr int KBUF = BN * KP;
 constexpr int VBUF = BN * VP;
 constexpr int STAGE = KBUF + VBUF;
@@ -172,12 +171,8 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
 
   // Loader geometry.  K DMA: wave w fills LDS rows 16 w + 4 i + t (t = lane
   // >> 4, i = 0..3), lane slot p = lane & 15 of a row receiving chunk
-  // p ^ (row & 15) of key 32 (w >> 1) + 4 (w & 1) + 8 i + t.  V: thread covers
-  // the 16-byte chunk lcc of tile rows lr0 + 16 i (16 lanes read one row).
+  // p ^ (row & 15) of key 32 (w >> 1) + 4 (w & 1) + 8 i + t.
   const int t4 = lane >> 4;
-  const int lcc = tid & 15;  // V: 16-byte chunk of rows lr0 + 16 i
-  const int lr0 = tid >> 4;
-  const int vrow0 = (lr0 & ~12) | ((lr0 & 4) << 1) | ((lr0 & 8) >> 1);  // LDS row of key lr0
   const int ntiles = (nk + BN - 1) / BN;
   const uint32_t rs_bytes = (uint32_t)rs * 2u;
   const uint32_t hoff = (uint32_t)(head * D * 2);
@@ -186,8 +181,15 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     kdoff[i] = kkey0 * rs_bytes + 16u * (uint32_t)((lane & 15) ^ (4 * i + t4));
-  const uint32_t voff = (uint32_t)lr0 * rs_bytes + (uint32_t)(lcc * 16);
-  uint4 vreg[4];
+  // V DMA: wave w fills key rows 16 w + 4 i + t, slot p receiving chunk
+  // p ^ vswz(row), vswz(k) = 2 (k & 3) + 8 (bit 3 of k)
+  const uint32_t vkey0 = (uint32_t)(16 * wave + t4);
+  const uint32_t vdoff[2] = {vkey0 * rs_bytes + 16u * (uint32_t)((lane & 15) ^ (2 * t4)),
+                             vkey0 * rs_bytes + 16u * (uint32_t)((lane & 15) ^ (2 * t4 + 8))};
+  // V operand read: this lane's key 8 g + (c >> 2) (+ 4 B + 32 h), bytes 32 dt + 8 (c & 3)
+  // of the row, i.e. chunk (2 dt + bit 1 of c) ^ vswz(key); XOR with 32 dt selects the d-tile
+  const uint32_t vlane = (uint32_t)((8 * g + (c >> 2)) * 2 * VP + 16 * ((c >> 1) & 1) +
+                                    16 * (2 * (c >> 2) + 8 * (g & 1)) + 8 * (c & 1));
 
   // Segment of the tile being loaded, kept in scalar registers: the segment
   // table is read only when a tile crosses into the next segment.
@@ -241,27 +243,26 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       }
     }
   };
-  auto vload = [&](int tile) __attribute__((always_inline)) {
+  auto vload = [&](int tile, int buf) __attribute__((always_inline)) {
+    uint16_t* vb = lds + buf * STAGE + KBUF;
     if (whole) {
       const __amdgpu_buffer_rsrc_t vr =
           __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 16 * i * rs_bytes, 0);
-        vreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
-      }
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void*)(vb + (16 * wave + 4 * i) * VP), 16,
+            vdoff[i >> 1], 4 * i * rs_bytes, 0, 0);
     } else {
       const int t0 = tile * BN;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = row_load(t0, lr0 + 16 * i, lcc, true);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * i + t4;
+        const int sw = 2 * (r & 3) + 8 * ((r >> 3) & 1);
+        const uint4 x = row_load(t0, r, (lane & 15) ^ sw, true);
+        *reinterpret_cast<uint4*>(vb + r * VP + (lane & 15) * 8) = x;
+      }
     }
-  };
-  auto vstore = [&](int buf) __attribute__((always_inline)) {
-    // key lr0 + 16 i lives in LDS row 16 i + vrow0 (key bits 2 and 3 swapped)
-    uint16_t* vb = lds + buf * STAGE + KBUF;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(vb + (16 * i + vrow0) * VP + lcc * 8) = vreg[i];
   };
 
   typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -269,8 +270,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
 
   locate(0);
   kload(0, 0);
-  vload(0);
-  vstore(0);
+  vload(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile 0's K DMA has landed
   // One 64-key tile j computed from LDS buffer `cur` while tile j + 1 is staged
   // into buffer 1 - cur.  The loop below runs two tiles per trip so that both
@@ -288,7 +288,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     // V operand by transposing reads (B = 0, 1 for keys + 0..3, + 4..7): this lane
     // addresses key 32 h + 8 g + (c >> 2) + 4 B, dims 16 dt + 4 (c & 3) .. +3, which
     // sits in LDS row 32 h + 16 (g >> 1) + 8 B + 4 (g & 1) + (c >> 2)
-    const uint16_t* vt = kb + KBUF + (16 * (g >> 1) + 4 * (g & 1) + (c >> 2)) * VP + 4 * (c & 3);
+    const char* vt = reinterpret_cast<const char*>(kb + KBUF);
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -308,7 +308,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
           for (int nt = 0; nt < NQT; ++nt)
             st[b][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[b][nt], 0, 0, 0);
         }
-      if (h == 0 && more) vload(j + 1);
+      if (h == 0 && more) vload(j + 1, 1 - cur);
       if ((j + 1) * BN > nk) {
         // last tile: row 4 g + i of block 2 h + b holds key 32 h + 8 g + 4 b + i
 #pragma unroll
@@ -370,9 +370,9 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       // O^T[d][query] += V^T P^T: A operand = V^T[16 dt + c][32 h + 8 g .. +7]
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t* va = vt + 32 * h * VP + 16 * dt;
+        const char* va = vt + (vlane ^ (32 * dt)) + 64 * h * VP;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 8 * VP));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 4 * 2 * VP));
         const bf16x8_t a =
             __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -381,7 +381,6 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       }
     }
     if (more) {
-      vstore(1 - cur);
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's K DMA has landed
     }
   };

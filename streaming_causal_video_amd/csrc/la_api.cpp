@@ -45,7 +45,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.4 (gfx950) attn-v8 fp8-v6"; }
+const char* la_version(void) { return "liblahip 0.4 (gfx950) attn-v9 fp8-v6"; }
 
 const char* la_status_string(int st) {
   switch (st) {
