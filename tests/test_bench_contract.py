@@ -41,3 +41,18 @@ def test_c2_json_line_has_the_contract_fields():
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert r["kernel"] == "attn_bf16_kernel" and r["kernel_version"].startswith("attn-")
+
+
+def test_traffic_tables_name_the_library_kernel_versions():
+    """The HBM traffic bench.py reports is keyed by kernel version: a version
+    bump in the library without new counter figures would report null."""
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    src = open(os.path.join(ROOT, "streaming_causal_video_amd", "csrc", "la_api.cpp")).read()
+    tags = re.search(r'la_version\(void\) \{ return "([^"]*)"', src).group(1).split()
+    attn = [t for t in tags if t.startswith("attn-")]
+    fp8 = [t for t in tags if t.startswith("fp8-")]
+    assert len(attn) == 1 and len(fp8) == 1, tags
+    assert attn[0] in bench.ATTN_TRAFFIC_BYTES
+    assert fp8[0] in bench.FP8_TRAFFIC_BYTES
