@@ -90,6 +90,7 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
     sws = torch.empty((st, H, d), dtype=torch.bfloat16, device=dev)
     table = torch.empty(L.la_rope_table_bytes(Hl, Wl, d) // 4, dtype=torch.float32, device=dev)
     L.la_rope_table_fill(table, Hl, Wl, d, THETA)
+    aws = L.AttnWorkspace(bt, H) if args.attn_schedule == "balanced" else None
     lat_shape = (16, 3, 60, 104)
     x = torch.randn(lat_shape, device=dev, generator=gen) if with_euler else None
     vels = [torch.randn(lat_shape, device=dev, generator=gen) for _ in range(pool)] if with_euler else None
@@ -103,8 +104,9 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
         skn = [t[:st] for t in k] if b == 1 else None
         svn = [t[:st] for t in v] if b == 1 else None
         L.la_denoise_step(stack.states, b, q, k, v, outs, qws, kws, sws, table, Hl, Wl, FRAMES,
-                          DELTA, THETA, sink_k_new=skn, sink_v_new=svn, x=x,
-                          vel=vels[e] if with_euler else None, dt=DT, timing_events=events)
+                          DELTA, THETA, scale=d ** -0.5, sink_k_new=skn, sink_v_new=svn, x=x,
+                          vel=vels[e] if with_euler else None, dt=DT, timing_events=events,
+                          attn_ws=aws)
 
     # warm-up: block 1 (sink replacement) .. the ring is full after block W
     block = 0
@@ -204,6 +206,7 @@ def gpu_chain_bench(args, Hl, Wl, W, H, d, n_layers, n_stages=4):
     lat_shape = (16, 3, 60, 104)
     x = torch.randn(lat_shape, device=dev, generator=gen)
     vels = [torch.randn(lat_shape, device=dev, generator=gen) for _ in range(n_stages)]
+    aws = L.AttnWorkspace(bt, H) if args.attn_schedule == "balanced" else None
     torch.cuda.synchronize()
     log(f"allocated {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
@@ -220,7 +223,7 @@ def gpu_chain_bench(args, Hl, Wl, W, H, d, n_layers, n_stages=4):
                 g["sink_v_new"] = [ins[e][l][2][:st] for l in range(n_layers)]
             stages.append(g)
         L.la_denoise_chain(stages, b, qws, kws, sws, table, Hl, Wl, x=x, frames_per_block=FRAMES,
-                           sink_delta=DELTA, theta=THETA)
+                           sink_delta=DELTA, theta=THETA, scale=d ** -0.5, attn_ws=aws)
 
     block = 0
     for _ in range(W + args.warmup):
@@ -340,7 +343,7 @@ def gpu_fp8_attn_bench(args, Hl, Wl, W, H, d):
     out = torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev)
 
     def run():
-        L.la_block_attn_fwd_fp8(ring.state, q, sk, sv, k, v, out, sc, sc, sc)
+        L.la_block_attn_fwd_fp8(ring.state, q, sk, sv, k, v, out, sc, sc, sc, scale=d ** -0.5)
 
     for _ in range(args.warmup + 3):
         run()
@@ -428,6 +431,7 @@ def gpu_refresh_bench(args, Hl, Wl, W, H, d, n_layers, n_steps=4):
     lat_shape = (16, 3, 60, 104)
     x = torch.randn(lat_shape, device=dev, generator=gen)
     vels = [torch.randn(lat_shape, device=dev, generator=gen) for _ in range(n_steps)]
+    aws = L.AttnWorkspace(bt, H) if args.attn_schedule == "balanced" else None
     torch.cuda.synchronize()
 
     def step(b):
@@ -437,10 +441,12 @@ def gpu_refresh_bench(args, Hl, Wl, W, H, d, n_layers, n_steps=4):
         v = [ins[e][l][2] for l in range(n_layers)]
         for i in range(n_steps):
             L.la_denoise_step(stack.states, b, q, k, v, outs, qws, kws, sws, table, Hl, Wl, FRAMES,
-                              DELTA, THETA, x=x, vel=vels[i], dt=DT, flags=L.LA_STEP_ATTEND_ONLY)
+                              DELTA, THETA, scale=d ** -0.5, x=x, vel=vels[i], dt=DT,
+                              flags=L.LA_STEP_ATTEND_ONLY, attn_ws=aws)
         L.la_denoise_step(stack.states, b, q, k, v, outs, qws, kws, sws, table, Hl, Wl, FRAMES,
-                          DELTA, THETA, sink_k_new=[t[:st] for t in k] if b == 1 else None,
-                          sink_v_new=[t[:st] for t in v] if b == 1 else None)
+                          DELTA, THETA, scale=d ** -0.5,
+                          sink_k_new=[t[:st] for t in k] if b == 1 else None,
+                          sink_v_new=[t[:st] for t in v] if b == 1 else None, attn_ws=aws)
 
     block = 0
     for _ in range(W + args.warmup):
@@ -520,6 +526,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0,
                     help="layers per stage for the chain / refresh workloads (default 40)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--attn-schedule", choices=["balanced", "grid"], default="balanced",
+                    help="attention work schedule: persistent balanced grid with a workspace "
+                         "(default) or one workgroup per query tile")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs one GPU's stage only (asked for {args.gpus} GPUs); spreading the "

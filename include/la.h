@@ -173,13 +173,17 @@ la_status la_rope_table_fill(void* dev_table, int32_t Hl, int32_t Wl, int32_t he
  *   store.  LA_F32: float32 throughout.  1 <= n_frames <= LA_MAX_BLOCK_FRAMES;
  *   head_dim % 8 == 0, 8 <= head_dim <= 256, and the frame band holds at most
  *   48 pairs.
+ *   q_scale (> 0, finite): q_out = q_scale * (rotated q), multiplied in float32
+ *   before the one rounding of the store (k_out and the sink are not scaled).
+ *   1 gives the plain rotation; la_denoise_step passes scale * log2(e) so that
+ *   the attention that follows takes its base-2 scores straight from Q K^T.
  *   Pointers must be 16-byte aligned.
  */
 la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, void* k_out,
                             int32_t n_frames, int64_t f0, const void* sink_k_in,
                             void* sink_k_out, int64_t sink_delta, const void* dev_table,
                             int32_t Hl, int32_t Wl, int32_t heads, int32_t head_dim,
-                            la_dtype dtype, double theta, la_stream_t stream);
+                            la_dtype dtype, double theta, float q_scale, la_stream_t stream);
 
 /*
  * la_block_attn_fwd - block attention of the current block (NOTES, 整体框架:
@@ -196,17 +200,46 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
  * appending the current block.
  *
  *   q_rot, k_cur_rot, v_cur, out : [n_q][heads][head_dim]; n_q = r->block_tokens.
+ *       q_rot holds q_scale times the rotated query (q_scale as given to
+ *       la_rope3d_rolling; 1 for the plain rotation): the scores are
+ *       scale / q_scale * q_rot . k.
  *   sink_k_rot : [r->sink_tokens][heads][head_dim] (output of la_rope3d_rolling).
  *   lse_or_null: if non-NULL, float32 [heads][n_q] natural-log
  *                log(sum exp(scale q.k)) per row.
- *   LA_BF16: bf16 MFMA products with float32 accumulation and float32 online
- *            softmax, bf16 output (round-to-nearest-even); head_dim == 128.
+ *   scale, q_scale : > 0 and finite.
+ *   workspace  : NULL, or device memory of at least la_attn_workspace_bytes(n_q,
+ *                r->heads) bytes, 256-byte aligned, zero-filled before its first
+ *                use (each call leaves it zero-filled again).  Without a workspace
+ *                the bf16 kernel runs one workgroup per (head, 192-query tile).
+ *                With one it runs a persistent grid of two workgroups per compute
+ *                unit: whole rounds of query tiles, then, when the last round would
+ *                leave more than half of the workgroups idle, the query tiles of
+ *                that round are cut into equal key ranges whose partial results
+ *                are merged (in a fixed order) by the last piece to finish.
+ *                Results are deterministic either way (not bit-identical between
+ *                the two when a round is cut).  Calls that share a workspace must
+ *                not run concurrently.  Ignored for LA_F32.
+ *   LA_BF16: bf16 MFMA products with float32 accumulation and a float32 online
+ *            softmax in base 2, bf16 output (round-to-nearest-even); head_dim ==
+ *            128.  The products take Q times scale * log2(e) / q_scale rounded to
+ *            bf16, or q_rot unchanged when that factor is 1 in float32 (q_scale ==
+ *            scale * log2(e) rounded to float32).
  *   LA_F32 : float32 throughout; head_dim 64 or 128.
  *   Pointers 16-byte aligned; `out` must not alias an input.
  */
 la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot,
                             const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
-                            float* lse_or_null, float scale, la_stream_t stream);
+                            float* lse_or_null, float scale, float q_scale, void* workspace,
+                            size_t workspace_bytes, la_stream_t stream);
+
+/*
+ * la_attn_workspace_bytes - size of the la_block_attn_fwd workspace for n_q
+ * queries and `heads` heads on the current device (an arrival counter per
+ * 192-query tile and head, and one partial record of 104,448 bytes per
+ * workgroup of the persistent grid, two workgroups per compute unit: 53.5 MB on
+ * a 256-CU MI355X).  0 if an argument is invalid or the device cannot be queried.
+ */
+size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads);
 
 /*
  * la_kvcache_append_evict - put block `block_id`'s rotated K and its V
@@ -276,7 +309,12 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *   rope_table             : la_rope_table_fill output for (Hl, Wl, head_dim, theta);
  *                            block_tokens must equal frames_per_block*Hl*Wl and
  *                            sink_tokens Hl*Wl.
- *   scale                  : softmax scale (1/sqrt(head_dim) for the model).
+ *   scale                  : softmax scale (1/sqrt(head_dim) for the model).  For
+ *                            bf16 rings step 1 writes Q times scale * log2(e)
+ *                            (la_rope3d_rolling's q_scale) and step 2 takes it as
+ *                            given.
+ *   attn_ws, attn_ws_bytes : the la_block_attn_fwd workspace shared by every
+ *                            layer (NULL for none).
  *   timing_events          : NULL, or 6*n_layers + 2 caller-created hipEvent_t
  *                            (as void*) recorded on `stream` around each layer's
  *                            RoPE [6l, 6l+1], attention [6l+2, 6l+3] and append
@@ -292,9 +330,9 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           void* k_rot_ws, void* sink_k_rot_ws, const void* const* sink_k_new,
                           const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                           int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
-                          double theta, float scale, float* x, const float* vel,
-                          int64_t n_latent, float dt, uint32_t flags,
-                          void* const* timing_events, la_stream_t stream);
+                          double theta, float scale, void* attn_ws, size_t attn_ws_bytes,
+                          float* x, const float* vel, int64_t n_latent, float dt,
+                          uint32_t flags, void* const* timing_events, la_stream_t stream);
 
 #define LA_STEP_ATTEND_ONLY 1u
 
@@ -366,8 +404,9 @@ typedef struct la_stage {
  * 80 GB card; NOTES, Table 3: four denoise steps on one GPU before the steps are
  * spread over GPUs; NOTES, 关键设计 4 and BLOG, 疑问 6: each stage keeps caches
  * at its own noise level and hands only the latent on).  Stage s is la_denoise_step(stages[s].rings, ...,
- * x, stages[s].vel, n_latent, stages[s].dt) with the shared workspaces, RoPE
- * table and geometry; the latent x is updated in place stage after stage.
+ * x, stages[s].vel, n_latent, stages[s].dt) with the shared workspaces (attn_ws
+ * included), RoPE table and geometry; the latent x is updated in place stage
+ * after stage.
  *
  * Besides every la_denoise_step check for every stage, the noise levels must
  * chain: stages[s+1].rings[*].noise_level == stages[s].rings[*].noise_level +
@@ -380,7 +419,8 @@ la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
                            int64_t block_id, void* q_rot_ws, void* k_rot_ws,
                            void* sink_k_rot_ws, const void* rope_table, int32_t Hl, int32_t Wl,
                            int32_t frames_per_block, int64_t sink_delta, double theta,
-                           float scale, float* x, int64_t n_latent, la_stream_t stream);
+                           float scale, void* attn_ws, size_t attn_ws_bytes, float* x,
+                           int64_t n_latent, la_stream_t stream);
 
 #ifdef __cplusplus
 }

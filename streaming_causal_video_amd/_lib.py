@@ -28,6 +28,7 @@ EXPORTED = [
     "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
     "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
     "la_denoise_step", "la_denoise_chain", "la_quantize_fp8", "la_block_attn_fwd_fp8",
+    "la_attn_workspace_bytes",
 ]
 
 
@@ -116,6 +117,7 @@ def _load():
                           "/opt/rocm's libamdhip64")
     P, I32, I64, F, D, VP = (ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_double, ctypes.c_void_p)
+    SZ = ctypes.c_size_t
     R = P(la_kvring)
     sig = {
         "la_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -127,19 +129,20 @@ def _load():
         "la_rope_table_bytes": (ctypes.c_size_t, [I32, I32, I32]),
         "la_rope_table_fill": (ctypes.c_int, [VP, I32, I32, I32, D, VP]),
         "la_rope3d_rolling": (ctypes.c_int, [VP, VP, VP, VP, I32, I64, VP, VP, I64, VP, I32, I32,
-                                             I32, I32, ctypes.c_int, D, VP]),
-        "la_block_attn_fwd": (ctypes.c_int, [R, VP, VP, VP, VP, I32, VP, VP, F, VP]),
+                                             I32, I32, ctypes.c_int, D, F, VP]),
+        "la_block_attn_fwd": (ctypes.c_int, [R, VP, VP, VP, VP, I32, VP, VP, F, F, VP, SZ, VP]),
+        "la_attn_workspace_bytes": (SZ, [I32, I32]),
         "la_kvcache_append_evict": (ctypes.c_int, [R, VP, VP, I64, F, P(I64), VP]),
         "la_sink_replace": (ctypes.c_int, [R, VP, VP, VP]),
         "la_fm_euler_step": (ctypes.c_int, [VP, VP, I64, F, VP]),
         "la_denoise_step": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP, VP,
-                                           P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, VP,
-                                           I64, F, ctypes.c_uint32, P(VP), VP]),
+                                           P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, SZ,
+                                           VP, VP, I64, F, ctypes.c_uint32, P(VP), VP]),
         "la_quantize_fp8": (ctypes.c_int, [VP, ctypes.c_int, VP, I64, F, VP]),
         "la_block_attn_fwd_fp8": (ctypes.c_int, [R, VP, VP, VP, VP, VP, I32, VP, VP, F, F, F, F,
                                                  VP]),
         "la_denoise_chain": (ctypes.c_int, [P(la_stage), I32, I32, I64, VP, VP, VP, VP, I32, I32,
-                                            I32, I64, D, F, VP, I64, VP]),
+                                            I32, I64, D, F, VP, SZ, VP, I64, VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -174,18 +177,23 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _ptr(t, name: str, shape=None, dtype=None):
-    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
-    if t is None:
-        return None
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _check_tensor(t, name: str, shape=None, dtype=None):
+    """Shape, dtype and contiguity of a tensor argument (not its device)."""
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t, name: str, shape=None, dtype=None):
+    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    _check_tensor(t, name, shape, dtype)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -238,7 +246,8 @@ def la_rope_table_fill(table, Hl: int, Wl: int, head_dim: int, theta: float = 10
 
 def la_rope3d_rolling(q_in, q_out, k_in, k_out, n_frames: int, f0: int, sink_k_in, sink_k_out,
                       sink_delta: int, table, Hl: int, Wl: int, heads: int, head_dim: int,
-                      theta: float = 10000.0) -> None:
+                      theta: float = 10000.0, q_scale: float = 1.0) -> None:
+    """q_out = q_scale * rotated q_in (q_scale = 1: the plain rotation)."""
     ref = next(t for t in (q_in, k_in, sink_k_in) if t is not None)
     dt = _dtype_code(ref)
     blk = (n_frames * Hl * Wl, heads, head_dim)
@@ -249,25 +258,51 @@ def la_rope3d_rolling(q_in, q_out, k_in, k_out, n_frames: int, f0: int, sink_k_i
              _ptr(sink_k_out, "sink_k_out", snk, ref.dtype)]
     _check(_load().la_rope3d_rolling(*args, n_frames, f0, *sargs, sink_delta,
                                      _ptr(table, "table"), Hl, Wl, heads, head_dim, dt, theta,
-                                     _stream()), "la_rope3d_rolling")
+                                     q_scale, _stream()), "la_rope3d_rolling")
+
+
+def la_attn_workspace_bytes(n_q: int, heads: int) -> int:
+    return _load().la_attn_workspace_bytes(n_q, heads)
+
+
+class AttnWorkspace:
+    """Zero-filled device buffer for la_block_attn_fwd's balanced schedule (one per
+    stream of attention calls; each call leaves it zero-filled again)."""
+
+    def __init__(self, n_q: int, heads: int, device="cuda"):
+        torch = _torch()
+        self.nbytes = la_attn_workspace_bytes(n_q, heads)
+        if self.nbytes == 0:
+            raise ValueError("la_attn_workspace_bytes failed (arguments or device)")
+        self.buf = torch.zeros(self.nbytes, dtype=torch.uint8, device=device)
+        if self.buf.data_ptr() % 256:
+            raise RuntimeError("attention workspace is not 256-byte aligned")
+
+
+def _ws(ws: Optional[AttnWorkspace]):
+    if ws is None:
+        return None, 0
+    return _ptr(ws.buf, "workspace"), ws.nbytes
 
 
 def la_block_attn_fwd(ring: "la_kvring", q_rot, sink_k_rot, k_cur_rot, v_cur, out,
-                      lse: Optional[object] = None, scale: Optional[float] = None) -> None:
+                      lse: Optional[object] = None, *, scale: float, q_scale: float = 1.0,
+                      workspace: Optional[AttnWorkspace] = None) -> None:
+    """scale: the softmax scale of the scores; q_scale: the factor already applied to
+    q_rot (la_rope3d_rolling's q_scale); workspace: None or an AttnWorkspace."""
     torch = _torch()
     dtype = torch.bfloat16 if ring.dtype == LA_BF16 else torch.float32
     blk = (ring.block_tokens, ring.heads, ring.head_dim)
     snk = (ring.sink_tokens, ring.heads, ring.head_dim)
-    if scale is None:
-        scale = ring.head_dim ** -0.5
     lse_p = None
     if lse is not None:
         lse_p = _ptr(lse, "lse", (ring.heads, ring.block_tokens), torch.float32)
+    ws_p, ws_n = _ws(workspace)
     _check(_load().la_block_attn_fwd(
         ctypes.byref(ring), _ptr(q_rot, "q_rot", blk, dtype), _ptr(sink_k_rot, "sink_k_rot", snk, dtype),
         _ptr(k_cur_rot, "k_cur_rot", blk, dtype), _ptr(v_cur, "v_cur", blk, dtype),
-        ring.block_tokens, _ptr(out, "out", blk, dtype), lse_p, scale, _stream()),
-        "la_block_attn_fwd")
+        ring.block_tokens, _ptr(out, "out", blk, dtype), lse_p, scale, q_scale, ws_p, ws_n,
+        _stream()), "la_block_attn_fwd")
 
 
 def _slot_dtype(ring: "la_kvring"):
@@ -293,15 +328,13 @@ def la_quantize_fp8(x, out, inv_scale: float) -> None:
 
 
 def la_block_attn_fwd_fp8(ring: "la_kvring", q8, sink_k8, sink_v8, k8_cur, v8_cur, out, dq: float,
-                          dk: float, dv: float, lse: Optional[object] = None,
-                          scale: Optional[float] = None) -> None:
+                          dk: float, dv: float, lse: Optional[object] = None, *,
+                          scale: float) -> None:
     """e4m3 attention: q8, sink_k8, sink_v8, k8_cur, v8_cur are uint8 code tensors, out bf16."""
     torch = _torch()
     blk = (ring.block_tokens, ring.heads, ring.head_dim)
     snk = (ring.sink_tokens, ring.heads, ring.head_dim)
     u8 = torch.uint8
-    if scale is None:
-        scale = ring.head_dim ** -0.5
     lse_p = None
     if lse is not None:
         lse_p = _ptr(lse, "lse", (ring.heads, ring.block_tokens), torch.float32)
@@ -338,75 +371,149 @@ def la_fm_euler_step(x, v, dt: float) -> None:
            "la_fm_euler_step")
 
 
-def _ptr_array(ts, name):
+def _check_list(ts, name, shape=None, dtype=None, n=None):
+    """_check_tensor on every entry of a per-layer tensor list of length n."""
+    if n is not None and len(ts) != n:
+        raise ValueError(f"{name} has {len(ts)} entries, expected {n}")
+    for i, t in enumerate(ts):
+        if t is None:
+            raise ValueError(f"{name}[{i}] is None")
+        _check_tensor(t, f"{name}[{i}]", shape, dtype)
+
+
+def _ptr_array(ts, name, shape=None, dtype=None, n=None):
+    """Host array of the device pointers of a list of tensors, each checked like _ptr."""
+    _check_list(ts, name, shape, dtype, n)
     arr = (ctypes.c_void_p * len(ts))()
     for i, t in enumerate(ts):
-        arr[i] = _ptr(t, f"{name}[{i}]").value
+        arr[i] = _ptr(t, f"{name}[{i}]", shape, dtype).value
     return arr
+
+
+def _step_dtype(ring: "la_kvring"):
+    """Tensor dtype of a step's per-layer activations (the step runs bf16 / f32 rings)."""
+    torch = _torch()
+    if ring.dtype == LA_BF16:
+        return torch.bfloat16
+    if ring.dtype == LA_F32:
+        return torch.float32
+    raise ValueError("la_denoise_step / la_denoise_chain run bf16 or float32 rings only")
+
+
+def _check_table(table, Hl: int, Wl: int, head_dim: int):
+    torch = _torch()
+    need = la_rope_table_bytes(Hl, Wl, head_dim)
+    if table.dtype != torch.float32 or table.numel() * 4 < need:
+        raise ValueError("rope_table must be float32 with at least la_rope_table_bytes bytes")
 
 
 def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_ws, k_rot_ws,
                     sink_k_rot_ws, rope_table, Hl: int, Wl: int, frames_per_block: int = 3,
-                    sink_delta: int = -1, theta: float = 10000.0, scale: Optional[float] = None,
+                    sink_delta: int = -1, theta: float = 10000.0, *, scale: float,
                     sink_k_new=None, sink_v_new=None, x=None, vel=None, dt: float = -0.25,
-                    timing_events=None, flags: int = 0) -> None:
+                    timing_events=None, flags: int = 0,
+                    attn_ws: Optional[AttnWorkspace] = None) -> None:
     """rings: a ctypes array of la_kvring (see KVRingStack); the other per-layer
-    arguments are lists of tensors.  timing_events: None or a ctypes array of
-    6*len(rings)+2 raw hipEvent_t handles.  flags: LA_STEP_ATTEND_ONLY or 0."""
+    arguments are lists of tensors.  scale: the softmax scale.  timing_events: None or a
+    ctypes array of 6*len(rings)+2 raw hipEvent_t handles.  flags: LA_STEP_ATTEND_ONLY
+    or 0.  attn_ws: None or an AttnWorkspace for the attention's balanced schedule."""
+    torch = _torch()
     n = len(rings)
-    if scale is None:
-        scale = rings[0].head_dim ** -0.5
-    skn = _ptr_array(sink_k_new, "sink_k_new") if sink_k_new is not None else None
-    svn = _ptr_array(sink_v_new, "sink_v_new") if sink_v_new is not None else None
+    if n < 1:
+        raise ValueError("rings is empty")
+    r0 = rings[0]
+    dtype = _step_dtype(r0)
+    blk = (r0.block_tokens, r0.heads, r0.head_dim)
+    snk = (r0.sink_tokens, r0.heads, r0.head_dim)
+    # every shape and dtype first, then the pointers
+    lists = [(q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (attn_out, "attn_out")]
+    for ts, name in lists:
+        _check_list(ts, name, blk, dtype, n)
+    for ts, name in ((sink_k_new, "sink_k_new"), (sink_v_new, "sink_v_new")):
+        if ts is not None:
+            _check_list(ts, name, snk, dtype, n)
+    for t, name, shp in ((q_rot_ws, "q_rot_ws", blk), (k_rot_ws, "k_rot_ws", blk),
+                         (sink_k_rot_ws, "sink_k_rot_ws", snk)):
+        _check_tensor(t, name, shp, dtype)
     n_lat = 0 if x is None else x.numel()
-    if x is not None and (vel is None or vel.numel() != n_lat):
-        raise ValueError("vel must match x")
+    if x is not None:
+        if vel is None or vel.numel() != n_lat:
+            raise ValueError("vel must match x")
+        if x.dtype != torch.float32 or vel.dtype != torch.float32:
+            raise ValueError("x and vel must be float32")
+    if timing_events is not None and len(timing_events) != 6 * n + 2:
+        raise ValueError(f"timing_events needs {6 * n + 2} events")
+    _check_table(rope_table, Hl, Wl, r0.head_dim)
+    skn = _ptr_array(sink_k_new, "sink_k_new", snk, dtype, n) if sink_k_new is not None else None
+    svn = _ptr_array(sink_v_new, "sink_v_new", snk, dtype, n) if sink_v_new is not None else None
+    ws_p, ws_n = _ws(attn_ws)
     _check(_load().la_denoise_step(
-        rings, n, block_id, _ptr_array(q_raw, "q_raw"), _ptr_array(k_raw, "k_raw"),
-        _ptr_array(v_raw, "v_raw"), _ptr_array(attn_out, "attn_out"), _ptr(q_rot_ws, "q_rot_ws"),
-        _ptr(k_rot_ws, "k_rot_ws"), _ptr(sink_k_rot_ws, "sink_k_rot_ws"), skn, svn,
-        _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta, scale,
-        _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, flags, timing_events, _stream()),
-        "la_denoise_step")
+        rings, n, block_id, _ptr_array(q_raw, "q_raw", blk, dtype, n),
+        _ptr_array(k_raw, "k_raw", blk, dtype, n), _ptr_array(v_raw, "v_raw", blk, dtype, n),
+        _ptr_array(attn_out, "attn_out", blk, dtype, n), _ptr(q_rot_ws, "q_rot_ws", blk, dtype),
+        _ptr(k_rot_ws, "k_rot_ws", blk, dtype), _ptr(sink_k_rot_ws, "sink_k_rot_ws", snk, dtype),
+        skn, svn, _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta,
+        scale, ws_p, ws_n, _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, flags, timing_events,
+        _stream()), "la_denoise_step")
 
 
 def la_denoise_chain(stages, block_id: int, q_rot_ws, k_rot_ws, sink_k_rot_ws, rope_table,
                      Hl: int, Wl: int, x=None, frames_per_block: int = 3, sink_delta: int = -1,
-                     theta: float = 10000.0, scale: Optional[float] = None) -> None:
+                     theta: float = 10000.0, *, scale: float,
+                     attn_ws: Optional[AttnWorkspace] = None) -> None:
     """stages: list of dicts, one per stage in order, with keys rings (a KVRingStack's
     .states array), q_raw, k_raw, v_raw, attn_out (lists of per-layer tensors), vel
     (tensor like x, or None when x is None), dt, and optionally sink_k_new,
-    sink_v_new (lists, block 1)."""
+    sink_v_new (lists, block 1).  scale: the softmax scale."""
+    torch = _torch()
     n_layers = len(stages[0]["rings"])
+    r0 = stages[0]["rings"][0]
+    dtype = _step_dtype(r0)
+    blk = (r0.block_tokens, r0.heads, r0.head_dim)
+    snk = (r0.sink_tokens, r0.heads, r0.head_dim)
+    if x is not None and x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    _check_table(rope_table, Hl, Wl, r0.head_dim)
+    for t, name, shp in ((q_rot_ws, "q_rot_ws", blk), (k_rot_ws, "k_rot_ws", blk),
+                         (sink_k_rot_ws, "sink_k_rot_ws", snk)):
+        _check_tensor(t, name, shp, dtype)
+    for i, g in enumerate(stages):  # every shape and dtype first, then the pointers
+        for key in ("q_raw", "k_raw", "v_raw", "attn_out"):
+            _check_list(g[key], f"stages[{i}].{key}", blk, dtype, n_layers)
+        for key in ("sink_k_new", "sink_v_new"):
+            if g.get(key) is not None:
+                _check_list(g[key], f"stages[{i}].{key}", snk, dtype, n_layers)
     arr = (la_stage * len(stages))()
     keep = []  # pointer arrays must outlive the call
     for i, g in enumerate(stages):
         if len(g["rings"]) != n_layers:
             raise ValueError("every stage needs the same number of layers")
+        if _step_dtype(g["rings"][0]) != dtype:
+            raise ValueError("every stage needs rings of the same dtype")
         st = arr[i]
         st.rings = ctypes.cast(g["rings"], ctypes.POINTER(la_kvring))
         for key in ("q_raw", "k_raw", "v_raw", "attn_out"):
-            a = _ptr_array(g[key], f"stages[{i}].{key}")
+            a = _ptr_array(g[key], f"stages[{i}].{key}", blk, dtype, n_layers)
             keep.append(a)
             setattr(st, key, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
         for key in ("sink_k_new", "sink_v_new"):
             if g.get(key) is not None:
-                a = _ptr_array(g[key], f"stages[{i}].{key}")
+                a = _ptr_array(g[key], f"stages[{i}].{key}", snk, dtype, n_layers)
                 keep.append(a)
                 setattr(st, key, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
         if x is not None:
-            if g.get("vel") is None or g["vel"].numel() != x.numel():
-                raise ValueError(f"stages[{i}].vel must match x")
-            st.vel = _ptr(g["vel"], f"stages[{i}].vel").value
+            v = g.get("vel")
+            if v is None or v.numel() != x.numel() or v.dtype != torch.float32:
+                raise ValueError(f"stages[{i}].vel must be float32 like x")
+            st.vel = _ptr(v, f"stages[{i}].vel").value
         st.dt = float(g["dt"])
-    if scale is None:
-        scale = stages[0]["rings"][0].head_dim ** -0.5
     n_lat = 0 if x is None else x.numel()
+    ws_p, ws_n = _ws(attn_ws)
     _check(_load().la_denoise_chain(
-        arr, len(stages), n_layers, block_id, _ptr(q_rot_ws, "q_rot_ws"), _ptr(k_rot_ws, "k_rot_ws"),
-        _ptr(sink_k_rot_ws, "sink_k_rot_ws"), _ptr(rope_table, "rope_table"), Hl, Wl,
-        frames_per_block, sink_delta, theta, scale, _ptr(x, "x"), n_lat, _stream()),
-        "la_denoise_chain")
+        arr, len(stages), n_layers, block_id, _ptr(q_rot_ws, "q_rot_ws", blk, dtype),
+        _ptr(k_rot_ws, "k_rot_ws", blk, dtype), _ptr(sink_k_rot_ws, "sink_k_rot_ws", snk, dtype),
+        _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta, scale,
+        ws_p, ws_n, _ptr(x, "x"), n_lat, _stream()), "la_denoise_chain")
 
 
 # ---------------------------------------------------------------- one layer's cache
@@ -418,7 +525,11 @@ class KVRing:
         """dtype: torch.bfloat16, torch.float32, or torch.uint8 for e4m3 slots (the
         sink of an e4m3 ring is bf16)."""
         torch = _torch()
-        code = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.uint8: LA_FP8_E4M3}[dtype]
+        codes = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.uint8: LA_FP8_E4M3}
+        if dtype not in codes:
+            raise TypeError(f"unsupported ring dtype {dtype} (bfloat16, float32, or uint8 "
+                            "for e4m3 slots)")
+        code = codes[dtype]
         sink_dtype = torch.bfloat16 if code == LA_FP8_E4M3 else dtype
         self.k_slots = torch.empty((W, block_tokens, heads, head_dim), dtype=dtype, device=device)
         self.v_slots = torch.empty_like(self.k_slots)
@@ -444,14 +555,19 @@ class KVRingStack:
     def __init__(self, n_layers: int, W: int, block_tokens: int, sink_tokens: int, heads: int,
                  head_dim: int, dtype, noise_level: float, device="cuda"):
         torch = _torch()
+        codes = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.uint8: LA_FP8_E4M3}
+        if dtype not in codes:
+            raise TypeError(f"unsupported ring dtype {dtype} (bfloat16, float32, or uint8 "
+                            "for e4m3 slots)")
+        code = codes[dtype]
+        sink_dtype = torch.bfloat16 if code == LA_FP8_E4M3 else dtype
         self.k_slots = torch.empty((n_layers, W, block_tokens, heads, head_dim), dtype=dtype,
                                    device=device)
         self.v_slots = torch.empty_like(self.k_slots)
-        self.sink_k_raw = torch.empty((n_layers, sink_tokens, heads, head_dim), dtype=dtype,
+        self.sink_k_raw = torch.empty((n_layers, sink_tokens, heads, head_dim), dtype=sink_dtype,
                                       device=device)
         self.sink_v = torch.empty_like(self.sink_k_raw)
         self.states = (la_kvring * n_layers)()
-        code = LA_BF16 if dtype == torch.bfloat16 else LA_F32
         for l in range(n_layers):
             la_kvring_init(self.states[l], self.k_slots[l], self.v_slots[l], self.sink_k_raw[l],
                            self.sink_v[l], W, block_tokens, sink_tokens, heads, head_dim, code,

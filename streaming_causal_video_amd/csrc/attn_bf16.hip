@@ -15,8 +15,8 @@
 //  * Products on v_mfma_f32_16x16x32_bf16: every K or V^T fragment read from
 //    LDS feeds three MFMAs (one per query tile), 48 flops per LDS byte; the
 //    LDS operand traffic, not the matrix core, bounded the earlier 32-row
-//    waves on 32x32x16 MFMAs.  At 4680 rows a head takes 25 workgroups
-//    (2.5 % padding), and 40 heads fill 512 CU slots in two rounds.
+//    waves on 32x32x16 MFMAs.  At 4680 rows a head takes 25 query tiles
+//    (2.5 % padding).
 //  * Scores are computed transposed, S^T = K Q^T: in each 16x16 result a lane
 //    holds one query (lane % 16) and four keys; the row max needs two lane
 //    swaps (v_permlane32_swap, v_permlane16_swap).
@@ -28,16 +28,22 @@
 //  * Each 64-key tile is processed as two 32-key halves (scores, softmax,
 //    P V): 24 score and 24 output registers per half instead of 48, which
 //    keeps the kernel within the 256 registers of two waves per SIMD.
-//  * Online softmax in float32 with the scale folded into a base-2 exponent
-//    (one FMA and one v_exp_f32 per score).  Probabilities are taken against
-//    the running reference max without a per-tile max; only when a query's
-//    sum over the half leaves [0, 2^64] (always on the first tile, whose
-//    reference starts at -1e30) is the reference raised to the half's max, O
-//    and the row sum rescaled and the half's probabilities recomputed.  Exact:
-//    numerator and denominator use the same reference, and P <= 2^64 keeps
-//    the float32 accumulators far from overflow.  P is rounded to bf16 for
-//    the second product (v_cvt_pk_bf16_f32) and the row sum is taken from
-//    those same bf16 pairs with v_dot2c_f32_bf16.
+//  * Softmax in base 2 with the score scale folded into Q: the kernel takes Q
+//    already multiplied by c = scale * log2(e) (the RoPE kernel of the step
+//    emits it that way, rounded to bf16 once; a caller's plain Q is multiplied
+//    and rounded here when its Q fragments are loaded), and the running
+//    reference m of each query enters the first score MFMA of a half as its C
+//    operand, so the accumulators leave the matrix core as c s - m and the
+//    probability of each score is a single v_exp_f32.  Probabilities are taken
+//    against the running reference without a per-tile max; only when a
+//    query's sum over the half leaves [0, 2^64] (and always on the first half
+//    of a piece) is the reference raised by the half's excess, the scores
+//    moved down by it, O and the row sum rescaled and the half's
+//    probabilities recomputed.  Exact: numerator and denominator use the same
+//    reference, and P <= 2^64 keeps the float32 accumulators far from
+//    overflow.  P is rounded to bf16 for the second product
+//    (v_cvt_pk_bf16_f32) and the row sum is taken from those same bf16 pairs
+//    with v_dot2c_f32_bf16.
 //  * K tiles go global -> LDS by DMA (buffer_load ... lds): no staging
 //    registers, issued one tile ahead right after the barrier, so a whole
 //    tile of compute hides their latency.  A DMA writes each wave's 1 KB
@@ -59,9 +65,24 @@
 //    per-thread 32-bit offsets computed once; the current segment's key range
 //    and base pointers stay in scalar registers (the segment table in kernel
 //    arguments is read only when a tile enters the next segment).
-//  * Workgroups are renumbered so that all query tiles of a head run on the
-//    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 while
-//    they stream the head's K/V.
+//  * Schedule.  A unit of work is (head, 192-query tile) over all ntiles
+//    64-key tiles.  Without a workspace the grid has one workgroup per unit.
+//    With one, the grid is persistent with P slots (two workgroups per CU):
+//    slot s runs units s, P + s, ... for the R = U / P full rounds, and the
+//    U' = U mod P units of the last round, when they would leave more than
+//    half of the slots idle, are cut into m = P / U' equal key ranges run by
+//    U' m slots (piece-major, so concurrent slots read the same key tiles of a
+//    head, as whole rounds do).  Cutting units at arbitrary key offsets to
+//    balance the slots exactly was measured 30 % slower at 1000 units: the
+//    concurrent slices then stream a head's K/V at scattered offsets and L2
+//    reuse is lost.  Each piece of a cut unit stores its unnormalised (O, m,
+//    l) per row in the workspace; the piece that arrives last (a per-unit
+//    counter) merges the pieces in piece order (so the result does not depend
+//    on arrival order), writes the output and resets the counter to zero.
+//    Nothing waits on another workgroup.
+//  * Workgroups are renumbered so that consecutive slots (and so the query
+//    tiles of one head) run on the same XCD (dispatch is round-robin over the
+//    8 XCDs) and share its L2 while they stream the head's K/V.
 #include "la_internal.h"
 
 namespace la {
@@ -115,12 +136,19 @@ __device__ __forceinline__ int key_of_krow(int r) {
   return (r & 32) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
 
+// Partial record of one piece (floats): per wave, O as f32x4 per (d-tile, query
+// tile, lane), then m and the row sum l per (query tile, lane).
+constexpr int kRecO = 8 * NQT * 64 * 4;
+constexpr int kRecWave = kRecO + 2 * NQT * 64;
+static_assert(NWAVES * kRecWave == kAttnRecFloats, "partial record size");
+
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                  float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
-                 float c2, int qtiles, int nwg) {
+                 float qmul, int qtiles, int nwg, AttnWork wk) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ int s_arrival;
 
   // XCD-aware renumbering: consecutive logical ids on one XCD.
   const int pid = __builtin_amdgcn_workgroup_id_x();
@@ -128,8 +156,6 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const int tall = (nwg % 8) == 0 ? 8 : (nwg % 8);
   const int xcd = pid % 8, loc = pid / 8;
   const int lin = xcd < tall ? xcd * per + loc : tall * per + (xcd - tall) * (per - 1) + loc;
-  const int head = lin / qtiles;
-  const int qt = lin - head * qtiles;
 
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
@@ -137,45 +163,13 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const int c = lane & 15;  // query (scores) / row (operands) within a 16-tile
   const int g = lane >> 4;  // 8-element k-group of the operands
   const int64_t rs = (int64_t)heads * D;
-  const int qbase = qt * BM + wave * QW;
-
-  // Q^T B-operand fragments: lane holds Q[query qbase + 16 nt + c][32 s + 8 g .. +7].
-  bf16x8_t qf[NQT][4];
-#pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    const int qrow = qbase + 16 * nt + c;
-    if (qrow < nq) {
-      const uint16_t* qp = q + qrow * rs + head * D + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qf[nt][s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qf[nt][s] = bf16x8_t{};
-    }
-  }
-
-  f32x4_t o[8][NQT];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) o[dt][nt] = f32x4_t{};
-  // Reference max (scale*log2(e) units) and this lane's row sum.  The reference
-  // starts finite, so the first tile's probabilities overflow to +inf (never
-  // NaN, even where masked keys hold -inf) and trigger the first raise.
-  float m_run[NQT], l_run[NQT];
-#pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    m_run[nt] = -1e30f;
-    l_run[nt] = 0.f;
-  }
-
-  // Loader geometry.  K DMA: wave w fills LDS rows 16 w + 4 i + t (t = lane
-  // >> 4, i = 0..3), lane slot p = lane & 15 of a row receiving chunk
-  // p ^ (row & 15) of key 32 (w >> 1) + 4 (w & 1) + 8 i + t.
-  const int t4 = lane >> 4;
   const int ntiles = (nk + BN - 1) / BN;
+
+  // Loader geometry (the same for every piece).  K DMA: wave w fills LDS rows
+  // 16 w + 4 i + t (t = lane >> 4, i = 0..3), lane slot p = lane & 15 of a row
+  // receiving chunk p ^ (row & 15) of key 32 (w >> 1) + 4 (w & 1) + 8 i + t.
+  const int t4 = lane >> 4;
   const uint32_t rs_bytes = (uint32_t)rs * 2u;
-  const uint32_t hoff = (uint32_t)(head * D * 2);
   const uint32_t kkey0 = (uint32_t)(32 * (wave >> 1) + 4 * (wave & 1) + t4);
   uint32_t kdoff[4];
 #pragma unroll
@@ -191,232 +185,393 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const uint32_t vlane = (uint32_t)((8 * g + (c >> 2)) * 2 * VP + 16 * ((c >> 1) & 1) +
                                     16 * (2 * (c >> 2) + 8 * (g & 1)) + 8 * (c & 1));
 
-  // Segment of the tile being loaded, kept in scalar registers: the segment
-  // table is read only when a tile crosses into the next segment.
-  int seg = 0, seg_start = 0, seg_end = segs.end[0];
-  const char* seg_k = static_cast<const char*>(segs.k[0]);
-  const char* seg_v = static_cast<const char*>(segs.v[0]);
-  bool whole = true;             // tile inside one segment
-  uint32_t sbase = 0, nbytes = 0;  // tile's byte offset in the segment, bytes left from there
-
-  auto locate = [&](int tile) __attribute__((always_inline)) {
-    const int t0 = tile * BN;
-    while (t0 >= seg_end) {
-      ++seg;
-      seg_start = seg_end;
-      seg_end = segs.end[seg];
-      seg_k = static_cast<const char*>(segs.k[seg]);
-      seg_v = static_cast<const char*>(segs.v[seg]);
-    }
-    whole = t0 + BN <= seg_end;
-    sbase = (uint32_t)(t0 - seg_start) * rs_bytes + hoff;
-    nbytes = (uint32_t)(seg_end - t0) * rs_bytes - hoff;
-  };
-  // one 16-byte chunk of tile row r; rows past the last key are clamped to it
-  // (their scores are masked)
-  auto row_load = [&](int t0, int r, int chunk, bool is_v) __attribute__((always_inline)) -> uint4 {
-    const int key = min(t0 + r, nk - 1);
-    int s = seg;
-    while (key >= segs.end[s]) ++s;
-    const int st = s ? segs.end[s - 1] : 0;
-    const int64_t o = (int64_t)(key - st) * rs + head * D + chunk * 8;
-    const uint16_t* base = static_cast<const uint16_t*>(is_v ? segs.v[s] : segs.k[s]);
-    return *reinterpret_cast<const uint4*>(base + o);
-  };
-  auto kload = [&](int tile, int buf) __attribute__((always_inline)) {
-    uint16_t* kb = lds + buf * STAGE;
-    if (whole) {
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            kr, (__attribute__((address_space(3))) void*)(kb + (16 * wave + 4 * i) * KP), 16,
-            kdoff[i], 8 * i * rs_bytes, 0, 0);
-    } else {
-      const int t0 = tile * BN;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * i + t4;
-        const uint4 x = row_load(t0, key_of_krow(r), (lane & 15) ^ (r & 15), false);
-        *reinterpret_cast<uint4*>(kb + r * KP + (lane & 15) * 8) = x;
-      }
-    }
-  };
-  auto vload = [&](int tile, int buf) __attribute__((always_inline)) {
-    uint16_t* vb = lds + buf * STAGE + KBUF;
-    if (whole) {
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            vr, (__attribute__((address_space(3))) void*)(vb + (16 * wave + 4 * i) * VP), 16,
-            vdoff[i >> 1], 4 * i * rs_bytes, 0, 0);
-    } else {
-      const int t0 = tile * BN;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * i + t4;
-        const int sw = 2 * (r & 3) + 8 * ((r >> 3) & 1);
-        const uint4 x = row_load(t0, r, (lane & 15) ^ sw, true);
-        *reinterpret_cast<uint4*>(vb + r * VP + (lane & 15) * 8) = x;
-      }
-    }
-  };
-
   typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
   const bf16x2v_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  locate(0);
-  kload(0, 0);
-  vload(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile 0's K DMA has landed
-  // One 64-key tile j computed from LDS buffer `cur` while tile j + 1 is staged
-  // into buffer 1 - cur.  The loop below runs two tiles per trip so that both
-  // buffers are compile-time constants (LDS addresses become immediates).
-  auto tile = [&](const int j, const int cur) __attribute__((always_inline)) {
-    __syncthreads();
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      locate(j + 1);
-      kload(j + 1, 1 - cur);
+  // This slot's pieces: whole units lin, lin + P, ... for the full rounds, then at
+  // most one piece of a unit of the last round (cut into wk.cuts key ranges).
+  const int units = qtiles * heads;
+  const int P = nwg;
+  const int rounds = units / P;
+  const int urem = units - rounds * P;
+  const int cuts = wk.cuts;
+  const int npieces = rounds + (lin < urem * cuts ? 1 : 0);
+
+  for (int it = 0; it < npieces; ++it) {
+    int unit = it * P + lin, kt0 = 0, kt1 = ntiles, cut = 0;
+    if (it == rounds) {
+      cut = lin / urem;  // piece-major: concurrent slots share key ranges
+      unit = rounds * P + (lin - cut * urem);
+      const int len = ntiles / cuts;
+      kt0 = cut * len;
+      kt1 = cut == cuts - 1 ? ntiles : kt0 + len;
     }
-    const uint16_t* kb = lds + cur * STAGE;
-    // K fragment: row 16 blk + c, chunk 4 s + g, stored at chunk (4 s + g) ^ c
-    const uint16_t* kr = kb + c * KP;
-    // V operand by transposing reads (B = 0, 1 for keys + 0..3, + 4..7): this lane
-    // addresses key 32 h + 8 g + (c >> 2) + 4 B, dims 16 dt + 4 (c & 3) .. +3, which
-    // sits in LDS row 32 h + 16 (g >> 1) + 8 B + 4 (g & 1) + (c >> 2)
-    const char* vt = reinterpret_cast<const char*>(kb + KBUF);
+    const int head = unit / qtiles;
+    const int qt = unit - head * qtiles;
+    const uint32_t hoff = (uint32_t)(head * D * 2);
+    const int qbase = qt * BM + wave * QW;
+
+    // Q^T B-operand fragments: lane holds Q[query qbase + 16 nt + c][32 s + 8 g .. +7],
+    // multiplied by qmul (when it is not 1) and rounded to bf16.
+    bf16x8_t qf[NQT][4];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      const int qrow = qbase + 16 * nt + c;
+      if (qrow < nq) {
+        const uint16_t* qp = q + qrow * rs + head * D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[nt][s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[nt][s] = bf16x8_t{};
+      }
+    }
+    if (qmul != 1.0f) {
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8_t v = qf[nt][s];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * qmul);
+          qf[nt][s] = v;
+        }
+    }
+
+    f32x4_t o[8][NQT];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) o[dt][nt] = f32x4_t{};
+    // cm[nt] = -m in all four elements, m = the query's reference (base-2 units): the
+    // C operand of the first score MFMA of a half.  This lane's row sum in l_run.
+    f32x4_t cm[NQT];
+    float l_run[NQT];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      cm[nt] = f32x4_t{};
+      l_run[nt] = 0.f;
+    }
+
+    // Segment of the tile being loaded, kept in scalar registers: the segment
+    // table is read only when a tile crosses into the next segment.
+    int seg = 0, seg_start = 0, seg_end = segs.end[0];
+    const char* seg_k = static_cast<const char*>(segs.k[0]);
+    const char* seg_v = static_cast<const char*>(segs.v[0]);
+    bool whole = true;               // tile inside one segment
+    uint32_t sbase = 0, nbytes = 0;  // tile's byte offset in the segment, bytes left from there
+
+    auto locate = [&](int tile) __attribute__((always_inline)) {
+      const int t0 = tile * BN;
+      while (t0 >= seg_end) {
+        ++seg;
+        seg_start = seg_end;
+        seg_end = segs.end[seg];
+        seg_k = static_cast<const char*>(segs.k[seg]);
+        seg_v = static_cast<const char*>(segs.v[seg]);
+      }
+      whole = t0 + BN <= seg_end;
+      sbase = (uint32_t)(t0 - seg_start) * rs_bytes + hoff;
+      nbytes = (uint32_t)(seg_end - t0) * rs_bytes - hoff;
+    };
+    // one 16-byte chunk of tile row r; rows past the last key are clamped to it
+    // (their scores are masked)
+    auto row_load = [&](int t0, int r, int chunk, bool is_v) __attribute__((always_inline)) -> uint4 {
+      const int key = min(t0 + r, nk - 1);
+      int s = seg;
+      while (key >= segs.end[s]) ++s;
+      const int st = s ? segs.end[s - 1] : 0;
+      const int64_t off = (int64_t)(key - st) * rs + head * D + chunk * 8;
+      const uint16_t* base = static_cast<const uint16_t*>(is_v ? segs.v[s] : segs.k[s]);
+      return *reinterpret_cast<const uint4*>(base + off);
+    };
+    auto kload = [&](int tile, int buf) __attribute__((always_inline)) {
+      uint16_t* kb = lds + buf * STAGE;
+      if (whole) {
+        const __amdgpu_buffer_rsrc_t kr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              kr, (__attribute__((address_space(3))) void*)(kb + (16 * wave + 4 * i) * KP), 16,
+              kdoff[i], 8 * i * rs_bytes, 0, 0);
+      } else {
+        const int t0 = tile * BN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * wave + 4 * i + t4;
+          const uint4 v = row_load(t0, key_of_krow(r), (lane & 15) ^ (r & 15), false);
+          *reinterpret_cast<uint4*>(kb + r * KP + (lane & 15) * 8) = v;
+        }
+      }
+    };
+    auto vload = [&](int tile, int buf) __attribute__((always_inline)) {
+      uint16_t* vb = lds + buf * STAGE + KBUF;
+      if (whole) {
+        const __amdgpu_buffer_rsrc_t vr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              vr, (__attribute__((address_space(3))) void*)(vb + (16 * wave + 4 * i) * VP), 16,
+              vdoff[i >> 1], 4 * i * rs_bytes, 0, 0);
+      } else {
+        const int t0 = tile * BN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * wave + 4 * i + t4;
+          const int sw = 2 * (r & 3) + 8 * ((r >> 3) & 1);
+          const uint4 v = row_load(t0, r, (lane & 15) ^ sw, true);
+          *reinterpret_cast<uint4*>(vb + r * VP + (lane & 15) * 8) = v;
+        }
+      }
+    };
+
+    __syncthreads();  // the previous piece's last tile is done with both LDS buffers
+    locate(kt0);
+    kload(kt0, 0);
+    vload(kt0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the first tile's K DMA has landed
+    // One 64-key tile j computed from LDS buffer `cur` while tile j + 1 is staged
+    // into buffer 1 - cur.  The loop below runs two tiles per trip so that both
+    // buffers are compile-time constants (LDS addresses become immediates).
+    auto tile = [&](const int j, const int cur) __attribute__((always_inline)) {
+      __syncthreads();
+      const bool more = j + 1 < kt1;
+      if (more) {
+        locate(j + 1);
+        kload(j + 1, 1 - cur);
+      }
+      const uint16_t* kb = lds + cur * STAGE;
+      // K fragment: row 16 blk + c, chunk 4 s + g, stored at chunk (4 s + g) ^ c
+      const uint16_t* kr = kb + c * KP;
+      // V operand by transposing reads (B = 0, 1 for keys + 0..3, + 4..7): this lane
+      // addresses key 32 h + 8 g + (c >> 2) + 4 B, dims 16 dt + 4 (c & 3) .. +3, which
+      // sits in LDS row 32 h + 16 (g >> 1) + 8 B + 4 (g & 1) + (c >> 2)
+      const char* vt = reinterpret_cast<const char*>(kb + KBUF);
 
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // S^T[key][query] for keys 32 h .. 32 h + 31: row blocks 2 h and 2 h + 1.
-      f32x4_t st[2][NQT];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) st[b][nt] = f32x4_t{};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              kr + 16 * (2 * h + b) * KP + (((4 * s + g) ^ c) * 8));
-#pragma unroll
-          for (int nt = 0; nt < NQT; ++nt)
-            st[b][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[b][nt], 0, 0, 0);
-        }
-      if (h == 0 && more) vload(j + 1, 1 - cur);
-      if ((j + 1) * BN > nk) {
-        // last tile: row 4 g + i of block 2 h + b holds key 32 h + 8 g + 4 b + i
+      for (int h = 0; h < 2; ++h) {
+        // S^T[key][query] - m for keys 32 h .. 32 h + 31: row blocks 2 h and 2 h + 1.
+        f32x4_t st[2][NQT];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (j * BN + 32 * h + 8 * g + 4 * b + i >= nk) {
+          for (int nt = 0; nt < NQT; ++nt) st[b][nt] = cm[nt];
 #pragma unroll
-              for (int nt = 0; nt < NQT; ++nt) st[b][nt][i] = -INFINITY;
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+                kr + 16 * (2 * h + b) * KP + (((4 * s + g) ^ c) * 8));
+#pragma unroll
+            for (int nt = 0; nt < NQT; ++nt)
+              st[b][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[b][nt], 0, 0, 0);
+          }
+        if (h == 0 && more) vload(j + 1, 1 - cur);
+        if ((j + 1) * BN > nk) {
+          // last tile: row 4 g + i of block 2 h + b holds key 32 h + 8 g + 4 b + i
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (j * BN + 32 * h + 8 * g + 4 * b + i >= nk) {
+#pragma unroll
+                for (int nt = 0; nt < NQT; ++nt) st[b][nt][i] = -INFINITY;
+              }
+            }
+        }
+
+        // P^T fragment of query tile nt: keys 32 h + 8 g .. +7, i.e. rows
+        // 4 g .. 4 g + 3 of both row blocks; tsum = this lane's sum of them.
+        bf16x8_t pf[NQT];
+        float tsum[NQT];
+        auto probs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) {
+            uint32_t w[4];
+            float ts = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = __builtin_amdgcn_exp2f(st[e >> 1][nt][2 * (e & 1)]);
+              const float p1 = __builtin_amdgcn_exp2f(st[e >> 1][nt][2 * (e & 1) + 1]);
+              w[e] = pack_bf16(p0, p1);
+              ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[e]), ones, ts,
+                                                   false);
+            }
+            tsum[nt] = ts;
+            pf[nt] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+          }
+        };
+        probs();
+        // The first half of a piece always sets the reference (it starts at 0, not at
+        // a key's score).
+        const bool first = h == 0 && j == kt0;
+        bool over = first;
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt)  // on the bits (sums are >= +0): also inf and any NaN,
+          over |= __float_as_uint(tsum[nt]) > kSumLimitBits;  // whatever the NaN flags
+        if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) {
+            // a = max over the half of c s - m: the reference becomes m + a on the first
+            // half of a piece and m + max(a, 0) afterwards; the scores move down by as much
+            const float a =
+                fmaxf(fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3])),
+                      fmaxf(fmaxf(st[1][nt][0], st[1][nt][1]), fmaxf(st[1][nt][2], st[1][nt][3])));
+            const float am = max4_lanes(a);
+            const float delta = first ? am : fmaxf(am, 0.f);
+            const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-delta);
+            cm[nt] -= delta;
+            st[0][nt] -= delta;
+            st[1][nt] -= delta;
+            l_run[nt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
+          }
+          probs();
+        }
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) l_run[nt] += tsum[nt];
+
+        // O^T[d][query] += V^T P^T: A operand = V^T[16 dt + c][32 h + 8 g .. +7]
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const char* va = vt + (vlane ^ (32 * dt)) + 64 * h * VP;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 4 * 2 * VP));
+          const bf16x8_t a =
+              __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt)
+            o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nt], o[dt][nt], 0, 0, 0);
+        }
+      }
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's K DMA has landed
+      }
+    };
+    for (int j = kt0; j < kt1; j += 2) {
+      tile(j, 0);
+      if (j + 1 < kt1) tile(j + 1, 1);
+    }
+
+    // Row totals; m of each row.
+    float lt[NQT], mr[NQT];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      lt[nt] = sum4_lanes(l_run[nt]);
+      mr[nt] = -cm[nt][0];
+    }
+    bool emit = true;
+    if (kt0 != 0 || kt1 != ntiles) {
+      // A piece of a cut unit: record (unit of the last round, piece) of the workspace.
+      const int rec0 = (unit - rounds * P) * cuts;
+      auto record = [&](int piece) -> float* {
+        return wk.partials + (int64_t)(rec0 + piece) * kAttnRecFloats + wave * kRecWave;
+      };
+      {
+        float* rec = record(cut);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt)
+            *reinterpret_cast<f32x4_t*>(rec + ((dt * NQT + nt) * 64 + lane) * 4) = o[dt][nt];
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          rec[kRecO + nt * 64 + lane] = mr[nt];
+          rec[kRecO + (NQT + nt) * 64 + lane] = lt[nt];
+        }
+      }
+      __threadfence();  // this piece's record is visible before its arrival is counted
+      __syncthreads();
+      if (tid == 0) s_arrival = atomicAdd(&wk.counters[unit], 1);
+      __syncthreads();
+      emit = s_arrival == cuts - 1;
+      if (emit) {
+        // Last piece to arrive: merge every piece's record (this one's included) in
+        // piece order, so the result is the same whichever piece arrives last.
+        __threadfence();
+        if (tid == 0) wk.counters[unit] = 0;
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) mr[nt] = -INFINITY;
+        for (int i = 0; i < cuts; ++i) {
+          const float* rec = record(i);
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) mr[nt] = fmaxf(mr[nt], rec[kRecO + nt * 64 + lane]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          lt[nt] = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[dt][nt] = f32x4_t{};
+        }
+        for (int i = 0; i < cuts; ++i) {
+          const float* rec = record(i);
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) {
+            const float f = __builtin_amdgcn_exp2f(rec[kRecO + nt * 64 + lane] - mr[nt]);
+            lt[nt] = fmaf(rec[kRecO + (NQT + nt) * 64 + lane], f, lt[nt]);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+              const f32x4_t v =
+                  *reinterpret_cast<const f32x4_t*>(rec + ((dt * NQT + nt) * 64 + lane) * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[dt][nt][e] = fmaf(v[e], f, o[dt][nt][e]);
             }
           }
+        }
       }
-
-      // P^T fragment of query tile nt: keys 32 h + 8 g .. +7, i.e. rows
-      // 4 g .. 4 g + 3 of both row blocks; tsum = this lane's sum of them.
-      bf16x8_t pf[NQT];
-      float tsum[NQT];
-      auto probs = [&]() __attribute__((always_inline)) {
+    }
+    if (emit) {
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-          const float nm = -m_run[nt];
-          uint32_t w[4];
-          float ts = 0.f;
+      for (int nt = 0; nt < NQT; ++nt) {
+        const int qrow = qbase + 16 * nt + c;
+        if (qrow < nq) {
+          const float inv = 1.f / lt[nt];
+          uint16_t* op = out + qrow * rs + head * D + 4 * g;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(st[e >> 1][nt][2 * (e & 1)], c2, nm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(st[e >> 1][nt][2 * (e & 1) + 1], c2, nm));
-            w[e] = pack_bf16(p0, p1);
-            ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[e]), ones, ts,
-                                                 false);
+          for (int dt = 0; dt < 8; ++dt) {
+            const uint32_t w0 = pack_bf16(o[dt][nt][0] * inv, o[dt][nt][1] * inv);
+            const uint32_t w1 = pack_bf16(o[dt][nt][2] * inv, o[dt][nt][3] * inv);
+            *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(w0, w1);
           }
-          tsum[nt] = ts;
-          pf[nt] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+          if (lse != nullptr && g == 0)
+            lse[(int64_t)head * nq + qrow] = (mr[nt] + __log2f(lt[nt])) * 0.69314718055994531f;
         }
-      };
-      probs();
-      bool over = false;
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt)  // on the bits (sums are >= +0): also inf and any NaN,
-        over |= __float_as_uint(tsum[nt]) > kSumLimitBits;  // whatever the NaN flags
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-          const float a =
-              fmaxf(fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3])),
-                    fmaxf(fmaxf(st[1][nt][0], st[1][nt][1]), fmaxf(st[1][nt][2], st[1][nt][3])));
-          const float m_new = fmaxf(m_run[nt], max4_lanes(a) * c2);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-          m_run[nt] = m_new;
-          l_run[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
-        }
-        probs();
       }
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) l_run[nt] += tsum[nt];
-
-      // O^T[d][query] += V^T P^T: A operand = V^T[16 dt + c][32 h + 8 g .. +7]
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const char* va = vt + (vlane ^ (32 * dt)) + 64 * h * VP;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(va + 4 * 2 * VP));
-        const bf16x8_t a =
-            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt)
-          o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nt], o[dt][nt], 0, 0, 0);
-      }
-    }
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's K DMA has landed
-    }
-  };
-  for (int j = 0; j < ntiles; j += 2) {
-    tile(j, 0);
-    if (j + 1 < ntiles) tile(j + 1, 1);
-  }
-
-#pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    const float lt = sum4_lanes(l_run[nt]);
-    const int qrow = qbase + 16 * nt + c;
-    if (qrow < nq) {
-      const float inv = 1.f / lt;
-      uint16_t* op = out + qrow * rs + head * D + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint32_t w0 = pack_bf16(o[dt][nt][0] * inv, o[dt][nt][1] * inv);
-        const uint32_t w1 = pack_bf16(o[dt][nt][2] * inv, o[dt][nt][3] * inv);
-        *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(w0, w1);
-      }
-      if (lse != nullptr && g == 0)
-        lse[(int64_t)head * nq + qrow] = (m_run[nt] + __log2f(lt)) * 0.69314718055994531f;
     }
   }
 }
 
 }  // namespace
 
+int attn_bf16_units(int nq, int heads) { return (nq + BM - 1) / BM * heads; }
+
 hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
-                            int nk, int heads, float scale, hipStream_t s) {
+                            int nk, int heads, float qmul, const AttnWorkspace& ws,
+                            hipStream_t s) {
   const int qtiles = (nq + BM - 1) / BM;
-  const float c2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
+  const int units = qtiles * heads;
+  const int ntiles = (nk + BN - 1) / BN;
+  AttnWork wk = {nullptr, nullptr, 1};
+  int nwg = units;  // one workgroup per unit
+  if (ws.counters != nullptr) {
+    // persistent slots; the last round is cut when it would leave over half idle
+    const int P = ws.slots;
+    const int urem = units % P;
+    int cuts = urem > 0 ? P / urem : 1;
+    if (cuts > ntiles) cuts = ntiles;
+    if (cuts >= 2) {
+      wk.counters = ws.counters;
+      wk.partials = ws.partials;
+      wk.cuts = cuts;
+      nwg = units < P ? urem * cuts : P;
+    }
+  }
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(nwg), dim3(NTHREADS), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
-                     nk, heads, c2, qtiles, qtiles * heads);
+                     nk, heads, qmul, qtiles, nwg, wk);
   return hipGetLastError();
 }
 

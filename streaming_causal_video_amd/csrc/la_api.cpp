@@ -41,11 +41,32 @@ void bands(int d, int* t, int* hw) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Compute units of the current device (cached per device); 0 if it cannot be read.
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+// Workspace layout of the bf16 attention: counters (one int32 per unit, padded to
+// 256 bytes), then one partial record per slot; slots = two per CU.
+size_t attn_counter_bytes(int n_q, int heads) {
+  return ((size_t)la::attn_bf16_units(n_q, heads) * 4 + 255) / 256 * 256;
+}
+size_t attn_ws_bytes(int n_q, int heads, int slots) {
+  return attn_counter_bytes(n_q, heads) + (size_t)slots * la::kAttnRecFloats * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.4 (gfx950) attn-v9 fp8-v6"; }
+const char* la_version(void) { return "liblahip 0.5 (gfx950) attn-v10 fp8-v6"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -125,9 +146,10 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
                             int32_t n_frames, int64_t f0, const void* sink_k_in,
                             void* sink_k_out, int64_t sink_delta, const void* dev_table,
                             int32_t Hl, int32_t Wl, int32_t heads, int32_t head_dim,
-                            la_dtype dtype, double theta, la_stream_t stream) {
+                            la_dtype dtype, double theta, float q_scale, la_stream_t stream) {
   if (!valid_dtype(dtype)) return LA_ERR_DTYPE;
   if (!dev_table || !(theta > 1.0)) return LA_ERR_INVALID_ARG;
+  if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
   if ((!q_in) != (!q_out) || (!k_in) != (!k_out) || (!sink_k_in) != (!sink_k_out))
     return LA_ERR_INVALID_ARG;
   if (n_frames < 1 || n_frames > LA_MAX_BLOCK_FRAMES || Hl < 1 || Wl < 1 || heads < 1 ||
@@ -164,19 +186,29 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
   g.hpairs = hw / 2;
   g.wpairs = hw / 2;
   la::RopeTensor t[3] = {
-      {q_in, q_out, (int32_t)(hwtok * n_frames), 0},
-      {k_in, k_out, (int32_t)(hwtok * n_frames), 0},
-      {sink_k_in, sink_k_out, (int32_t)hwtok, n_frames},
+      {q_in, q_out, (int32_t)(hwtok * n_frames), 0, q_scale},
+      {k_in, k_out, (int32_t)(hwtok * n_frames), 0, 1.0f},
+      {sink_k_in, sink_k_out, (int32_t)hwtok, n_frames, 1.0f},
   };
   return hip_status(la::launch_rope(t, 3, g, tc, static_cast<const float*>(dev_table), dtype,
                                     static_cast<hipStream_t>(stream)));
 }
 
+size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads) {
+  if (n_q < 1 || heads < 1) return 0;
+  const int cus = device_cus();
+  if (cus < 1) return 0;
+  return attn_ws_bytes(n_q, heads, 2 * cus);
+}
+
 la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot,
                             const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
-                            float* lse_or_null, float scale, la_stream_t stream) {
+                            float* lse_or_null, float scale, float q_scale, void* workspace,
+                            size_t workspace_bytes, la_stream_t stream) {
   if (!r || !q_rot || !sink_k_rot || !k_cur_rot || !v_cur || !out) return LA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return LA_ERR_INVALID_ARG;
+  if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
+  if (workspace && ((uintptr_t)workspace % 256)) return LA_ERR_INVALID_ARG;
   if (!valid_dtype(r->dtype)) return LA_ERR_DTYPE;
   if (n_q != r->block_tokens || n_q < 1) return LA_ERR_SHAPE;
   if (r->dtype == LA_BF16 && r->head_dim != 128) return LA_ERR_SHAPE;
@@ -219,11 +251,25 @@ la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* s
   segs.nseg = n;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (r->dtype == LA_BF16)
-    e = la::launch_attn_bf16(q_rot, out, lse_or_null, segs, n_q, end, r->heads, scale, s);
-  else
+  if (r->dtype == LA_BF16) {
+    // base-2 scores: Q times scale * log2(e) / q_scale, rounded to bf16 in the kernel
+    // unless that factor is 1 in float32 (Q already scaled by the caller)
+    const float qmul = (float)((double)scale * 1.4426950408889634 / (double)q_scale);
+    la::AttnWorkspace ws = {nullptr, nullptr, 0};
+    if (workspace) {
+      const int cus = device_cus();
+      if (cus < 1) return LA_ERR_HIP;
+      if (workspace_bytes < attn_ws_bytes(n_q, r->heads, 2 * cus)) return LA_ERR_SHAPE;
+      ws.counters = static_cast<int32_t*>(workspace);
+      ws.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             attn_counter_bytes(n_q, r->heads));
+      ws.slots = 2 * cus;
+    }
+    e = la::launch_attn_bf16(q_rot, out, lse_or_null, segs, n_q, end, r->heads, qmul, ws, s);
+  } else {
     e = la::launch_attn_f32(q_rot, out, lse_or_null, segs, n_q, end, r->heads, r->head_dim,
-                            scale, s);
+                            scale / q_scale, s);
+  }
   return hip_status(e);
 }
 
@@ -342,6 +388,17 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
 
 namespace {
 
+// The step's scale and attention workspace (NULL, or 256-byte aligned and at least
+// la_attn_workspace_bytes for the ring's geometry).
+la_status validate_attn_ws(const la_kvring& r0, float scale, const void* ws, size_t bytes) {
+  if (!(scale > 0.f) || !isfinite(scale)) return LA_ERR_INVALID_ARG;
+  if (!ws) return LA_OK;
+  if ((uintptr_t)ws % 256) return LA_ERR_INVALID_ARG;
+  if (r0.dtype == LA_BF16 && bytes < la_attn_workspace_bytes(r0.block_tokens, r0.heads))
+    return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
 // Checks of one stage's arguments, shared by la_denoise_step and la_denoise_chain.
 la_status validate_stage(const la_kvring* rings, int32_t n_layers, int64_t block_id,
                          const void* const* q_raw, const void* const* k_raw,
@@ -383,9 +440,14 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
                         void* k_rot_ws, void* sink_k_rot_ws, const void* const* sink_k_new,
                         const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                         int32_t Wl, int32_t frames_per_block, int64_t sink_delta, double theta,
-                        float scale, float* x, const float* vel, int64_t n_latent, float dt,
-                        uint32_t flags, void* const* timing_events, la_stream_t stream) {
+                        float scale, void* attn_ws, size_t attn_ws_bytes, float* x,
+                        const float* vel, int64_t n_latent, float dt, uint32_t flags,
+                        void* const* timing_events, la_stream_t stream) {
   const bool append = !(flags & LA_STEP_ATTEND_ONLY);
+  // bf16 rings: RoPE emits Q already multiplied by the attention's base-2 score scale
+  // (one rounding), and the attention takes it as given
+  const float q_scale =
+      rings[0].dtype == LA_BF16 ? (float)((double)scale * 1.4426950408889634) : 1.0f;
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> la_status {
@@ -402,11 +464,12 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
     LA_TRY(mark(6 * l));
     LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
                              r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
-                             r->heads, r->head_dim, (la_dtype)r->dtype, theta, stream));
+                             r->heads, r->head_dim, (la_dtype)r->dtype, theta, q_scale, stream));
     LA_TRY(mark(6 * l + 1));
     LA_TRY(mark(6 * l + 2));
     LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot_ws, v_raw[l], r->block_tokens,
-                             attn_out[l], nullptr, scale, stream));
+                             attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes,
+                             stream));
     LA_TRY(mark(6 * l + 3));
     LA_TRY(mark(6 * l + 4));
     if (append)
@@ -433,8 +496,8 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                           void* k_rot_ws, void* sink_k_rot_ws, const void* const* sink_k_new,
                           const void* const* sink_v_new, const void* rope_table, int32_t Hl,
                           int32_t Wl, int32_t frames_per_block, int64_t sink_delta,
-                          double theta, float scale, float* x, const float* vel,
-                          int64_t n_latent, float dt, uint32_t flags,
+                          double theta, float scale, void* attn_ws, size_t attn_ws_bytes,
+                          float* x, const float* vel, int64_t n_latent, float dt, uint32_t flags,
                           void* const* timing_events, la_stream_t stream) {
   // ---- validate the whole step before enqueuing anything
   if (!q_rot_ws || !k_rot_ws || !sink_k_rot_ws || !rope_table) return LA_ERR_INVALID_ARG;
@@ -442,20 +505,25 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                                      sink_k_new, sink_v_new, Hl, Wl, frames_per_block, flags);
   if (v != LA_OK) return v;
   if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
+  {
+    const la_status w = validate_attn_ws(rings[0], scale, attn_ws, attn_ws_bytes);
+    if (w != LA_OK) return w;
+  }
   if (timing_events)
     for (int i = 0; i < 6 * n_layers + 2; ++i)
       if (!timing_events[i]) return LA_ERR_INVALID_ARG;
   return enqueue_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out, q_rot_ws,
                        k_rot_ws, sink_k_rot_ws, sink_k_new, sink_v_new, rope_table, Hl, Wl,
-                       frames_per_block, sink_delta, theta, scale, x, vel, n_latent, dt,
-                       flags, timing_events, stream);
+                       frames_per_block, sink_delta, theta, scale, attn_ws, attn_ws_bytes, x, vel,
+                       n_latent, dt, flags, timing_events, stream);
 }
 
 la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
                            int64_t block_id, void* q_rot_ws, void* k_rot_ws,
                            void* sink_k_rot_ws, const void* rope_table, int32_t Hl, int32_t Wl,
                            int32_t frames_per_block, int64_t sink_delta, double theta,
-                           float scale, float* x, int64_t n_latent, la_stream_t stream) {
+                           float scale, void* attn_ws, size_t attn_ws_bytes, float* x,
+                           int64_t n_latent, la_stream_t stream) {
   // ---- validate every stage, and the noise-level chain, before enqueuing anything
   if (!stages || n_stages < 1 || !q_rot_ws || !k_rot_ws || !sink_k_rot_ws || !rope_table)
     return LA_ERR_INVALID_ARG;
@@ -481,14 +549,18 @@ la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,
       if (fabs((double)g.rings[0].noise_level - expect) > 1e-6) return LA_ERR_NOISE_LEVEL;
     }
   }
+  {
+    const la_status w = validate_attn_ws(stages[0].rings[0], scale, attn_ws, attn_ws_bytes);
+    if (w != LA_OK) return w;
+  }
   for (int s = 0; s < n_stages; ++s) {
     const la_stage& g = stages[s];
     const la_status st = enqueue_stage(g.rings, n_layers, block_id, g.q_raw, g.k_raw, g.v_raw,
                                        g.attn_out, q_rot_ws, k_rot_ws, sink_k_rot_ws,
                                        g.sink_k_new, g.sink_v_new, rope_table, Hl, Wl,
-                                       frames_per_block, sink_delta, theta, scale,
-                                       n_latent > 0 ? x : nullptr, g.vel, n_latent, g.dt,
-                                       0u, nullptr, stream);
+                                       frames_per_block, sink_delta, theta, scale, attn_ws,
+                                       attn_ws_bytes, n_latent > 0 ? x : nullptr, g.vel,
+                                       n_latent, g.dt, 0u, nullptr, stream);
     if (st != LA_OK) return st;
   }
   return LA_OK;

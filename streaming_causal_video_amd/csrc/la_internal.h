@@ -32,6 +32,7 @@ struct RopeTensor {
   void* out;
   int32_t tokens;
   int32_t trow0;  // temporal row of this tensor's frame 0
+  float scale;    // factor applied to the rotated values before the store
 };
 
 struct RopeGeom {
@@ -45,8 +46,25 @@ hipError_t launch_rope_table(float* table, int Hl, int Wl, int hpairs, int wpair
 hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size_t bytes,
                         hipStream_t s);
 hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream_t s);
+// Workspace of the bf16 attention's persistent schedule: an arrival counter per unit
+// (zero between calls) and one partial record of kAttnRecFloats floats per slot.
+constexpr int kAttnRecFloats = 4 * (8 * 3 * 64 * 4 + 2 * 3 * 64);
+struct AttnWorkspace {
+  int32_t* counters;  // nullptr: no workspace, one workgroup per unit
+  float* partials;
+  int32_t slots;      // persistent workgroups (two per CU)
+};
+struct AttnWork {  // as passed to the kernel
+  int32_t* counters;
+  float* partials;
+  int32_t cuts;  // key ranges per unit of the last round (1: no unit is cut)
+};
+int attn_bf16_units(int nq, int heads);
+// qmul: factor applied to Q (then rounded to bf16) so that the kernel's base-2 scores
+// are Q K^T; 1.0f when the caller's Q is already scaled.
 hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
-                            int nk, int heads, float scale, hipStream_t s);
+                            int nk, int heads, float qmul, const AttnWorkspace& ws,
+                            hipStream_t s);
 hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, float scale, float dq, float dk, float dv,
                            hipStream_t s);

@@ -90,6 +90,15 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
     cs[i] = temporal ? tc.cs[trow][ti][0] : e.x;
     sn[i] = temporal ? tc.cs[trow][ti][1] : e.y;
   }
+  // An output scale (the attention's score scale folded into Q) multiplies the
+  // pair's cos/sin once per thread; with scale 1 the products are exact.
+  if (T.scale != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < kPPC; ++i) {
+      cs[i] *= T.scale;
+      sn[i] *= T.scale;
+    }
+  }
 
   for (int h0 = 0; h0 < g.heads; h0 += hg_n * kNH) {
     u32x4_t x[kNH];

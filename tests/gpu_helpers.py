@@ -85,6 +85,24 @@ def block_f0(block: int) -> int:
     return FRAMES_PER_BLOCK * (block - 1)
 
 
+def softmax_scale(head_dim: int) -> float:
+    return head_dim ** -0.5
+
+
+def q_prescale(head_dim: int) -> float:
+    """The factor la_denoise_step has RoPE apply to Q for bf16 rings: the softmax scale
+    times log2(e), rounded to float32 (the attention then takes Q as given)."""
+    return float(np.float32(softmax_scale(head_dim) * np.log2(np.e)))
+
+
+def prescaled_q(q: si.Stored, head_dim: int):
+    """Given bf16 Q -> (bf16 Q times q_prescale, rounded to nearest even; the float64 Q
+    that those bits stand for, i.e. divided by q_prescale again; the factor)."""
+    c = q_prescale(head_dim)
+    qs = si.make_stored(q.values * c, "bf16")
+    return qs, qs.values / c, c
+
+
 class GpuLayerStream:
     """One layer of the stage streamed block by block through the C ABI.
 
@@ -93,7 +111,11 @@ class GpuLayerStream:
     with the first latent frame of block 1's raw K and V.
     """
 
-    def __init__(self, shape: si.LayerShape, layer: int = 0, keep_lse: bool = False):
+    def __init__(self, shape: si.LayerShape, layer: int = 0, keep_lse: bool = False,
+                 fused: bool = True, workspace: bool = True):
+        """fused: RoPE writes Q times q_prescale and the attention takes it as given (the
+        step's form); else the plain rotation and q_scale 1.  workspace: run the
+        attention's balanced schedule (bf16 only)."""
         import streaming_causal_video_amd as L
         t = torch()
         self.L = L
@@ -117,6 +139,10 @@ class GpuLayerStream:
         self.out = t.empty_like(self.q_rot)
         self.lse = t.empty((s.heads, s.block_tokens), dtype=t.float32, device="cuda") if keep_lse else None
         self._dev = {}
+        bf16 = shape.dtype == "bf16"
+        self.scale = softmax_scale(s.head_dim)
+        self.q_scale = q_prescale(s.head_dim) if fused and bf16 else 1.0
+        self.ws = L.AttnWorkspace(s.block_tokens, s.heads) if workspace and bf16 else None
 
     def block_dev(self, block: int):
         e = self.shape.entry(block)
@@ -130,14 +156,19 @@ class GpuLayerStream:
         f0 = block_f0(block)
         L.la_rope3d_rolling(q, self.q_rot, k, self.k_rot, FRAMES_PER_BLOCK, f0,
                             self.ring.sink_k_raw, self.sink_k_rot, SINK_DELTA, self.table, s.Hl,
-                            s.Wl, s.heads, s.head_dim, THETA)
-        L.la_block_attn_fwd(self.ring.state, self.q_rot, self.sink_k_rot, self.k_rot, v, self.out,
-                            self.lse)
+                            s.Wl, s.heads, s.head_dim, THETA, q_scale=self.q_scale)
+        self.attend(v)
         ev = L.la_kvcache_append_evict(self.ring.state, self.k_rot, v, block, NOISE_LEVEL)
         if block == 1:
             n = s.sink_tokens
             L.la_sink_replace(self.ring.state, k[:n], v[:n])
         return ev
+
+    def attend(self, v_cur):
+        """la_block_attn_fwd of the rotated Q/K in place over the ring (before the append)."""
+        self.L.la_block_attn_fwd(self.ring.state, self.q_rot, self.sink_k_rot, self.k_rot, v_cur,
+                                 self.out, self.lse, scale=self.scale, q_scale=self.q_scale,
+                                 workspace=self.ws)
 
 
 @functools.lru_cache(maxsize=None)
@@ -147,3 +178,27 @@ def gpu_available() -> bool:
         return t.cuda.is_available()
     except Exception:
         return False
+
+
+def oracle_block_all_heads(shape: si.LayerShape, block: int, rows=None, workers: int = 8,
+                           **kw):
+    """StreamOracle.block_output(block) for every head, the heads spread over host
+    threads (numpy releases the GIL in its products and exponentials).  Returns (out
+    [rows, heads, d], lse [heads, rows])."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import StreamOracle
+
+    groups = [list(range(h, shape.heads, workers)) for h in range(min(workers, shape.heads))]
+
+    def one(hs):
+        return hs, StreamOracle(shape, heads=hs, **kw).block_output(block, rows=rows, with_lse=True)
+
+    n = shape.block_tokens if rows is None else len(rows)
+    out = np.empty((n, shape.heads, shape.head_dim))
+    lse = np.empty((shape.heads, n))
+    with ThreadPoolExecutor(len(groups)) as ex:
+        for hs, (o, l) in ex.map(one, groups):
+            out[:, hs, :] = o
+            lse[hs, :] = l
+    return out, lse

@@ -148,16 +148,16 @@ def test_attention_argument_checks_before_launch():
     p = ctypes.c_void_p(0x70000)
     out = ctypes.c_void_p(0x80000)
     # wrong n_q
-    assert lib.la_block_attn_fwd(ctypes.byref(r), p, p, p, p, 47, out, None, 0.1, None) == _lib.LA_ERR_SHAPE
+    assert lib.la_block_attn_fwd(ctypes.byref(r), p, p, p, p, 47, out, None, 0.1, 1.0, None, 0, None) == _lib.LA_ERR_SHAPE
     # non-positive scale
-    assert lib.la_block_attn_fwd(ctypes.byref(r), p, p, p, p, 48, out, None, 0.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_block_attn_fwd(ctypes.byref(r), p, p, p, p, 48, out, None, 0.0, 1.0, None, 0, None) == _lib.LA_ERR_INVALID_ARG
     # out aliasing q
-    assert lib.la_block_attn_fwd(ctypes.byref(r), p, p, p, p, 48, p, None, 0.1, None) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_block_attn_fwd(ctypes.byref(r), p, p, p, p, 48, p, None, 0.1, 1.0, None, 0, None) == _lib.LA_ERR_INVALID_ARG
     # bf16 path needs head_dim 128
     r64 = L.la_kvring()
     f = [0x10000] * 4
     L.la_kvring_init(r64, *f, 2, 48, 16, 2, 64, L.LA_BF16, 0.5)
-    assert lib.la_block_attn_fwd(ctypes.byref(r64), p, p, p, p, 48, out, None, 0.1, None) == _lib.LA_ERR_SHAPE
+    assert lib.la_block_attn_fwd(ctypes.byref(r64), p, p, p, p, 48, out, None, 0.1, 1.0, None, 0, None) == _lib.LA_ERR_SHAPE
 
 
 def test_rope_and_euler_argument_checks():
@@ -165,10 +165,10 @@ def test_rope_and_euler_argument_checks():
     p = ctypes.c_void_p(0x70000)
     assert lib.la_rope_table_bytes(30, 52, 128) == (30 + 52) * 21 * 2 * 4
     assert lib.la_rope_table_bytes(4, 4, 64) == (4 + 4) * 10 * 2 * 4
-    assert lib.la_rope3d_rolling(p, p, None, None, 0, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4, None) == _lib.LA_ERR_SHAPE
-    assert lib.la_rope3d_rolling(p, p, None, None, 5, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4, None) == _lib.LA_ERR_SHAPE
-    assert lib.la_rope3d_rolling(p, None, None, None, 3, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4, None) == _lib.LA_ERR_INVALID_ARG
-    assert lib.la_rope3d_rolling(p, p, None, None, 3, 0, None, None, -1, p, 4, 4, 2, 64, 5, 1e4, None) == _lib.LA_ERR_DTYPE
+    assert lib.la_rope3d_rolling(p, p, None, None, 0, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4, 1.0, None) == _lib.LA_ERR_SHAPE
+    assert lib.la_rope3d_rolling(p, p, None, None, 5, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4, 1.0, None) == _lib.LA_ERR_SHAPE
+    assert lib.la_rope3d_rolling(p, None, None, None, 3, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4, 1.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_rope3d_rolling(p, p, None, None, 3, 0, None, None, -1, p, 4, 4, 2, 64, 5, 1e4, 1.0, None) == _lib.LA_ERR_DTYPE
     assert lib.la_fm_euler_step(p, p, 0, -0.25, None) == _lib.LA_OK  # n == 0: nothing to do
     assert lib.la_fm_euler_step(p, p, -1, -0.25, None) == _lib.LA_ERR_INVALID_ARG
     assert lib.la_fm_euler_step(ctypes.c_void_p(0x70000), ctypes.c_void_p(0x70004), 16, -0.25, None) == _lib.LA_ERR_INVALID_ARG
@@ -218,26 +218,26 @@ def test_chain_refusals_change_nothing():
     s2, a2 = _fake_stage(r2, -0.25, 0x3000000)
     # ... but 0.75 + (-0.25) != 0.4: refused
     stages = (_lib.la_stage * 3)(s0, s1, s2)
-    st = lib.la_denoise_chain(stages, 3, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64, None)
+    st = lib.la_denoise_chain(stages, 3, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, None, 0, x, 64, None)
     assert st == _lib.LA_ERR_NOISE_LEVEL
     # the same rings in two stages: refused
     s1b, a1b = _fake_stage(r0, -0.25, 0x2000000)
     r0b = _fake_rings(2, 0.75)
     stages = (_lib.la_stage * 2)(s0, s1b)
-    assert lib.la_denoise_chain(stages, 2, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64,
+    assert lib.la_denoise_chain(stages, 2, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, None, 0, x, 64,
                                 None) == _lib.LA_ERR_INVALID_ARG
     # out-of-order block: refused
     stages = (_lib.la_stage * 2)(s0, s1)
-    assert lib.la_denoise_chain(stages, 2, 2, 2, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64,
+    assert lib.la_denoise_chain(stages, 2, 2, 2, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, None, 0, x, 64,
                                 None) == _lib.LA_ERR_STATE
     # latent without a velocity: refused
     s1.vel = None
     stages = (_lib.la_stage * 2)(s0, s1)
-    assert lib.la_denoise_chain(stages, 2, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, x, 64,
+    assert lib.la_denoise_chain(stages, 2, 2, 1, p, p, p, p, 4, 4, 3, -1, 1e4, 0.1, None, 0, x, 64,
                                 None) == _lib.LA_ERR_INVALID_ARG
     # shape mismatch inside a stage
     stages = (_lib.la_stage * 1)(s0)
-    assert lib.la_denoise_chain(stages, 1, 2, 1, p, p, p, p, 5, 4, 3, -1, 1e4, 0.1, x, 64,
+    assert lib.la_denoise_chain(stages, 1, 2, 1, p, p, p, p, 5, 4, 3, -1, 1e4, 0.1, None, 0, x, 64,
                                 None) == _lib.LA_ERR_SHAPE
     assert [bytes(r) for r in (r0, r1, r2)] == before
     del a0, a1, a2, a1b, r0b
@@ -251,10 +251,10 @@ def test_fp8_ring_and_entry_point_refusals():
     r8 = L.la_kvring()
     L.la_kvring_init(r8, 0x10000, 0x20000, 0x30000, 0x40000, 2, 48, 16, 2, 128, L.LA_FP8_E4M3, 0.5)
     assert r8.dtype == L.LA_FP8_E4M3
-    assert lib.la_block_attn_fwd(ctypes.byref(r8), p, p, p, p, 48, out, None, 0.1, None) == _lib.LA_ERR_DTYPE
+    assert lib.la_block_attn_fwd(ctypes.byref(r8), p, p, p, p, 48, out, None, 0.1, 1.0, None, 0, None) == _lib.LA_ERR_DTYPE
     qarr = (ctypes.c_void_p * 1)(0x50000)
     assert lib.la_denoise_step(ctypes.byref(r8), 1, 1, qarr, qarr, qarr, qarr, p, p, p, None, None,
-                               p, 4, 4, 3, -1, 1e4, 0.1, None, None, 0, -0.25, 0, None,
+                               p, 4, 4, 3, -1, 1e4, 0.1, None, 0, None, None, 0, -0.25, 0, None,
                                None) == _lib.LA_ERR_DTYPE
     # la_block_attn_fwd_fp8: wrong ring dtype, head_dim, factors, alignment, aliasing
     rb = make_ring(2)
@@ -290,8 +290,8 @@ def test_denoise_step_flag_refusals():
     arr = (ctypes.c_void_p * 1)(0x50000)
     before = bytes(rings[0])
     call = lambda flags, sink: lib.la_denoise_step(rings, 1, 1, arr, arr, arr, arr, p, p, p, sink,
-                                                   sink, p, 4, 4, 3, -1, 1e4, 0.1, None, None, 0,
-                                                   -0.25, flags, None, None)
+                                                   sink, p, 4, 4, 3, -1, 1e4, 0.1, None, 0, None, None,
+                                                   0, -0.25, flags, None, None)
     assert call(2, None) == _lib.LA_ERR_INVALID_ARG
     assert call(L.LA_STEP_ATTEND_ONLY, arr) == _lib.LA_ERR_INVALID_ARG
     assert bytes(rings[0]) == before
@@ -314,7 +314,7 @@ def test_attention_refuses_segments_beyond_32_bit_offsets():
 
     # bf16: (block + 64) x 40 x 128 x 2 B >= 2^32 from block = 419,367
     big = ring(419_400, L.LA_BF16)
-    assert lib.la_block_attn_fwd(ctypes.byref(big), p, p, p, p, 419_400, out, None, 0.1,
+    assert lib.la_block_attn_fwd(ctypes.byref(big), p, p, p, p, 419_400, out, None, 0.1, 1.0, None, 0,
                                  None) == _lib.LA_ERR_SHAPE
     # e4m3: (block + 64) x 40 x 128 B >= 2^32 from block = 838,797
     big8 = ring(838_800, L.LA_FP8_E4M3)
@@ -323,8 +323,92 @@ def test_attention_refuses_segments_beyond_32_bit_offsets():
     # just below the limits the size check passes and only the (deliberately) wrong n_q is
     # refused, so the refusal above came from the size
     ok = ring(419_300, L.LA_BF16)
-    assert lib.la_block_attn_fwd(ctypes.byref(ok), p, p, p, p, 419_299, out, None, 0.1,
+    assert lib.la_block_attn_fwd(ctypes.byref(ok), p, p, p, p, 419_299, out, None, 0.1, 1.0, None, 0,
                                  None) == _lib.LA_ERR_SHAPE
     ok8 = ring(838_700, L.LA_FP8_E4M3)
     assert lib.la_block_attn_fwd_fp8(ctypes.byref(ok8), p, p, p, p, p, 838_699, out, None,
                                      0.1, 1.0, 1.0, 1.0, None) == _lib.LA_ERR_SHAPE
+
+
+def test_scale_and_workspace_refusals():
+    """q_scale and the softmax scale must be positive and finite; a workspace must be
+    256-byte aligned; RoPE refuses a non-positive q_scale.  All before any launch."""
+    lib = L.lib()
+    r = make_ring(2)
+    p = ctypes.c_void_p(0x70000)
+    out = ctypes.c_void_p(0x80000)
+    call = lambda scale, q_scale, ws, nbytes: lib.la_block_attn_fwd(
+        ctypes.byref(r), p, p, p, p, 48, out, None, scale, q_scale, ws, nbytes, None)
+    assert call(0.1, 0.0, None, 0) == _lib.LA_ERR_INVALID_ARG
+    assert call(0.1, float("inf"), None, 0) == _lib.LA_ERR_INVALID_ARG
+    assert call(float("nan"), 1.0, None, 0) == _lib.LA_ERR_INVALID_ARG
+    assert call(0.1, 1.0, ctypes.c_void_p(0x90010), 1 << 30) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_rope3d_rolling(p, p, None, None, 3, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4,
+                                 0.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_rope3d_rolling(p, p, None, None, 3, 0, None, None, -1, p, 4, 4, 2, 64, 1, 1e4,
+                                 -1.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert lib.la_attn_workspace_bytes(0, 40) == 0
+    assert lib.la_attn_workspace_bytes(4680, 0) == 0
+    # the step: a misaligned workspace, or a non-positive scale, is refused
+    rings = _fake_rings(1, 0.5)
+    arr = (ctypes.c_void_p * 1)(0x50000)
+    before = bytes(rings[0])
+    step = lambda scale, ws: lib.la_denoise_step(rings, 1, 1, arr, arr, arr, arr, p, p, p, None,
+                                                 None, p, 4, 4, 3, -1, 1e4, scale, ws, 1 << 30,
+                                                 None, None, 0, -0.25, 0, None, None)
+    assert step(0.1, ctypes.c_void_p(0x90010)) == _lib.LA_ERR_INVALID_ARG
+    assert step(0.0, None) == _lib.LA_ERR_INVALID_ARG
+    assert bytes(rings[0]) == before
+
+
+def test_kvringstack_rejects_unsupported_dtypes():
+    """KVRingStack maps dtypes as KVRing does and raises before allocating anything."""
+    import torch
+    for dt in (torch.float16, torch.int8, torch.float64):
+        with pytest.raises(TypeError):
+            L.KVRingStack(2, 2, 48, 16, 2, 128, dt, 0.5)
+        with pytest.raises(TypeError):
+            L.KVRing(2, 48, 16, 2, 128, dt, 0.5)
+
+
+def test_step_wrapper_checks_every_tensor():
+    """la_denoise_step / la_denoise_chain (Python) check each per-layer tensor's shape and
+    dtype against the rings before anything reaches the library (CPU tensors: a tensor
+    that passes every shape and dtype check is then refused as not being on the GPU)."""
+    import torch
+    Hl, Wl, heads, d = 4, 4, 2, 128
+    rings = _fake_rings(2, 0.5, Hl=Hl, Wl=Wl, heads=heads, d=d)
+    bt, st = 3 * Hl * Wl, Hl * Wl
+    blk = lambda dtype=torch.bfloat16: torch.zeros((bt, heads, d), dtype=dtype)
+    snk = lambda: torch.zeros((st, heads, d), dtype=torch.bfloat16)
+    table = torch.zeros(L.la_rope_table_bytes(Hl, Wl, d) // 4)
+    good = dict(q_raw=[blk(), blk()], k_raw=[blk(), blk()], v_raw=[blk(), blk()],
+                attn_out=[blk(), blk()], q_rot_ws=blk(), k_rot_ws=blk(), sink_k_rot_ws=snk())
+
+    def call(**over):
+        a = dict(good, **over)
+        L.la_denoise_step(rings, 1, a["q_raw"], a["k_raw"], a["v_raw"], a["attn_out"],
+                          a["q_rot_ws"], a["k_rot_ws"], a["sink_k_rot_ws"],
+                          a.get("table", table), Hl, Wl, scale=0.1, x=a.get("x"),
+                          vel=a.get("vel"))
+
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        call()
+    with pytest.raises(ValueError, match="v_raw\\[1\\] has dtype"):
+        call(v_raw=[blk(), blk(torch.float32)])
+    with pytest.raises(ValueError, match="q_rot_ws has shape"):
+        call(q_rot_ws=snk())
+    with pytest.raises(ValueError, match="sink_k_rot_ws has shape"):
+        call(sink_k_rot_ws=blk())
+    with pytest.raises(ValueError, match="attn_out has 1 entries"):
+        call(attn_out=[blk()])
+    with pytest.raises(ValueError, match="rope_table"):
+        call(table=torch.zeros(4))
+    with pytest.raises(ValueError, match="float32"):
+        call(x=torch.zeros(8, dtype=torch.bfloat16), vel=torch.zeros(8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="vel must match x"):
+        call(x=torch.zeros(8), vel=torch.zeros(7))
+    stage = dict(rings=rings, q_raw=good["q_raw"], k_raw=good["k_raw"], v_raw=good["v_raw"],
+                 attn_out=[blk(), snk()], dt=-0.25)
+    with pytest.raises(ValueError, match="stages\\[0\\]\\.attn_out\\[1\\] has shape"):
+        L.la_denoise_chain([stage], 1, blk(), blk(), snk(), table, Hl, Wl, scale=0.1)

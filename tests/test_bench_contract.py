@@ -43,9 +43,11 @@ def test_c2_json_line_has_the_contract_fields():
     assert r["kernel"] == "attn_bf16_kernel" and r["kernel_version"].startswith("attn-")
 
 
-def test_traffic_tables_name_the_library_kernel_versions():
-    """The HBM traffic bench.py reports is keyed by kernel version: a version
-    bump in the library without new counter figures would report null."""
+def test_traffic_tables_are_backed_by_profiles():
+    """The HBM traffic bench.py reports is keyed by kernel version: every version in its
+    tables has a counter summary under profiles/ that names it, and a library version
+    with no entry (the kernel changed since the counters were taken) reports null."""
+    import glob
     import re
     sys.path.insert(0, ROOT)
     import bench
@@ -54,5 +56,8 @@ def test_traffic_tables_name_the_library_kernel_versions():
     attn = [t for t in tags if t.startswith("attn-")]
     fp8 = [t for t in tags if t.startswith("fp8-")]
     assert len(attn) == 1 and len(fp8) == 1, tags
-    assert attn[0] in bench.ATTN_TRAFFIC_BYTES
-    assert fp8[0] in bench.FP8_TRAFFIC_BYTES
+    profiles = "".join(open(f).read() for f in glob.glob(os.path.join(ROOT, "profiles", "*")))
+    for table in (bench.ATTN_TRAFFIC_BYTES, bench.FP8_TRAFFIC_BYTES):
+        for version in table:
+            assert re.search(rf"\b{re.escape(version)}\b", profiles), version
+    assert bench.ATTN_TRAFFIC_BYTES.get("attn-v0") is None

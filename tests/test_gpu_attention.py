@@ -8,8 +8,8 @@ import pytest
 import seeded_inputs as si
 from oracle import StreamOracle, attention_lse
 
-from gpu_helpers import (F32_MAX_ABS, GpuLayerStream, check_attention, say, to_dev, to_f64,
-                         torch)
+from gpu_helpers import (F32_MAX_ABS, GpuLayerStream, check_attention, oracle_block_all_heads,
+                         prescaled_q, rel_l2, say, softmax_scale, to_dev, to_f64, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,21 +40,47 @@ def _compare_block(gs, orc, b, rows=None, heads=None, lse_tol=None):
         assert np.abs(gl - lse_ref).max() <= lse_tol, f"{what}: lse"
 
 
-@pytest.mark.parametrize("shape,nblocks", [
-    (si.C1, 10),                # fp32, 10 streamed blocks, AAS after block 1
-    (si.SMALL_F32, 6),
-    (si.SMALL_F32_D128, 5),
-    (si.SMALL_BF16, 6),         # ragged: 35-token frames, 105-token blocks
-    (si.MID_BF16, 6),           # several query tiles and key tiles
+# bf16 attention forms: "step" = RoPE emits Q times scale*log2(e) and the attention takes
+# it as given, with the balanced schedule (what la_denoise_step runs); "plain" = the plain
+# rotated Q, multiplied in the kernel, one workgroup per query tile; "plain_ws" = plain Q
+# with the balanced schedule.
+MODES = {"step": dict(fused=True, workspace=True), "plain": dict(fused=False, workspace=False),
+         "plain_ws": dict(fused=False, workspace=True)}
+
+
+@pytest.mark.parametrize("shape,nblocks,mode", [
+    (si.C1, 10, "plain"),               # fp32, 10 streamed blocks, AAS after block 1
+    (si.SMALL_F32, 6, "plain"),
+    (si.SMALL_F32_D128, 5, "plain"),
+    (si.SMALL_BF16, 6, "step"),         # ragged: 35-token frames, 105-token blocks
+    (si.SMALL_BF16, 6, "plain"),
+    (si.MID_BF16, 6, "step"),           # several query tiles and key tiles; every unit
+    (si.MID_BF16, 6, "plain"),          # split into one piece per key tile
+    (si.MID_BF16, 6, "plain_ws"),
 ])
-def test_stream_every_block_full_output(L, shape, nblocks):
-    say(f"stream cfg {shape.cfg_id} x{nblocks}")
-    gs = GpuLayerStream(shape, keep_lse=True)
+def test_stream_every_block_full_output(L, shape, nblocks, mode):
+    say(f"stream cfg {shape.cfg_id} x{nblocks} {mode}")
+    gs = GpuLayerStream(shape, keep_lse=True, **MODES[mode])
     orc = StreamOracle(shape)
     lse_tol = 1e-5 if shape.dtype == "f32" else 5e-3
     for b in range(1, nblocks + 1):
         gs.step(b)
         _compare_block(gs, orc, b, lse_tol=lse_tol)
+
+
+def test_workspace_too_small_is_refused(L):
+    """A workspace below la_attn_workspace_bytes is refused before any launch."""
+    t = torch()
+    s = si.SMALL_BF16
+    gs = GpuLayerStream(s, fused=False, workspace=True)
+    need = L.la_attn_workspace_bytes(s.block_tokens, s.heads)
+    small = L.AttnWorkspace(s.block_tokens, s.heads)
+    small.nbytes = need - 256
+    with pytest.raises(L.LAError) as e:
+        L.la_block_attn_fwd(gs.ring.state, gs.q_rot, gs.sink_k_rot, gs.k_rot, gs.k_rot, gs.out,
+                            scale=gs.scale, workspace=small)
+    assert e.value.status == L._lib.LA_ERR_SHAPE
+    assert need > 2 * 104448
 
 
 def test_window_of_one_block(L):
@@ -72,12 +98,40 @@ def _rows(n, seed, k=96):
     return r[r < n]
 
 
-@pytest.mark.parametrize("shape", [si.C2, si.C2_PRESCALED])
-def test_c2_full_size_sampled(L, shape):
-    """One 40x128 layer at 480x832: blocks 1..5 streamed, block 1 (Nk 6240) and block 5
-    (Nk 24960) checked on sampled rows of three heads."""
-    say(f"C2 full size cfg {shape.cfg_id}")
+def test_c2_block5_every_output(L):
+    """One 40x128 layer at 480x832 streamed through blocks 1..5 in the step's form; block 5
+    (Nk 24960, the measured configuration) is compared with the float64 oracle on every
+    head, row and dimension (4680 x 40 x 128 outputs) and every row's LSE; block 1
+    (Nk 6240) on sampled rows of all heads."""
+    shape = si.C2
+    say("C2 full size, every output of block 5")
     gs = GpuLayerStream(shape, keep_lse=True)
+    rows1 = _rows(shape.block_tokens, 5)
+    for b in range(1, 6):
+        gs.step(b)
+        if b in (1, 5):
+            torch().cuda.synchronize()
+            got = to_f64(gs.out)
+            gl = gs.lse.cpu().numpy().astype(np.float64)
+            rows = None if b == 5 else rows1
+            ref, lse_ref = oracle_block_all_heads(shape, b, rows=rows)
+            g = got if rows is None else got[rows]
+            check_attention(g, ref, f"C2 block {b}")
+            gl = gl if rows is None else gl[:, rows]
+            lse_err = float(np.abs(gl - lse_ref).max())
+            say(f"C2 block {b}: max-abs {np.abs(g - ref).max():.3e}, rel-L2 {rel_l2(g, ref):.3e}, "
+                f"lse {lse_err:.3e}")
+            assert lse_err <= 5e-3, f"C2 block {b}: lse {lse_err:.3e}"
+
+
+@pytest.mark.parametrize("mode", ["plain"])
+def test_c2_prescaled_inputs_sampled(L, mode):
+    """The literal reading of the workload (inputs scaled by 1/sqrt(128) and the 1/sqrt(d)
+    softmax scale, logits ~100 times smaller): blocks 1 and 5 on sampled rows of three
+    heads, with the plain Q form and one workgroup per query tile."""
+    shape = si.C2_PRESCALED
+    say(f"C2 prescaled inputs, {mode}")
+    gs = GpuLayerStream(shape, keep_lse=True, **MODES[mode])
     orc = StreamOracle(shape, heads=[0, 21, 39])
     rows = _rows(shape.block_tokens, 5)
     for b in range(1, 6):
@@ -86,31 +140,72 @@ def test_c2_full_size_sampled(L, shape):
             _compare_block(gs, orc, b, rows=rows, lse_tol=5e-3)
 
 
-def test_c5_full_size_sampled(L):
-    """720p-shaped layer: Nk = 3520 + 4*10560 + 10560 = 56320 at block 5, with eviction at 6."""
+def test_c5_all_heads_sampled(L):
+    """720p-shaped layer: Nk = 3520 + 4*10560 + 10560 = 56320 at block 5, with eviction at
+    6; all 40 heads on sampled rows."""
     shape = si.C5
-    say("C5 full size")
+    say("C5 full size, all heads")
     gs = GpuLayerStream(shape)
-    orc = StreamOracle(shape, heads=[3, 38])
     rows = _rows(shape.block_tokens, 6, k=48)
     for b in range(1, 7):
         gs.step(b)
         if b in (5, 6):
-            _compare_block(gs, orc, b, rows=rows)
+            torch().cuda.synchronize()
+            ref, _ = oracle_block_all_heads(shape, b, rows=rows)
+            g = to_f64(gs.out)[rows]
+            check_attention(g, ref, f"C5 block {b}")
+            say(f"C5 block {b}: max-abs {np.abs(g - ref).max():.3e}, rel-L2 {rel_l2(g, ref):.3e}")
 
 
-def test_determinism(L):
-    """Two attention calls on an unchanged ring give identical bits."""
+@pytest.mark.parametrize("mode", ["step", "plain"])
+def test_determinism(L, mode):
+    """Attention calls on an unchanged ring give identical bits (with the balanced
+    schedule the merge of a split unit's pieces runs in piece order whichever piece
+    arrives last), and each call leaves the workspace's counters at zero."""
     t = torch()
-    gs = GpuLayerStream(si.MID_BF16)
+    gs = GpuLayerStream(si.MID_BF16, keep_lse=True, **MODES[mode])
     for b in range(1, 5):
         gs.step(b)
     v5 = gs.block_dev(5)[2]
-    L.la_block_attn_fwd(gs.ring.state, gs.q_rot, gs.sink_k_rot, gs.k_rot, v5, gs.out)
-    first = gs.out.clone()
-    L.la_block_attn_fwd(gs.ring.state, gs.q_rot, gs.sink_k_rot, gs.k_rot, v5, gs.out)
+    gs.attend(v5)
+    first, first_lse = gs.out.clone(), gs.lse.clone()
+    for _ in range(3):
+        gs.attend(v5)
+        t.cuda.synchronize()
+        assert t.equal(first.view(t.int16), gs.out.view(t.int16))
+        assert t.equal(first_lse, gs.lse)
+    if gs.ws is not None:
+        units = -(-si.MID_BF16.block_tokens // 192) * si.MID_BF16.heads
+        counters = gs.ws.buf[:4 * units].view(t.int32)
+        assert int(counters.abs().sum()) == 0, "arrival counters not reset"
+
+
+def test_c2_workspace_and_grid_agree(L):
+    """At the C2 shape (1000 query tiles, 390 key tiles each, split over a persistent
+    grid of two workgroups per CU) the balanced schedule and the one-workgroup-per-tile
+    grid agree.  They round P to bf16 against different running references (a piece
+    starts its own), so outputs may differ by an output ulp and each row sum by the
+    P-rounding noise: relative error 2^-9/sqrt(3) per probability, averaged over
+    ~N/e effective keys, ~1e-5 rms, ~1e-4 at the extreme of 187,200 rows."""
+    t = torch()
+    shape = si.C2
+    gs = GpuLayerStream(shape, keep_lse=True, fused=True, workspace=True)
+    for b in range(1, 5):
+        gs.step(b)
+    v5 = gs.block_dev(5)[2]
+    q5, k5, _ = gs.block_dev(5)
+    L.la_rope3d_rolling(q5, gs.q_rot, k5, gs.k_rot, 3, 12, gs.ring.sink_k_raw, gs.sink_k_rot, -1,
+                        gs.table, shape.Hl, shape.Wl, shape.heads, shape.head_dim,
+                        q_scale=gs.q_scale)
+    gs.attend(v5)
+    a, la_ = gs.out.clone(), gs.lse.clone()
+    gs.ws = None
+    gs.attend(v5)
     t.cuda.synchronize()
-    assert t.equal(first.view(t.int16), gs.out.view(t.int16))
+    d = (a.double() - gs.out.double()).abs().max().item()
+    dl = (la_ - gs.lse).abs().max().item()
+    say(f"workspace vs grid: max |diff| {d:.3e}, lse {dl:.3e}")
+    assert d <= 2 ** -7 and dl <= 1e-3
 
 
 def test_peaked_logits_on_given_bf16_inputs(L):
@@ -134,12 +229,17 @@ def test_peaked_logits_on_given_bf16_inputs(L):
         vals.append(v.values)
     q, kc, vc = s.block_inputs(0, 3)
     q, kc = x4(q), x4(kc)
+    # Q in the step's form: times scale*log2(e), rounded to bf16; the oracle reads the
+    # float64 values those bits stand for
+    qs, q_eff, c = prescaled_q(q, s.head_dim)
     out = t.empty((s.block_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
-    L.la_block_attn_fwd(ring.state, to_dev(q), ring.sink_k_raw, to_dev(kc), to_dev(vc), out)
+    ws = L.AttnWorkspace(s.block_tokens, s.heads)
+    L.la_block_attn_fwd(ring.state, to_dev(qs), ring.sink_k_raw, to_dev(kc), to_dev(vc), out,
+                        scale=softmax_scale(s.head_dim), q_scale=c, workspace=ws)
     t.cuda.synchronize()
     allk = np.concatenate([sk.values, *keys, kc.values])
     allv = np.concatenate([sv.values, *vals, vc.values])
-    ref, _ = attention_lse(q.values, allk, allv, s.head_dim ** -0.5)
+    ref, _ = attention_lse(q_eff, allk, allv, s.head_dim ** -0.5)
     check_attention(to_f64(out), ref, "peaked")
 
 
@@ -171,13 +271,16 @@ def test_late_dominant_keys_raise_the_reference(L):
             alpha = 100.0 * np.sqrt(d) / (np.log2(np.e) * float(qi @ qi))
             kv[p, h] = alpha * qi
     kc = si.make_stored(kv, "bf16")
+    qs, q_eff, c = prescaled_q(q, d)
     out = t.empty((s.block_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
     lse = t.empty((s.heads, s.block_tokens), dtype=t.float32, device="cuda")
-    L.la_block_attn_fwd(ring.state, to_dev(q), ring.sink_k_raw, to_dev(kc), to_dev(vc), out, lse)
+    ws = L.AttnWorkspace(s.block_tokens, s.heads)
+    L.la_block_attn_fwd(ring.state, to_dev(qs), ring.sink_k_raw, to_dev(kc), to_dev(vc), out, lse,
+                        scale=softmax_scale(d), q_scale=c, workspace=ws)
     t.cuda.synchronize()
     allk = np.concatenate([sk.values, *keys, kc.values])
     allv = np.concatenate([sv.values, *vals, vc.values])
-    ref, lse_ref = attention_lse(q.values, allk, allv, d ** -0.5)
+    ref, lse_ref = attention_lse(q_eff, allk, allv, d ** -0.5)
     got = to_f64(out)
     check_attention(got, ref, "late dominant keys")
     rows = sorted(planted)
@@ -186,8 +289,9 @@ def test_late_dominant_keys_raise_the_reference(L):
     assert np.abs(gl - lse_ref).max() <= 5e-3
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("sink,block", [(2, 5), (1, 1), (3, 40)])
-def test_tiny_key_ranges(L, sink, block):
+def test_tiny_key_ranges(L, sink, block, use_ws):
     """First block of a ring with no cached blocks: only sink + block keys (as few
     as 2), so the first 64-key tile is also the last and most of it is masked."""
     t = torch()
@@ -201,7 +305,9 @@ def test_tiny_key_ranges(L, sink, block):
     ring.sink_v.copy_(to_dev(sv))
     out = t.empty((block, heads, d), dtype=t.bfloat16, device="cuda")
     lse = t.empty((heads, block), dtype=t.float32, device="cuda")
-    L.la_block_attn_fwd(ring.state, to_dev(q), ring.sink_k_raw, to_dev(kc), to_dev(vc), out, lse)
+    ws = L.AttnWorkspace(block, heads) if use_ws else None
+    L.la_block_attn_fwd(ring.state, to_dev(q), ring.sink_k_raw, to_dev(kc), to_dev(vc), out, lse,
+                        scale=softmax_scale(d), workspace=ws)
     t.cuda.synchronize()
     ref, lse_ref = attention_lse(q.values, np.concatenate([sk.values, kc.values]),
                                  np.concatenate([sv.values, vc.values]), d ** -0.5)

@@ -110,7 +110,7 @@ class Fp8Stream:
         for dev, ref in zip((q8, k8, v8), self.codes[b]):
             assert np.array_equal(dev.cpu().numpy(), ref), f"block {b}: codes differ"
         L.la_block_attn_fwd_fp8(self.ring.state, q8, self.sink_k8, self.sink_v8, k8, v8, self.out,
-                                sc, sc, sc, lse=self.lse)
+                                sc, sc, sc, lse=self.lse, scale=s.head_dim ** -0.5)
         L.la_kvcache_append_evict(self.ring.state, k8, v8, b, 0.75)
 
     def reference(self, b, rows=None, heads=None):

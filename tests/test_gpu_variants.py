@@ -52,6 +52,9 @@ class Work:
         self.kws = t.empty(blk, dtype=t.bfloat16, device="cuda")
         self.sws = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
         self.outs = [t.empty(blk, dtype=t.bfloat16, device="cuda") for _ in range(N_LAYERS)]
+        # attention workspace: the balanced schedule in these passes (None: one
+        # workgroup per query tile)
+        self.aws = L.AttnWorkspace(s.block_tokens, s.heads)
 
 
 def run_pass(L, w, rings, layers, b, *, sink_delta=SINK_DELTA, replace_sink=True, flags=0,
@@ -63,9 +66,10 @@ def run_pass(L, w, rings, layers, b, *, sink_delta=SINK_DELTA, replace_sink=True
     rep = replace_sink and b == 1 and not flags
     L.la_denoise_step(rings, b, [d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev],
                       w.outs, w.qws, w.kws, w.sws, w.table, s.Hl, s.Wl, FRAMES_PER_BLOCK,
-                      sink_delta, THETA, sink_k_new=[d[1][:n] for d in dev] if rep else None,
+                      sink_delta, THETA, scale=s.head_dim ** -0.5,
+                      sink_k_new=[d[1][:n] for d in dev] if rep else None,
                       sink_v_new=[d[2][:n] for d in dev] if rep else None, x=x, vel=vel,
-                      dt=-0.25, flags=flags)
+                      dt=-0.25, flags=flags, attn_ws=w.aws)
 
 
 def check_outs(w, oracles, b, what):
