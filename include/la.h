@@ -233,6 +233,26 @@ la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* s
                             size_t workspace_bytes, la_stream_t stream);
 
 /*
+ * la_block_attn_fwd_noalloc - la_block_attn_fwd with a workspace that is a
+ * static device array of the library instead of caller memory.  For callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no allocating routine.
+ *   The array holds the arrival counters of at most 16,384 (head, 192-query
+ *   tile) units and the partial records of 512 persistent workgroups (53.5 MB on
+ *   each device the library runs on, held until the process ends); more units
+ *   (n_q / 192 rounded up, times heads) return LA_ERR_SHAPE.  On a device with
+ *   more than 256 compute units the persistent grid is limited to 512
+ *   workgroups.  Each call clears the counters first (a fill kernel on `stream`).
+ *   All calls on one device share the array: calls that overlap on a device
+ *   race.  Arguments and results otherwise as la_block_attn_fwd with a workspace.
+ */
+la_status la_block_attn_fwd_noalloc(const la_kvring* r, const void* q_rot,
+                                    const void* sink_k_rot, const void* k_cur_rot,
+                                    const void* v_cur, int32_t n_q, void* out,
+                                    float* lse_or_null, float scale, float q_scale,
+                                    la_stream_t stream);
+
+/*
  * la_attn_workspace_bytes - size of the la_block_attn_fwd workspace for n_q
  * queries and `heads` heads on the current device (an arrival counter per
  * 192-query tile and head, and one partial record of 104,448 bytes per

@@ -28,7 +28,7 @@ EXPORTED = [
     "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
     "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
     "la_denoise_step", "la_denoise_chain", "la_quantize_fp8", "la_block_attn_fwd_fp8",
-    "la_attn_workspace_bytes",
+    "la_attn_workspace_bytes", "la_block_attn_fwd_noalloc",
 ]
 
 
@@ -132,6 +132,7 @@ def _load():
                                              I32, I32, ctypes.c_int, D, F, VP]),
         "la_block_attn_fwd": (ctypes.c_int, [R, VP, VP, VP, VP, I32, VP, VP, F, F, VP, SZ, VP]),
         "la_attn_workspace_bytes": (SZ, [I32, I32]),
+        "la_block_attn_fwd_noalloc": (ctypes.c_int, [R, VP, VP, VP, VP, I32, VP, VP, F, F, VP]),
         "la_kvcache_append_evict": (ctypes.c_int, [R, VP, VP, I64, F, P(I64), VP]),
         "la_sink_replace": (ctypes.c_int, [R, VP, VP, VP]),
         "la_fm_euler_step": (ctypes.c_int, [VP, VP, I64, F, VP]),
@@ -303,6 +304,24 @@ def la_block_attn_fwd(ring: "la_kvring", q_rot, sink_k_rot, k_cur_rot, v_cur, ou
         _ptr(k_cur_rot, "k_cur_rot", blk, dtype), _ptr(v_cur, "v_cur", blk, dtype),
         ring.block_tokens, _ptr(out, "out", blk, dtype), lse_p, scale, q_scale, ws_p, ws_n,
         _stream()), "la_block_attn_fwd")
+
+
+def la_block_attn_fwd_noalloc(ring: "la_kvring", q_rot, sink_k_rot, k_cur_rot, v_cur, out,
+                              lse: Optional[object] = None, *, scale: float,
+                              q_scale: float = 1.0) -> None:
+    """la_block_attn_fwd with the library's static workspace (no allocation)."""
+    torch = _torch()
+    dtype = torch.bfloat16 if ring.dtype == LA_BF16 else torch.float32
+    blk = (ring.block_tokens, ring.heads, ring.head_dim)
+    snk = (ring.sink_tokens, ring.heads, ring.head_dim)
+    lse_p = None
+    if lse is not None:
+        lse_p = _ptr(lse, "lse", (ring.heads, ring.block_tokens), torch.float32)
+    _check(_load().la_block_attn_fwd_noalloc(
+        ctypes.byref(ring), _ptr(q_rot, "q_rot", blk, dtype), _ptr(sink_k_rot, "sink_k_rot", snk, dtype),
+        _ptr(k_cur_rot, "k_cur_rot", blk, dtype), _ptr(v_cur, "v_cur", blk, dtype),
+        ring.block_tokens, _ptr(out, "out", blk, dtype), lse_p, scale, q_scale, _stream()),
+        "la_block_attn_fwd_noalloc")
 
 
 def _slot_dtype(ring: "la_kvring"):

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["la_api.cpp", "rope.hip", "stream_ops.hip", "attn_bf16.hip", "attn_fp8.hip",
-           "attn_f32.hip"]
+           "attn_f32.hip", "noalloc.hip"]
 
 # Per-source extra flags.  The attention kernels never see NaN inputs, so they are
 # built without NaN-quieting semantics: fmaxf then maps to bare v_max/v_max3

@@ -201,10 +201,17 @@ size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads) {
   return attn_ws_bytes(n_q, heads, 2 * cus);
 }
 
-la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot,
-                            const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
-                            float* lse_or_null, float scale, float q_scale, void* workspace,
-                            size_t workspace_bytes, la_stream_t stream) {
+}  // extern "C"
+
+namespace la {
+
+la_status status_of(hipError_t e) { return hip_status(e); }
+
+la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot,
+                   const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
+                   float* lse_or_null, float scale, float q_scale, void* workspace,
+                   size_t workspace_bytes, int slot_cap, bool clear_counters,
+                   la_stream_t stream) {
   if (!r || !q_rot || !sink_k_rot || !k_cur_rot || !v_cur || !out) return LA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return LA_ERR_INVALID_ARG;
   if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
@@ -259,11 +266,17 @@ la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* s
     if (workspace) {
       const int cus = device_cus();
       if (cus < 1) return LA_ERR_HIP;
-      if (workspace_bytes < attn_ws_bytes(n_q, r->heads, 2 * cus)) return LA_ERR_SHAPE;
+      int slots = 2 * cus;
+      if (slot_cap > 0 && slots > slot_cap) slots = slot_cap;
+      if (workspace_bytes < attn_ws_bytes(n_q, r->heads, slots)) return LA_ERR_SHAPE;
       ws.counters = static_cast<int32_t*>(workspace);
       ws.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              attn_counter_bytes(n_q, r->heads));
-      ws.slots = 2 * cus;
+      ws.slots = slots;
+      if (clear_counters) {
+        e = la::launch_zero(workspace, attn_counter_bytes(n_q, r->heads), s);
+        if (e != hipSuccess) return hip_status(e);
+      }
     }
     e = la::launch_attn_bf16(q_rot, out, lse_or_null, segs, n_q, end, r->heads, qmul, ws, s);
   } else {
@@ -271,6 +284,22 @@ la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* s
                             scale / q_scale, s);
   }
   return hip_status(e);
+}
+
+size_t attn_workspace_bytes(int n_q, int heads, int slots) {
+  return attn_ws_bytes(n_q, heads, slots);
+}
+
+}  // namespace la
+
+extern "C" {
+
+la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot,
+                            const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
+                            float* lse_or_null, float scale, float q_scale, void* workspace,
+                            size_t workspace_bytes, la_stream_t stream) {
+  return la::attn_fwd(r, q_rot, sink_k_rot, k_cur_rot, v_cur, n_q, out, lse_or_null, scale,
+                      q_scale, workspace, workspace_bytes, 0, false, stream);
 }
 
 la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t n,

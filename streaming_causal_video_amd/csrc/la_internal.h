@@ -70,6 +70,20 @@ hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs&
                            hipStream_t s);
 hipError_t launch_quantize_fp8(const void* in, int in_dtype, void* out, int64_t n, float inv_scale,
                                hipStream_t s);
+// la_block_attn_fwd with its workspace given explicitly: slot_cap > 0 limits the
+// persistent grid to that many workgroups; clear_counters zeroes the arrival counters
+// (with a small fill kernel) before the launch.
+la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot,
+                   const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
+                   float* lse_or_null, float scale, float q_scale, void* workspace,
+                   size_t workspace_bytes, int slot_cap, bool clear_counters,
+                   la_stream_t stream);
+// Bytes of an attention workspace for `slots` persistent workgroups.
+size_t attn_workspace_bytes(int n_q, int heads, int slots);
+// Status of a HIP error (records its text as the thread's last HIP error).
+la_status status_of(hipError_t e);
+// Zero `bytes` (a multiple of 4) of device memory on stream s.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_attn_f32(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, int head_dim, float scale, hipStream_t s);
 

@@ -139,7 +139,23 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const void* __restr
   }
 }
 
+__global__ __launch_bounds__(kThreads) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads)
+    p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  int64_t wgs = (n + kThreads - 1) / kThreads;
+  if (wgs > 1024) wgs = 1024;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s,
+                     static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
 
 hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size_t bytes,
                         hipStream_t s) {
