@@ -49,8 +49,14 @@
 //    tile of compute hides their latency.  A DMA writes each wave's 1 KB
 //    contiguously, so K rows have no padding (256-byte pitch) and each
 //    16-byte chunk c of row r sits at chunk c ^ (r & 15), which keeps the
-//    fragment reads free of bank conflicts.  Tiles that straddle a segment
-//    boundary or run past the last key take a synchronous per-row copy.
+//    fragment reads free of bank conflicts.
+//  * Each segment of the key table is tiled on its own (segment s has
+//    ceil(len_s / 64) tiles, the last one partial), so every tile lies in one
+//    segment: its DMA uses one buffer descriptor whose record count ends at
+//    the segment's last row (rows past it load as zeros) and its missing keys
+//    are masked.  No per-row path for tiles that straddle two segments, and no
+//    per-tile segment search beyond one compare.  At 1560 + 5 x 4680 keys this
+//    computes 1.3 % masked keys; at 3520 + 5 x 10560 none.
 //  * V stays key-major in LDS (64 rows of 128 dims, 256-byte pitch) and the A
 //    operand of the second product (V^T: 16 dims x 8 keys per lane) is read
 //    with two ds_read_b64_tr_b16: in each 16-lane group lane i receives, as
@@ -147,8 +153,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
 attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                  float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
                  float qmul, int qtiles, int nwg, AttnWork wk) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  // The K and V buffers of the two stages are separate objects, so that the compiler
+  // can tell a DMA into one stage from the fragment reads of the other and does not
+  // wait for the DMA before those reads.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k0[KBUF], lds_v0[VBUF], lds_k1[KBUF],
+      lds_v1[VBUF];
   __shared__ int s_arrival;
+  auto kbuf = [&](int buf) __attribute__((always_inline)) -> uint16_t* {
+    return buf ? lds_k1 : lds_k0;
+  };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) -> uint16_t* {
+    return buf ? lds_v1 : lds_v0;
+  };
 
   // XCD-aware renumbering: consecutive logical ids on one XCD.
   const int pid = __builtin_amdgcn_workgroup_id_x();
@@ -163,7 +179,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const int c = lane & 15;  // query (scores) / row (operands) within a 16-tile
   const int g = lane >> 4;  // 8-element k-group of the operands
   const int64_t rs = (int64_t)heads * D;
-  const int ntiles = (nk + BN - 1) / BN;
+  const int ntiles = segs.tend[segs.nseg - 1];
 
   // Loader geometry (the same for every piece).  K DMA: wave w fills LDS rows
   // 16 w + 4 i + t (t = lane >> 4, i = 0..3), lane slot p = lane & 15 of a row
@@ -196,6 +212,17 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
   const int urem = units - rounds * P;
   const int cuts = wk.cuts;
   const int npieces = rounds + (lin < urem * cuts ? 1 : 0);
+
+  // Zero both V buffers once: the rows of a segment's partial last tile past its end
+  // are masked (P = 0 exactly) but still enter P V, so they must hold finite values;
+  // the DMA leaves either zeros there (rows outside the buffer descriptor) or the V
+  // rows of an earlier tile.
+#pragma unroll
+  for (int i = 0; i < VBUF / (8 * NTHREADS); ++i) {
+    const int e = (i * NTHREADS + tid) * 8;  // bf16 element index within a V buffer
+    *reinterpret_cast<uint4*>(lds_v0 + e) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(lds_v1 + e) = make_uint4(0, 0, 0, 0);
+  }
 
   for (int it = 0; it < npieces; ++it) {
     int unit = it * P + lin, kt0 = 0, kt1 = ntiles, cut = 0;
@@ -254,101 +281,73 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     }
 
     // Segment of the tile being loaded, kept in scalar registers: the segment
-    // table is read only when a tile crosses into the next segment.
-    int seg = 0, seg_start = 0, seg_end = segs.end[0];
+    // table is read only when the tiles enter the next segment.
+    int seg = 0, seg_t0 = 0, seg_t1 = segs.tend[0], seg_len = segs.end[0];
     const char* seg_k = static_cast<const char*>(segs.k[0]);
     const char* seg_v = static_cast<const char*>(segs.v[0]);
-    bool whole = true;               // tile inside one segment
     uint32_t sbase = 0, nbytes = 0;  // tile's byte offset in the segment, bytes left from there
+    int valid = BN;                  // keys of the tile inside its segment
 
     auto locate = [&](int tile) __attribute__((always_inline)) {
-      const int t0 = tile * BN;
-      while (t0 >= seg_end) {
+      while (tile >= seg_t1) {
+        seg_len = segs.end[seg + 1] - segs.end[seg];
         ++seg;
-        seg_start = seg_end;
-        seg_end = segs.end[seg];
+        seg_t0 = seg_t1;
+        seg_t1 = segs.tend[seg];
         seg_k = static_cast<const char*>(segs.k[seg]);
         seg_v = static_cast<const char*>(segs.v[seg]);
       }
-      whole = t0 + BN <= seg_end;
-      sbase = (uint32_t)(t0 - seg_start) * rs_bytes + hoff;
-      nbytes = (uint32_t)(seg_end - t0) * rs_bytes - hoff;
+      const int r0 = (tile - seg_t0) * BN;  // the tile's first row in the segment
+      valid = seg_len - r0 < BN ? seg_len - r0 : BN;
+      sbase = (uint32_t)r0 * rs_bytes + hoff;
+      nbytes = (uint32_t)(seg_len - r0) * rs_bytes - hoff;
     };
-    // one 16-byte chunk of tile row r; rows past the last key are clamped to it
-    // (their scores are masked)
-    auto row_load = [&](int t0, int r, int chunk, bool is_v) __attribute__((always_inline)) -> uint4 {
-      const int key = min(t0 + r, nk - 1);
-      int s = seg;
-      while (key >= segs.end[s]) ++s;
-      const int st = s ? segs.end[s - 1] : 0;
-      const int64_t off = (int64_t)(key - st) * rs + head * D + chunk * 8;
-      const uint16_t* base = static_cast<const uint16_t*>(is_v ? segs.v[s] : segs.k[s]);
-      return *reinterpret_cast<const uint4*>(base + off);
+    auto kload = [&](int buf) __attribute__((always_inline)) {
+      uint16_t* kb = kbuf(buf);
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void*)(kb + (16 * wave + 4 * i) * KP), 16,
+            kdoff[i], 8 * i * rs_bytes, 0, 0);
     };
-    auto kload = [&](int tile, int buf) __attribute__((always_inline)) {
-      uint16_t* kb = lds + buf * STAGE;
-      if (whole) {
-        const __amdgpu_buffer_rsrc_t kr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
+    auto vload = [&](int buf) __attribute__((always_inline)) {
+      uint16_t* vb = vbuf(buf);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              kr, (__attribute__((address_space(3))) void*)(kb + (16 * wave + 4 * i) * KP), 16,
-              kdoff[i], 8 * i * rs_bytes, 0, 0);
-      } else {
-        const int t0 = tile * BN;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * wave + 4 * i + t4;
-          const uint4 v = row_load(t0, key_of_krow(r), (lane & 15) ^ (r & 15), false);
-          *reinterpret_cast<uint4*>(kb + r * KP + (lane & 15) * 8) = v;
-        }
-      }
-    };
-    auto vload = [&](int tile, int buf) __attribute__((always_inline)) {
-      uint16_t* vb = lds + buf * STAGE + KBUF;
-      if (whole) {
-        const __amdgpu_buffer_rsrc_t vr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              vr, (__attribute__((address_space(3))) void*)(vb + (16 * wave + 4 * i) * VP), 16,
-              vdoff[i >> 1], 4 * i * rs_bytes, 0, 0);
-      } else {
-        const int t0 = tile * BN;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * wave + 4 * i + t4;
-          const int sw = 2 * (r & 3) + 8 * ((r >> 3) & 1);
-          const uint4 v = row_load(t0, r, (lane & 15) ^ sw, true);
-          *reinterpret_cast<uint4*>(vb + r * VP + (lane & 15) * 8) = v;
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void*)(vb + (16 * wave + 4 * i) * VP), 16,
+            vdoff[i >> 1], 4 * i * rs_bytes, 0, 0);
     };
 
     __syncthreads();  // the previous piece's last tile is done with both LDS buffers
     locate(kt0);
-    kload(kt0, 0);
-    vload(kt0, 0);
+    int valid_next = valid;  // keys of the tile in flight
+    kload(0);
+    vload(0);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the first tile's K DMA has landed
     // One 64-key tile j computed from LDS buffer `cur` while tile j + 1 is staged
     // into buffer 1 - cur.  The loop below runs two tiles per trip so that both
     // buffers are compile-time constants (LDS addresses become immediates).
     auto tile = [&](const int j, const int cur) __attribute__((always_inline)) {
       __syncthreads();
+      const int nvalid = valid_next;  // keys of this tile (the rest are masked)
       const bool more = j + 1 < kt1;
       if (more) {
         locate(j + 1);
-        kload(j + 1, 1 - cur);
+        valid_next = valid;
+        kload(1 - cur);
       }
-      const uint16_t* kb = lds + cur * STAGE;
+      const uint16_t* kb = kbuf(cur);
       // K fragment: row 16 blk + c, chunk 4 s + g, stored at chunk (4 s + g) ^ c
       const uint16_t* kr = kb + c * KP;
       // V operand by transposing reads (B = 0, 1 for keys + 0..3, + 4..7): this lane
       // addresses key 32 h + 8 g + (c >> 2) + 4 B, dims 16 dt + 4 (c & 3) .. +3, which
       // sits in LDS row 32 h + 16 (g >> 1) + 8 B + 4 (g & 1) + (c >> 2)
-      const char* vt = reinterpret_cast<const char*>(kb + KBUF);
+      const char* vt = reinterpret_cast<const char*>(vbuf(cur));
 
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -368,14 +367,15 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
             for (int nt = 0; nt < NQT; ++nt)
               st[b][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[b][nt], 0, 0, 0);
           }
-        if (h == 0 && more) vload(j + 1, 1 - cur);
-        if ((j + 1) * BN > nk) {
-          // last tile: row 4 g + i of block 2 h + b holds key 32 h + 8 g + 4 b + i
+        if (h == 0 && more) vload(1 - cur);
+        if (nvalid < BN) {
+          // the last tile of a segment: row 4 g + i of block 2 h + b holds key
+          // 32 h + 8 g + 4 b + i of the tile
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              if (j * BN + 32 * h + 8 * g + 4 * b + i >= nk) {
+              if (32 * h + 8 * g + 4 * b + i >= nvalid) {
 #pragma unroll
                 for (int nt = 0; nt < NQT; ++nt) st[b][nt][i] = -INFINITY;
               }
@@ -553,7 +553,7 @@ hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs
                             hipStream_t s) {
   const int qtiles = (nq + BM - 1) / BM;
   const int units = qtiles * heads;
-  const int ntiles = (nk + BN - 1) / BN;
+  const int ntiles = segs.tend[segs.nseg - 1];
   AttnWork wk = {nullptr, nullptr, 1};
   int nwg = units;  // one workgroup per unit
   if (ws.counters != nullptr) {

@@ -66,7 +66,7 @@ size_t attn_ws_bytes(int n_q, int heads, int slots) {
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.5 (gfx950) attn-v10 fp8-v6"; }
+const char* la_version(void) { return "liblahip 0.5 (gfx950) attn-v11 fp8-v6"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -256,6 +256,10 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
   end += r->block_tokens;
   segs.end[n++] = end;
   segs.nseg = n;
+  for (int i = 0, t = 0; i < n; ++i) {
+    t += (segs.end[i] - (i ? segs.end[i - 1] : 0) + 63) / 64;
+    segs.tend[i] = t;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (r->dtype == LA_BF16) {

@@ -11,11 +11,14 @@ namespace la {
 // Segment table of one attention call: keys [end[s-1], end[s]) come from
 // segment s, whose rows start at k[s] / v[s] with a row stride of
 // heads*head_dim elements.  Order: sink, cached blocks, current block.
+// tend[s]: 64-key tiles of segments 0..s when each segment is tiled on its own
+// (the bf16 kernel's tiling).
 constexpr int kMaxSegs = LA_MAX_WINDOW + 2;
 struct AttnSegs {
   const void* k[kMaxSegs];
   const void* v[kMaxSegs];
   int32_t end[kMaxSegs];
+  int32_t tend[kMaxSegs];
   int32_t nseg;
 };
 
