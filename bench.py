@@ -77,8 +77,10 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
     def randn(shape, dtype=torch.bfloat16):
         return torch.randn(shape, device=dev, dtype=torch.float32, generator=gen).to(dtype)
 
-    log(f"setup: {n_layers} layers, Hl={Hl} Wl={Wl} W={W} H={H} d={d}, Nq={bt} Nk={nk}")
-    stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, NOISE)
+    staged = args.ring == "staged"
+    log(f"setup: {n_layers} layers, Hl={Hl} Wl={Wl} W={W} H={H} d={d}, Nq={bt} Nk={nk}, "
+        f"{args.ring} rings")
+    stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, NOISE, staged=staged)
     for l in range(n_layers):
         stack.sink_k_raw[l].copy_(randn((st, H, d)))
         stack.sink_v[l].copy_(randn((st, H, d)))
@@ -148,11 +150,16 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
     rope_ms, _ = avg(0)
     attn_ms, attn_sd = avg(2)
     app_ms, _ = avg(4)
+    # per timed block: attention time of each layer's launch, averaged over the layers
+    per_block = [float(np.mean([objs[6 * l + 2].elapsed_time(objs[6 * l + 3])
+                                for l in range(n_layers)])) for objs in ev_objs]
+    per_block_step = [objs[0].elapsed_time(objs[6 * n_layers + 1]) for objs in ev_objs]
     eul = [objs[6 * n_layers].elapsed_time(objs[6 * n_layers + 1]) for objs in ev_objs]
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall / args.steps * 1e3:.3f} ms/step)")
     fl = attn_flops(bt, nk, d, H)
     rope_bytes = 2 * (2 * bt + st) * H * d * 2
-    app_bytes = 2 * 2 * bt * H * d * 2
+    # the fused append (staged rings) copies V only: RoPE wrote K into the slot
+    app_bytes = (1 if staged else 2) * 2 * bt * H * d * 2
     res = {
         "ms_per_step": ms_step,
         "blocks_per_s": 1e3 / ms_step,
@@ -165,7 +172,123 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
         "append_bytes": app_bytes,
         "euler_us": float(np.mean(eul)) * 1e3,
         "nq": bt, "nk": nk,
+        "first_block": block - args.steps + 1,
+        "per_block_attn_ms": per_block, "per_block_step_ms": per_block_step,
     }
+    return res
+
+
+def drift(first_block, per_block):
+    """Drift of a per-block series: means of the first and last tenth and the slope of a
+    least-squares line, in % of the mean per 100 blocks."""
+    y = np.asarray(per_block)
+    n = len(y)
+    k = max(1, n // 10)
+    x = np.arange(first_block, first_block + n)
+    slope = float(np.polyfit(x, y, 1)[0]) if n > 1 else 0.0
+    return {"blocks": f"{first_block}-{first_block + n - 1}", "mean_ms": round(float(y.mean()), 4),
+            "first_tenth_ms": round(float(y[:k].mean()), 4),
+            "last_tenth_ms": round(float(y[-k:].mean()), 4),
+            "slope_pct_per_100_blocks": round(100 * 100 * slope / float(y.mean()), 3),
+            "cv_pct": round(100 * float(y.std() / y.mean()), 2)}
+
+
+def hbm_kernels_bench(Hl, Wl, W, H, d, reps=24, euler_elems=1 << 28):
+    """The HBM-bound kernels alone, each launched `reps` times back to back between two
+    events over rotating buffers whose total exceeds the 256 MB last-level cache (so
+    every launch streams from HBM): RoPE of Q, K and the sink K (six input and six
+    output sets), the ring append (six K/V input sets into a 4-slot ring), and the
+    Euler update of a batched latent of `euler_elems` float32 values (x and v 1 GiB
+    each at the default).  RoPE and the append are checked once through the Python
+    binding and then called through the C entry points with their arguments built
+    beforehand, so that the host's marshalling does not pace the launches.  Returns
+    per-launch microseconds and GB/s."""
+    import ctypes
+
+    import torch
+    import streaming_causal_video_amd as L
+    from streaming_causal_video_amd._lib import LA_OK
+
+    dev = "cuda"
+    bt, st = FRAMES * Hl * Wl, Hl * Wl
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(55)
+
+    def randn(shape, dtype=torch.bfloat16):
+        return torch.randn(shape, device=dev, dtype=torch.float32, generator=gen).to(dtype)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n=reps):
+        fn(0)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us per launch
+
+    res = {}
+    nsets = 6
+    table = torch.empty(L.la_rope_table_bytes(Hl, Wl, d) // 4, dtype=torch.float32, device=dev)
+    L.la_rope_table_fill(table, Hl, Wl, d, THETA)
+    ins = [(randn((bt, H, d)), randn((bt, H, d)), randn((st, H, d))) for _ in range(nsets)]
+    outs = [tuple(torch.empty_like(t) for t in s) for s in ins]
+
+    lib = L.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    qs = float(np.float32(d ** -0.5 * np.log2(np.e)))
+    statuses = []
+    rope_args = []
+    for j in range(nsets):
+        a, b = ins[j], outs[j]
+        L.la_rope3d_rolling(a[0], b[0], a[1], b[1], FRAMES, 300 + 3 * j, a[2], b[2], DELTA, table,
+                            Hl, Wl, H, d, THETA, q_scale=qs)
+        rope_args.append((ptr(a[0]), ptr(b[0]), ptr(a[1]), ptr(b[1]), FRAMES, 300 + 3 * j,
+                          ptr(a[2]), ptr(b[2]), DELTA, ptr(table), Hl, Wl, H, d, L.LA_BF16, THETA,
+                          qs, stream))
+
+    def rope(i):
+        statuses.append(lib.la_rope3d_rolling(*rope_args[i % nsets]))
+
+    rope_bytes = 2 * (2 * bt + st) * H * d * 2
+    us = timed(rope)
+    res.update(rope_us=us, rope_GBps=rope_bytes / (us * 1e-6) / 1e9)
+    del outs
+    ring = L.KVRing(W, bt, st, H, d, torch.bfloat16, NOISE)
+    L.la_kvcache_append_evict(ring.state, ins[0][0], ins[0][1], 1, NOISE)
+    block = [1]
+    evicted = ctypes.c_int64()
+    app_args = [(ptr(ins[j][0]), ptr(ins[j][1])) for j in range(nsets)]
+
+    def append(i):
+        block[0] += 1
+        statuses.append(lib.la_kvcache_append_evict(ctypes.byref(ring.state), *app_args[i % nsets],
+                                                    block[0], NOISE, ctypes.byref(evicted),
+                                                    stream))
+
+    app_bytes = 2 * 2 * bt * H * d * 2
+    us = timed(append)
+    res.update(append_us=us, append_GBps=app_bytes / (us * 1e-6) / 1e9)
+    if any(st_ != LA_OK for st_ in statuses):
+        raise RuntimeError(f"standalone launches failed: {sorted(set(statuses))}")
+    del ring, ins
+    torch.cuda.empty_cache()
+    x = torch.randn(euler_elems, device=dev, generator=gen)
+    v = torch.randn(euler_elems, device=dev, generator=gen)
+    eul_reps = 8
+
+    def euler(i):
+        L.la_fm_euler_step(x, v, DT)
+
+    e_bytes = 3 * 4 * euler_elems
+    us = timed(euler, eul_reps)
+    res.update(euler_batched_elems=euler_elems, euler_batched_us=us,
+               euler_batched_GBps=e_bytes / (us * 1e-6) / 1e9)
+    del x, v
+    torch.cuda.empty_cache()
     return res
 
 
@@ -190,7 +313,8 @@ def gpu_chain_bench(args, Hl, Wl, W, H, d, n_layers, n_stages=4):
         f"Nq={bt} Nk={nk}, noise levels {levels}")
     stacks = []
     for i in range(n_stages):
-        stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, levels[i])
+        stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, levels[i],
+                              staged=args.ring == "staged")
         for l in range(n_layers):
             stack.sink_k_raw[l].copy_(randn((st, H, d)))
             stack.sink_v[l].copy_(randn((st, H, d)))
@@ -260,58 +384,94 @@ def blas_threads():
     return os.cpu_count() or 1
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(Hl, Wl, W, H, d, n_layers, budget_s=15.0):
-    """Time the float64 oracle on this host on a bounded sample of one step:
-    (layer, head) units of RoPE + attention + append, extrapolated to all
-    n_layers x H units, plus the Euler update on the whole latent."""
+    """Time the float64 oracle on this host, part by part, at the workload's sizes, in
+    the GPU's units: RoPE of the whole block's Q and K and of the sink K (GB/s of the
+    kernel's bf16 bytes), the ring append of a whole block (GB/s), the Euler update of
+    the 16x3x60x104 latent (GB/s), and attention over all Nk keys for as many heads as
+    fit in `budget_s` (TFLOP/s); the step's time is then extrapolated to all heads and
+    layers (stated in `sample`)."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from oracle import Ring, attention_lse, euler_step, rope3d
 
     rng = np.random.default_rng(0)
     bt, st = FRAMES * Hl * Wl, Hl * Wl
-    q = rng.standard_normal((bt, 1, d))
-    k = rng.standard_normal((bt, 1, d))
-    v = rng.standard_normal((bt, 1, d))
-    sk = rng.standard_normal((st, 1, d))
-    sv = rng.standard_normal((st, 1, d))
-    cached_k = [rng.standard_normal((bt, 1, d)) for _ in range(W)]
-    cached_v = [rng.standard_normal((bt, 1, d)) for _ in range(W)]
+    nk = st + (W + 1) * bt
     f0 = FRAMES * 100
-    units = 0
-    t_start = time.perf_counter()
-    while True:
-        ring = Ring(W, NOISE)
-        for i in range(W):
-            ring.append(i + 1, cached_k[i], cached_v[i], NOISE)
-        qr = rope3d(q, FRAMES, Hl, Wl, f0, THETA)
-        kr = rope3d(k, FRAMES, Hl, Wl, f0, THETA)
-        skr = rope3d(sk, 1, Hl, Wl, f0 + DELTA, THETA)
-        ck, cv = ring.keys_values()
-        attention_lse(qr, np.concatenate([skr, *ck, kr]), np.concatenate([sv, *cv, v]), d ** -0.5)
-        ring.append(W + 1, kr, v, NOISE)
-        units += 1
-        if time.perf_counter() - t_start >= budget_s or units >= n_layers * H:
-            break
-    t_units = (time.perf_counter() - t_start) / units
+
+    def clock(fn):
+        t = time.perf_counter()
+        out = fn()
+        return time.perf_counter() - t, out
+
+    q = rng.standard_normal((bt, H, d))
+    k = rng.standard_normal((bt, H, d))
+    v = rng.standard_normal((bt, H, d))
+    sk = rng.standard_normal((st, H, d))
+    sv = rng.standard_normal((st, H, d))
+    t_rope, (qr, kr, skr) = clock(lambda: (rope3d(q, FRAMES, Hl, Wl, f0, THETA),
+                                           rope3d(k, FRAMES, Hl, Wl, f0, THETA),
+                                           rope3d(sk, 1, Hl, Wl, f0 + DELTA, THETA)))
+    ring = Ring(W, NOISE)
+    for i in range(W):
+        ring.append(i + 1, rng.standard_normal((bt, H, d)), rng.standard_normal((bt, H, d)),
+                    NOISE)
+    ck, cv = ring.keys_values()
+    keys = np.concatenate([skr, *ck, kr])
+    vals = np.concatenate([sv, *cv, v])
+    t_att, heads_done = 0.0, 0
+    while heads_done < H and (heads_done == 0 or t_att < budget_s):
+        h = heads_done
+        dt_h, _ = clock(lambda: attention_lse(qr[:, h:h + 1], keys[:, h:h + 1], vals[:, h:h + 1],
+                                              d ** -0.5))
+        t_att += dt_h
+        heads_done += 1
+    t_head = t_att / heads_done
+    t_app, _ = clock(lambda: ring.append(W + 1, kr, v, NOISE))
     lat = rng.standard_normal((16, 3, 60, 104)).astype(np.float32)
     vel = rng.standard_normal((16, 3, 60, 104)).astype(np.float32)
-    te = time.perf_counter()
-    euler_step(lat, vel, DT).astype(np.float32)
-    t_euler = time.perf_counter() - te
-    t_step = t_units * n_layers * H + t_euler
+    t_eul, _ = clock(lambda: euler_step(lat, vel, DT).astype(np.float32))
+    t_layer = t_rope + H * t_head + t_app
+    t_step = n_layers * t_layer + t_eul
+    rope_bytes = 2 * (2 * bt + st) * H * d * 2
+    app_bytes = 2 * 2 * bt * H * d * 2
+    flop_head = 4.0 * bt * nk * d
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+    except Exception:
+        blas = []
     return {
         "value": 1.0 / t_step,
         "unit": "blocks/s",
         "cores": blas_threads(),
         "kind": "oracle",
-        "sample": (f"{units} of {n_layers * H} (layer, head) units of one step "
-                   f"(RoPE of Q, K, sink K + fp64 attention over {bt} x "
-                   f"{st + (W + 1) * bt} keys + ring append), timed "
-                   f"{t_units * units:.1f} s and scaled x{n_layers * H / units:.0f}; Euler on the "
-                   f"whole latent timed once"),
+        "sample": (f"float64 numpy oracle at {bt} queries x {nk} keys x {H} heads x {d}: RoPE of "
+                   f"the whole Q, K and sink K and the ring append of a whole block timed once, "
+                   f"attention timed on {heads_done} of {H} heads ({t_att:.1f} s) and scaled "
+                   f"x{H / heads_done:.0f}, then x{n_layers} layers, plus the Euler update of "
+                   f"the 16x3x60x104 latent"),
         "seconds_per_step_extrapolated": t_step,
+        "cpu_model": cpu_model(),
         "host_cpus": os.cpu_count(),
         "host_affinity": len(os.sched_getaffinity(0)),
+        "blas": [f"{api}:{n}" for api, n in blas],
+        "attn_tflops": flop_head / t_head / 1e12,
+        "rope_GBps": rope_bytes / t_rope / 1e9,
+        "append_GBps": app_bytes / t_app / 1e9,
+        "euler_GBps": 3 * 4 * lat.size / t_eul / 1e9,
     }
 
 
@@ -526,6 +686,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0,
                     help="layers per stage for the chain / refresh workloads (default 40)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--ring", choices=["staged", "plain"], default="staged",
+                    help="staged: W + 1 slots per ring, RoPE writes K into the next slot and the "
+                         "append copies only V (fused); plain: W slots, K and V copied")
     ap.add_argument("--attn-schedule", choices=["balanced", "grid"], default="balanced",
                     help="attention work schedule: persistent balanced grid with a workspace "
                          "(default) or one workgroup per query tile")
@@ -555,8 +718,10 @@ def main():
         name = "C2 one layer: bf16 block attention 40x128, Nq 4680, Nk 24960 (+RoPE, append, Euler)"
     elif args.workload == "c3":
         geo = dict(Hl=30, Wl=52, W=8, H=40, d=128, n_layers=1)
-        name = ("C3 one layer, window of 8 blocks: bf16 block attention 40x128, Nq 4680, "
-                "Nk 43680 (+RoPE, append, Euler)")
+        name = ("C3 one layer, window of 8 blocks, 200 streamed blocks: bf16 block attention "
+                "40x128, Nq 4680, Nk 43680 (+RoPE, append, Euler)")
+        if args.steps == 10:  # blocks 1..8 fill the ring; blocks 9..200 are timed
+            args.warmup, args.steps = 0, 192
     elif args.workload == "c5":
         geo = dict(Hl=44, Wl=80, W=4, H=40, d=128, n_layers=1)
         name = ("C5 720p-shaped layer: 44x80 tokens/frame, Nq 10560, Nk 56320 (sink + 4 cached "
@@ -585,21 +750,48 @@ def main():
         "data": "synthetic N(0,1) Q/K/V, sinks, latent and velocity resident in HBM (no trained weights)",
         "config": {"workload": name, "layers": geo["n_layers"], "heads": geo["H"],
                    "head_dim": geo["d"], "block_tokens": r["nq"], "sink_tokens": geo["Hl"] * geo["Wl"],
-                   "window_blocks": geo["W"], "nk": r["nk"], "parallelism": "none (1 GPU = 1 stage)"},
+                   "window_blocks": geo["W"], "nk": r["nk"],
+                   "rings": ("staged: W + 1 slots, RoPE writes K into the next slot, the append "
+                             "copies V (fused)" if args.ring == "staged" else
+                             "plain: W slots, the append copies K and V"),
+                   "parallelism": "none (1 GPU = 1 stage)"},
         "attn_tflops": round(r["attn_tflops"], 2),
         "attn_ms": round(r["attn_ms"], 4),
+        "per_block_drift": {"attention": drift(r["first_block"], r["per_block_attn_ms"]),
+                            "step": drift(r["first_block"], r["per_block_step_ms"])},
         "roofline": {"bound": "mfma", "achieved": round(r["attn_tflops"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(peak_frac, 4),
                      "traffic": traffic, "kernel": "attn_bf16_kernel", "kernel_version": version,
                      "flop_per_launch": r["attn_flop_per_launch"]},
         "streaming_kernels": {
+            "method": ("in the step: HIP events around each launch, mean over layers and timed "
+                       "steps (includes the gap between launches)"),
             "rope_us": round(r["rope_us"], 2), "rope_GBps": round(r["rope_gbs"], 1),
             "rope_frac_hbm": round(r["rope_gbs"] / PEAK_HBM_GBS, 4),
             "append_us": round(r["append_us"], 2), "append_GBps": round(r["append_gbs"], 1),
             "append_frac_hbm": round(r["append_gbs"] / PEAK_HBM_GBS, 4),
+            "append_bytes": r["append_bytes"],
             "euler_us": round(r["euler_us"], 2),
         },
     }
+    if args.workload in ("c4", "c2", "c5"):
+        hb = hbm_kernels_bench(geo["Hl"], geo["Wl"], geo["W"], geo["H"], geo["d"])
+        sk = out["streaming_kernels"]
+        sk["standalone"] = {
+            "method": ("each kernel launched 24 times back to back between two HIP events over "
+                       "rotating buffers larger than the 256 MB last-level cache (Euler: 8 "
+                       "launches on a batched latent); per-launch average"),
+            "rope_us": round(hb["rope_us"], 2), "rope_GBps": round(hb["rope_GBps"], 1),
+            "rope_frac_hbm": round(hb["rope_GBps"] / PEAK_HBM_GBS, 4),
+            "append_us": round(hb["append_us"], 2), "append_GBps": round(hb["append_GBps"], 1),
+            "append_frac_hbm": round(hb["append_GBps"] / PEAK_HBM_GBS, 4),
+            "euler_batched_elems": hb["euler_batched_elems"],
+            "euler_batched_us": round(hb["euler_batched_us"], 1),
+            "euler_batched_GBps": round(hb["euler_batched_GBps"], 1),
+            "euler_batched_frac_hbm": round(hb["euler_batched_GBps"] / PEAK_HBM_GBS, 4),
+        }
+        log(f"standalone HBM kernels: RoPE {hb['rope_GBps']:.0f} GB/s, append "
+            f"{hb['append_GBps']:.0f} GB/s, batched Euler {hb['euler_batched_GBps']:.0f} GB/s")
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on host cores ...")
         out["cpu_baseline"] = cpu_baseline(geo["Hl"], geo["Wl"], geo["W"], geo["H"], geo["d"],

@@ -61,7 +61,13 @@ typedef enum la_status {
  * its K/V slots in e4m3 and its sink (raw K and V) in bf16, because the sink
  * is re-rotated at every block from its raw values.
  */
+/* C++ gives the enum a fixed underlying type, so that any int a C caller passes is a
+ * value of the type (validated by every call) rather than undefined behaviour. */
+#ifdef __cplusplus
+typedef enum la_dtype : int { LA_BF16 = 0, LA_F32 = 1, LA_FP8_E4M3 = 2 } la_dtype;
+#else
 typedef enum la_dtype { LA_BF16 = 0, LA_F32 = 1, LA_FP8_E4M3 = 2 } la_dtype;
+#endif
 
 typedef void* la_stream_t; /* hipStream_t */
 
@@ -72,9 +78,13 @@ typedef void* la_stream_t; /* hipStream_t */
  * la_kvring - one layer's rolling noisy KV cache plus its attention sink.
  * A plain host struct owned by the caller; it only points at device memory.
  *
- *   k_slots, v_slots : device, [W][block_tokens][heads][head_dim] of dtype.
+ *   k_slots, v_slots : device, [nslots][block_tokens][heads][head_dim] of dtype.
  *                      (dtype LA_FP8_E4M3: e4m3 codes; the sink stays bf16.)
- *                      Slot s holds block b with (b - 1) mod W == s.
+ *                      Slot s holds block b with (b - 1) mod nslots == s.
+ *   nslots           : W (la_kvring_init), or W + 1 (la_kvring_init_staged: one
+ *                      slot beyond the window, where the next block's K and V can
+ *                      be written before the block's attention has read the
+ *                      window; the fused step below uses it).
  *   sink_k_raw       : device, [sink_tokens][heads][head_dim], the sink's
  *                      unrotated K (it is re-rotated at every block).
  *   sink_v           : device, same shape, the sink's V.
@@ -95,6 +105,7 @@ typedef struct la_kvring {
   void* sink_k_raw;
   void* sink_v;
   int32_t W;
+  int32_t nslots;
   int32_t block_tokens;
   int32_t sink_tokens;
   int32_t heads;
@@ -118,15 +129,43 @@ const char* la_version(void);
 /*
  * la_kvring_init - fill *r for an empty window.  Pure host; touches no device
  * memory (the slot contents are unspecified until blocks are appended).
- * 1 <= W <= LA_MAX_WINDOW; all sizes > 0; pointers non-NULL.
+ * 1 <= W <= LA_MAX_WINDOW; all sizes > 0; pointers non-NULL and 16-byte aligned;
+ * 8 <= head_dim <= 256, head_dim % 8 == 0; a slot (block_tokens * heads *
+ * head_dim elements) and the sink must each be a multiple of 16 bytes, else
+ * LA_ERR_SHAPE (this only restricts e4m3 rings).
  */
 la_status la_kvring_init(la_kvring* r, void* k_slots, void* v_slots, void* sink_k_raw,
                          void* sink_v, int32_t W, int32_t block_tokens, int32_t sink_tokens,
                          int32_t heads, int32_t head_dim, la_dtype dtype, float noise_level);
 
 /*
+ * la_kvring_init_staged - la_kvring_init for a ring with one slot more than its
+ * window: k_slots and v_slots hold W + 1 slots (W + 1 <= LA_MAX_WINDOW, else
+ * LA_ERR_SHAPE).  The window and its rules are unchanged (the last W blocks
+ * are attended to; block b - W leaves the window when block b is appended);
+ * only the placement differs: block b goes to slot (b - 1) mod (W + 1), which
+ * holds no block of the window while block b is being computed.  That lets a
+ * step write the block's rotated K straight into its slot (la_kvring_next_slot)
+ * instead of into a workspace that the append then copies: the pages' fused
+ * kernels (NOTES, Table 3, FP8 + FlashAttention-3 + fused kernels).
+ */
+la_status la_kvring_init_staged(la_kvring* r, void* k_slots, void* v_slots, void* sink_k_raw,
+                                void* sink_v, int32_t W, int32_t block_tokens,
+                                int32_t sink_tokens, int32_t heads, int32_t head_dim,
+                                la_dtype dtype, float noise_level);
+
+/*
+ * la_kvring_next_slot - device addresses of the K and V slot that block
+ * r->last_block + 1 will occupy.  Pure host.  LA_ERR_STATE if that slot still
+ * holds a block of the window (a ring of W slots with W blocks cached), since
+ * writing it before the block's attention would change what the attention
+ * reads; a staged ring's next slot is always free.
+ */
+la_status la_kvring_next_slot(const la_kvring* r, void** k_slot, void** v_slot);
+
+/*
  * la_kvring_advance - where appending block `block_id` would go, without
- * changing anything.  Pure host.  *slot = (block_id - 1) mod W; *evicted =
+ * changing anything.  Pure host.  *slot = (block_id - 1) mod nslots; *evicted =
  * the block that leaves the window (block_id - W) or 0 if none.  Returns
  * LA_ERR_STATE unless block_id == r->last_block + 1.
  */
@@ -264,12 +303,15 @@ size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads);
 /*
  * la_kvcache_append_evict - put block `block_id`'s rotated K and its V
  * (both [block_tokens][heads][head_dim], computed by this stage from its own
- * noisy input, BLOG 疑问 4) into slot (block_id - 1) mod W, evicting block
+ * noisy input, BLOG 疑问 4) into slot (block_id - 1) mod nslots, evicting block
  * block_id - W.  Requires block_id == r->last_block + 1 (else LA_ERR_STATE)
  * and noise_level == r->noise_level (else LA_ERR_NOISE_LEVEL: the timestep-
  * forcing rule of NEWS 方法概述, the cache and the latent share one noise
  * level).  *evicted_or_null receives the evicted id or 0.  The copy is
- * enqueued on `stream`; the index update happens at call time.
+ * enqueued on `stream`; the index update happens at call time.  A k_rot (v)
+ * that is the destination slot's own K (V) buffer, as la_kvring_next_slot
+ * returns it, is already in place and is not copied; any other k_rot or v must
+ * not overlap the destination slot.
  */
 la_status la_kvcache_append_evict(la_kvring* r, const void* k_rot, const void* v,
                                   int64_t block_id, float noise_level,
@@ -307,6 +349,11 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *   4. if block_id == 1 and sink_k_new != NULL: la_sink_replace with
  *      (sink_k_new[l], sink_v_new[l]) (Adaptive Attention Sink, NOTES 关键设计 3);
  * then la_fm_euler_step(x, vel, n_latent, dt) if x != NULL.
+ * Fused append (NOTES, Table 3, fused kernels): for a staged ring
+ * (la_kvring_init_staged) and without LA_STEP_ATTEND_ONLY, step 1 writes the
+ * rotated K straight into the ring's next slot (la_kvring_next_slot) instead of
+ * k_rot_ws, step 2 reads it there, and step 3 copies only V.  The results and
+ * the window's contents are the same bits as with k_rot_ws.
  *
  * flags (bitwise or):
  *   LA_STEP_ATTEND_ONLY : skip steps 3 and 4 (no append, no sink replacement);
@@ -366,7 +413,7 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
  *   in        : device, n elements of in_dtype (LA_BF16 or LA_F32), 16-byte aligned.
  *   out       : device, n bytes, 16-byte aligned, not overlapping in.
  *   inv_scale : > 0 and finite.
- * n == 0 is a no-op.  NaN inputs give unspecified codes.
+ * n == 0 is a no-op.  A NaN input gives the NaN code of its sign (0x7F, 0xFF).
  */
 la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t n,
                           float inv_scale, la_stream_t stream);

@@ -12,7 +12,9 @@ no format or scale convention; the reading here is the plainest one:
   1.75 * 2^8 = 448 and codes 0x7F / 0xFF are NaN;
 * encoding rounds to the nearest representable value, ties to an even
   mantissa, and saturates: magnitudes beyond 448 become 448; the sign is kept,
-  also when the value rounds to zero (-0 is code 0x80);
+  also when the value rounds to zero (-0 is code 0x80); a NaN becomes the NaN
+  code of its sign (0x7F, or 0xFF with the sign bit set), the only codes the
+  format reserves for NaN;
 * a tensor is quantised with one per-tensor scale s: code = E4M3(x / s), and
   its value is decode(code) * s.
 
@@ -45,11 +47,10 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def e4m3_encode(x) -> np.ndarray:
     """Nearest e4m3 code of each float64 value (ties to even mantissa), saturating
-    at +-448.  NaN inputs are not accepted."""
+    at +-448; NaN gives the NaN code of its sign (0x7F / 0xFF)."""
     x = np.asarray(x, dtype=np.float64)
-    if np.isnan(x).any():
-        raise ValueError("e4m3_encode: NaN input")
-    a = np.minimum(np.abs(x), E4M3_MAX)
+    nan = np.isnan(x)
+    a = np.minimum(np.abs(np.where(nan, 0.0, x)), E4M3_MAX)
     # exponent of the binade holding a, clamped to the subnormal binade at the bottom
     _, ex = np.frexp(a)  # a = f * 2^ex with 0.5 <= f < 1  (ex = 0 for a = 0)
     e = np.clip(ex - 1, 1 - _BIAS, 8)  # unbiased exponent, >= -6
@@ -62,6 +63,7 @@ def e4m3_encode(x) -> np.ndarray:
     normal = q >= 8
     code = np.where(normal, ((e + _BIAS).astype(np.int64) << 3) | (q.astype(np.int64) - 8),
                     q.astype(np.int64))
+    code = np.where(nan, 0x7F, code)
     code = np.where(np.signbit(x), code | 0x80, code)  # the sign survives rounding to zero
     return code.astype(np.uint8)
 

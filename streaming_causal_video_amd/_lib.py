@@ -24,8 +24,8 @@ LA_STEP_ATTEND_ONLY = 1
 LA_MAX_BLOCK_FRAMES = 4
 
 EXPORTED = [
-    "la_status_string", "la_last_hip_error", "la_version", "la_kvring_init", "la_kvring_advance",
-    "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
+    "la_status_string", "la_last_hip_error", "la_version", "la_kvring_init",
+    "la_kvring_init_staged", "la_kvring_advance", "la_kvring_next_slot", "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
     "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
     "la_denoise_step", "la_denoise_chain", "la_quantize_fp8", "la_block_attn_fwd_fp8",
     "la_attn_workspace_bytes", "la_block_attn_fwd_noalloc",
@@ -41,6 +41,7 @@ class la_kvring(ctypes.Structure):
         ("sink_k_raw", ctypes.c_void_p),
         ("sink_v", ctypes.c_void_p),
         ("W", ctypes.c_int32),
+        ("nslots", ctypes.c_int32),
         ("block_tokens", ctypes.c_int32),
         ("sink_tokens", ctypes.c_int32),
         ("heads", ctypes.c_int32),
@@ -124,7 +125,10 @@ def _load():
         "la_last_hip_error": (ctypes.c_char_p, []),
         "la_version": (ctypes.c_char_p, []),
         "la_kvring_init": (ctypes.c_int, [R, VP, VP, VP, VP, I32, I32, I32, I32, I32, ctypes.c_int, F]),
+        "la_kvring_init_staged": (ctypes.c_int, [R, VP, VP, VP, VP, I32, I32, I32, I32, I32,
+                                                 ctypes.c_int, F]),
         "la_kvring_advance": (ctypes.c_int, [R, I64, P(I32), P(I64)]),
+        "la_kvring_next_slot": (ctypes.c_int, [R, P(VP), P(VP)]),
         "la_kvring_count": (I32, [R]),
         "la_rope_table_bytes": (ctypes.c_size_t, [I32, I32, I32]),
         "la_rope_table_fill": (ctypes.c_int, [VP, I32, I32, I32, D, VP]),
@@ -208,15 +212,36 @@ def la_version() -> str:
     return _load().la_version().decode()
 
 
+def _addr(x):
+    return ctypes.c_void_p(x if isinstance(x, int) else x.data_ptr())
+
+
 def la_kvring_init(ring: "la_kvring", k_slots, v_slots, sink_k_raw, sink_v, W: int,
                    block_tokens: int, sink_tokens: int, heads: int, head_dim: int,
                    dtype: int, noise_level: float) -> None:
     """Pointers may be tensors or raw integer addresses."""
-    def addr(x):
-        return ctypes.c_void_p(x if isinstance(x, int) else x.data_ptr())
-    _check(_load().la_kvring_init(ctypes.byref(ring), addr(k_slots), addr(v_slots),
-                                  addr(sink_k_raw), addr(sink_v), W, block_tokens, sink_tokens,
+    _check(_load().la_kvring_init(ctypes.byref(ring), _addr(k_slots), _addr(v_slots),
+                                  _addr(sink_k_raw), _addr(sink_v), W, block_tokens, sink_tokens,
                                   heads, head_dim, dtype, noise_level), "la_kvring_init")
+
+
+def la_kvring_init_staged(ring: "la_kvring", k_slots, v_slots, sink_k_raw, sink_v, W: int,
+                          block_tokens: int, sink_tokens: int, heads: int, head_dim: int,
+                          dtype: int, noise_level: float) -> None:
+    """la_kvring_init with W + 1 slots in k_slots / v_slots."""
+    _check(_load().la_kvring_init_staged(ctypes.byref(ring), _addr(k_slots), _addr(v_slots),
+                                         _addr(sink_k_raw), _addr(sink_v), W, block_tokens,
+                                         sink_tokens, heads, head_dim, dtype, noise_level),
+           "la_kvring_init_staged")
+
+
+def la_kvring_next_slot(ring: "la_kvring"):
+    """(k_slot, v_slot) device addresses where block last_block + 1 will be stored."""
+    k = ctypes.c_void_p()
+    v = ctypes.c_void_p()
+    _check(_load().la_kvring_next_slot(ctypes.byref(ring), ctypes.byref(k), ctypes.byref(v)),
+           "la_kvring_next_slot")
+    return k.value, v.value
 
 
 def la_kvring_advance(ring: "la_kvring", block_id: int):
@@ -540,9 +565,9 @@ class KVRing:
     """One layer's ring + sink: device buffers from torch, index state in la_kvring."""
 
     def __init__(self, W: int, block_tokens: int, sink_tokens: int, heads: int, head_dim: int,
-                 dtype, noise_level: float, device="cuda"):
+                 dtype, noise_level: float, device="cuda", staged: bool = False):
         """dtype: torch.bfloat16, torch.float32, or torch.uint8 for e4m3 slots (the
-        sink of an e4m3 ring is bf16)."""
+        sink of an e4m3 ring is bf16).  staged: W + 1 slots (la_kvring_init_staged)."""
         torch = _torch()
         codes = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.uint8: LA_FP8_E4M3}
         if dtype not in codes:
@@ -550,21 +575,23 @@ class KVRing:
                             "for e4m3 slots)")
         code = codes[dtype]
         sink_dtype = torch.bfloat16 if code == LA_FP8_E4M3 else dtype
-        self.k_slots = torch.empty((W, block_tokens, heads, head_dim), dtype=dtype, device=device)
+        ns = W + 1 if staged else W
+        self.k_slots = torch.empty((ns, block_tokens, heads, head_dim), dtype=dtype, device=device)
         self.v_slots = torch.empty_like(self.k_slots)
         self.sink_k_raw = torch.empty((sink_tokens, heads, head_dim), dtype=sink_dtype,
                                       device=device)
         self.sink_v = torch.empty_like(self.sink_k_raw)
         self.state = la_kvring()
-        la_kvring_init(self.state, self.k_slots, self.v_slots, self.sink_k_raw, self.sink_v, W,
-                       block_tokens, sink_tokens, heads, head_dim, code, noise_level)
+        init = la_kvring_init_staged if staged else la_kvring_init
+        init(self.state, self.k_slots, self.v_slots, self.sink_k_raw, self.sink_v, W,
+             block_tokens, sink_tokens, heads, head_dim, code, noise_level)
 
     @property
     def count(self) -> int:
         return la_kvring_count(self.state)
 
     def slot_ids(self):
-        return [int(self.state.slot_block[s]) for s in range(self.state.W)]
+        return [int(self.state.slot_block[s]) for s in range(self.state.nslots)]
 
 
 class KVRingStack:
@@ -572,7 +599,9 @@ class KVRingStack:
     la_denoise_step can take them as one array."""
 
     def __init__(self, n_layers: int, W: int, block_tokens: int, sink_tokens: int, heads: int,
-                 head_dim: int, dtype, noise_level: float, device="cuda"):
+                 head_dim: int, dtype, noise_level: float, device="cuda", staged: bool = False):
+        """staged: W + 1 slots per ring (la_kvring_init_staged; la_denoise_step then
+        writes each layer's rotated K straight into its next slot)."""
         torch = _torch()
         codes = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.uint8: LA_FP8_E4M3}
         if dtype not in codes:
@@ -580,14 +609,15 @@ class KVRingStack:
                             "for e4m3 slots)")
         code = codes[dtype]
         sink_dtype = torch.bfloat16 if code == LA_FP8_E4M3 else dtype
-        self.k_slots = torch.empty((n_layers, W, block_tokens, heads, head_dim), dtype=dtype,
+        ns = W + 1 if staged else W
+        self.k_slots = torch.empty((n_layers, ns, block_tokens, heads, head_dim), dtype=dtype,
                                    device=device)
         self.v_slots = torch.empty_like(self.k_slots)
         self.sink_k_raw = torch.empty((n_layers, sink_tokens, heads, head_dim), dtype=sink_dtype,
                                       device=device)
         self.sink_v = torch.empty_like(self.sink_k_raw)
         self.states = (la_kvring * n_layers)()
+        init = la_kvring_init_staged if staged else la_kvring_init
         for l in range(n_layers):
-            la_kvring_init(self.states[l], self.k_slots[l], self.v_slots[l], self.sink_k_raw[l],
-                           self.sink_v[l], W, block_tokens, sink_tokens, heads, head_dim, code,
-                           noise_level)
+            init(self.states[l], self.k_slots[l], self.v_slots[l], self.sink_k_raw[l],
+                 self.sink_v[l], W, block_tokens, sink_tokens, heads, head_dim, code, noise_level)

@@ -74,6 +74,46 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def asan_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime (it also carries UBSan)."""
+    import glob
+    found = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib",
+                                          "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise RuntimeError("clang's shared ASan runtime was not found")
+    return found[-1]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """A CPU-side checking build: the host library code (la_api.cpp: argument checks,
+    ring and sink state, the step and chain drivers) compiled with AddressSanitizer and
+    UndefinedBehaviorSanitizer for the host only, linked with the ordinary kernel
+    objects of the last build().  Returns the library path; load it into a process
+    that has asan_runtime() preloaded.  Not for GPU runs."""
+    os.makedirs(out_dir, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in SOURCES[1:]]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_obj = os.path.join(out_dir, "la_api_san.o")
+    cmd = [hipcc(), *[f for f in CFLAGS if f != "-O3"], "-O1", "-g", *san, "-x", "hip", "-c",
+           os.path.join(CSRC, SOURCES[0]), "-o", api_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized compile failed:\n{res.stderr}")
+    rocm = os.path.dirname(os.path.dirname(hipcc()))
+    lib = os.path.join(out_dir, "liblahip_san.so")
+    cmd = [os.path.join(rocm, "llvm", "bin", "clang++"), "-shared", "-fsanitize=address,undefined",
+           "-shared-libsan", api_obj, *objs, "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", lib]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{res.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

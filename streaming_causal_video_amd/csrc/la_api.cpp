@@ -83,23 +83,43 @@ const char* la_status_string(int st) {
 
 const char* la_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
-la_status la_kvring_init(la_kvring* r, void* k_slots, void* v_slots, void* sink_k_raw,
-                         void* sink_v, int32_t W, int32_t block_tokens, int32_t sink_tokens,
-                         int32_t heads, int32_t head_dim, la_dtype dtype, float noise_level) {
+}  // extern "C"
+
+namespace {
+
+// Slots of a ring: W, or W + 1 for a staged ring; 0 if the struct is not a valid ring.
+int ring_slots(const la_kvring* r) {
+  if (r->W < 1 || r->W > LA_MAX_WINDOW) return 0;
+  if (r->nslots != r->W && r->nslots != r->W + 1) return 0;
+  if (r->nslots > LA_MAX_WINDOW) return 0;
+  return r->nslots;
+}
+
+la_status ring_init(la_kvring* r, void* k_slots, void* v_slots, void* sink_k_raw, void* sink_v,
+                    int32_t W, int32_t nslots, int32_t block_tokens, int32_t sink_tokens,
+                    int32_t heads, int32_t head_dim, la_dtype dtype, float noise_level) {
   if (!r || !k_slots || !v_slots || !sink_k_raw || !sink_v) return LA_ERR_INVALID_ARG;
   if (!valid_ring_dtype(dtype)) return LA_ERR_DTYPE;
-  if (W < 1 || W > LA_MAX_WINDOW || block_tokens < 1 || sink_tokens < 1 || heads < 1 ||
+  if (W < 1 || nslots > LA_MAX_WINDOW || block_tokens < 1 || sink_tokens < 1 || heads < 1 ||
       head_dim < 8 || head_dim % 8 != 0 || head_dim > 256)
     return LA_ERR_SHAPE;
   if (!isfinite(noise_level)) return LA_ERR_INVALID_ARG;
   if (!aligned16(k_slots) || !aligned16(v_slots) || !aligned16(sink_k_raw) || !aligned16(sink_v))
     return LA_ERR_INVALID_ARG;
+  // every slot and the sink must be whole 16-byte vectors, so that each slot starts
+  // 16-byte aligned (an e4m3 ring with heads * head_dim * block_tokens not a multiple
+  // of 16 would not)
+  const int64_t row = (int64_t)heads * head_dim;
+  if ((row * block_tokens * (int64_t)elem_size(dtype)) % 16 != 0 ||
+      (row * sink_tokens * (int64_t)sink_elem_size(dtype)) % 16 != 0)
+    return LA_ERR_SHAPE;
   memset(r, 0, sizeof(*r));
   r->k_slots = k_slots;
   r->v_slots = v_slots;
   r->sink_k_raw = sink_k_raw;
   r->sink_v = sink_v;
   r->W = W;
+  r->nslots = nslots;
   r->block_tokens = block_tokens;
   r->sink_tokens = sink_tokens;
   r->heads = heads;
@@ -109,13 +129,49 @@ la_status la_kvring_init(la_kvring* r, void* k_slots, void* v_slots, void* sink_
   return LA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+la_status la_kvring_init(la_kvring* r, void* k_slots, void* v_slots, void* sink_k_raw,
+                         void* sink_v, int32_t W, int32_t block_tokens, int32_t sink_tokens,
+                         int32_t heads, int32_t head_dim, la_dtype dtype, float noise_level) {
+  return ring_init(r, k_slots, v_slots, sink_k_raw, sink_v, W, W, block_tokens, sink_tokens,
+                   heads, head_dim, dtype, noise_level);
+}
+
+la_status la_kvring_init_staged(la_kvring* r, void* k_slots, void* v_slots, void* sink_k_raw,
+                                void* sink_v, int32_t W, int32_t block_tokens,
+                                int32_t sink_tokens, int32_t heads, int32_t head_dim,
+                                la_dtype dtype, float noise_level) {
+  return ring_init(r, k_slots, v_slots, sink_k_raw, sink_v, W, W + 1, block_tokens, sink_tokens,
+                   heads, head_dim, dtype, noise_level);
+}
+
 la_status la_kvring_advance(const la_kvring* r, int64_t block_id, int32_t* slot,
                             int64_t* evicted) {
   if (!r || !slot || !evicted) return LA_ERR_INVALID_ARG;
-  if (r->W < 1 || r->W > LA_MAX_WINDOW) return LA_ERR_STATE;
+  const int ns = ring_slots(r);
+  if (ns == 0) return LA_ERR_STATE;
   if (block_id != r->last_block + 1 || block_id < 1) return LA_ERR_STATE;
-  *slot = (int32_t)((block_id - 1) % r->W);
+  *slot = (int32_t)((block_id - 1) % ns);
   *evicted = block_id > r->W ? block_id - r->W : 0;
+  return LA_OK;
+}
+
+la_status la_kvring_next_slot(const la_kvring* r, void** k_slot, void** v_slot) {
+  if (!r || !k_slot || !v_slot) return LA_ERR_INVALID_ARG;
+  int32_t slot;
+  int64_t evicted;
+  const la_status st = la_kvring_advance(r, r->last_block + 1, &slot, &evicted);
+  if (st != LA_OK) return st;
+  // a ring of W slots reuses the slot of the block that leaves the window, which
+  // the next block's attention still reads
+  if (r->nslots == r->W && evicted != 0) return LA_ERR_STATE;
+  const size_t slot_bytes =
+      (size_t)r->block_tokens * r->heads * r->head_dim * elem_size(r->dtype);
+  *k_slot = static_cast<char*>(r->k_slots) + slot * slot_bytes;
+  *v_slot = static_cast<char*>(r->v_slots) + slot * slot_bytes;
   return LA_OK;
 }
 
@@ -214,6 +270,7 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
                    la_stream_t stream) {
   if (!r || !q_rot || !sink_k_rot || !k_cur_rot || !v_cur || !out) return LA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return LA_ERR_INVALID_ARG;
+  if (ring_slots(r) == 0) return LA_ERR_STATE;
   if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
   if (workspace && ((uintptr_t)workspace % 256)) return LA_ERR_INVALID_ARG;
   if (!valid_dtype(r->dtype)) return LA_ERR_DTYPE;
@@ -244,8 +301,9 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
   end += r->sink_tokens;
   segs.end[n++] = end;
   // cached blocks, oldest first
+  const int ns = ring_slots(r);
   for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b) {
-    const int slot = (int)((b - 1) % r->W);
+    const int slot = (int)((b - 1) % ns);
     segs.k[n] = static_cast<const char*>(r->k_slots) + slot * slot_bytes;
     segs.v[n] = static_cast<const char*>(r->v_slots) + slot * slot_bytes;
     end += r->block_tokens;
@@ -330,6 +388,7 @@ la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* 
   for (float x : f)
     if (!(x > 0.f) || !isfinite(x)) return LA_ERR_INVALID_ARG;
   if (r->dtype != LA_FP8_E4M3) return LA_ERR_DTYPE;
+  if (ring_slots(r) == 0) return LA_ERR_STATE;
   if (n_q != r->block_tokens || n_q < 1 || r->head_dim != 128) return LA_ERR_SHAPE;
   const void* ptrs[6] = {q8, sink_k8, sink_v8, k8_cur, v8_cur, out};
   for (const void* p : ptrs)
@@ -353,8 +412,9 @@ la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* 
   segs.v[n] = sink_v8;
   end += r->sink_tokens;
   segs.end[n++] = end;
+  const int ns = ring_slots(r);
   for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b) {
-    const int slot = (int)((b - 1) % r->W);
+    const int slot = (int)((b - 1) % ns);
     segs.k[n] = static_cast<const char*>(r->k_slots) + slot * slot_bytes;
     segs.v[n] = static_cast<const char*>(r->v_slots) + slot * slot_bytes;
     end += r->block_tokens;
@@ -381,11 +441,24 @@ la_status la_kvcache_append_evict(la_kvring* r, const void* k_rot, const void* v
   if (noise_level != r->noise_level) return LA_ERR_NOISE_LEVEL;
   const size_t slot_bytes =
       (size_t)r->block_tokens * r->heads * r->head_dim * elem_size(r->dtype);
-  const hipError_t e =
-      la::launch_copy2(static_cast<char*>(r->k_slots) + slot * slot_bytes, k_rot,
-                       static_cast<char*>(r->v_slots) + slot * slot_bytes, v, slot_bytes,
-                       static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_status(e);
+  char* kd = static_cast<char*>(r->k_slots) + slot * slot_bytes;
+  char* vd = static_cast<char*>(r->v_slots) + slot * slot_bytes;
+  // a half that is already in its slot (written there by the caller) is not copied
+  const void* ks = k_rot == kd ? nullptr : k_rot;
+  const void* vs = v == vd ? nullptr : v;
+  if (!ks) {
+    kd = vd;
+    ks = vs;
+    vd = nullptr;
+    vs = nullptr;
+  } else if (!vs) {
+    vd = nullptr;
+  }
+  if (ks) {
+    const hipError_t e =
+        la::launch_copy2(kd, ks, vd, vs, slot_bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e);
+  }
   r->slot_block[slot] = block_id;
   r->last_block = block_id;
   if (evicted_or_null) *evicted_or_null = evicted;
@@ -452,6 +525,7 @@ la_status validate_stage(const la_kvring* rings, int32_t n_layers, int64_t block
     return LA_ERR_SHAPE;
   for (int l = 0; l < n_layers; ++l) {
     const la_kvring& r = rings[l];
+    if (ring_slots(&r) == 0) return LA_ERR_STATE;
     if (r.W != r0.W || r.block_tokens != r0.block_tokens || r.sink_tokens != r0.sink_tokens ||
         r.heads != r0.heads || r.head_dim != r0.head_dim || r.dtype != r0.dtype)
       return LA_ERR_SHAPE;
@@ -494,19 +568,25 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
   } while (0)
   for (int l = 0; l < n_layers; ++l) {
     la_kvring* r = &rings[l];
+    // fused append: a staged ring takes the rotated K in its next slot directly
+    void* k_rot = k_rot_ws;
+    if (append && r->nslots == r->W + 1) {
+      void* v_slot;
+      LA_TRY(la_kvring_next_slot(r, &k_rot, &v_slot));
+    }
     LA_TRY(mark(6 * l));
-    LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
+    LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot, frames_per_block, f0,
                              r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
                              r->heads, r->head_dim, (la_dtype)r->dtype, theta, q_scale, stream));
     LA_TRY(mark(6 * l + 1));
     LA_TRY(mark(6 * l + 2));
-    LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot_ws, v_raw[l], r->block_tokens,
+    LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
                              attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes,
                              stream));
     LA_TRY(mark(6 * l + 3));
     LA_TRY(mark(6 * l + 4));
     if (append)
-      LA_TRY(la_kvcache_append_evict(r, k_rot_ws, v_raw[l], block_id, r->noise_level, nullptr,
+      LA_TRY(la_kvcache_append_evict(r, k_rot, v_raw[l], block_id, r->noise_level, nullptr,
                                      stream));
     if (append && block_id == 1 && sink_k_new)
       LA_TRY(la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream));

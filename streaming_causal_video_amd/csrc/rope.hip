@@ -41,11 +41,12 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // pass is issued, unpredicated (head indexes are clamped), before the first
 // rotation, so a thread keeps kNH 16-byte loads in flight; only the stores are
 // predicated.  The token is uniform, so addresses are a scalar row base plus a
-// 32-bit lane offset.  Loads are non-temporal (the raw inputs are dead after
-// this kernel); stores are ordinary, so the rotated Q and K the attention reads
-// next may still be in the cache (measured: 2 us faster per C2-shaped call than
-// non-temporal stores).  In-place calls are safe: a thread writes exactly the
-// chunks it read.
+// 32-bit lane offset.  Loads and stores are non-temporal: at a block's 224 MB the
+// rotated tensors do not stay in the caches for the attention anyway (measured per
+// C2-shaped call over buffers beyond the caches: 39.8 us against 42.6 us with
+// ordinary stores, and no change inside the step).  Neither one workgroup per
+// several rows nor more threads per row was faster (measured).  In-place calls are
+// safe: a thread writes exactly the chunks it read.
 template <bool kBF16, int kNH>
 __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTensor t1,
                                                           RopeTensor t2, RopeGeom g,
@@ -68,6 +69,19 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
   const size_t row_bytes = (size_t)g.heads * g.head_dim * kEB;
   const char* src = static_cast<const char*>(T.in) + (size_t)tok * row_bytes;
   char* dst = static_cast<char*>(T.out) + (size_t)tok * row_bytes;
+
+  u32x4_t x[kNH];
+  auto load_pass = [&](int h0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kNH; ++k) {
+      const int head = min(h0 + hg + k * hg_n, g.heads - 1);
+      const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
+      x[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + off));
+    }
+  };
+  // The first pass's loads go out before the cos/sin lookups, so that one memory
+  // latency covers both (the lookups' wait would otherwise come first).
+  load_pass(0);
 
   // cos/sin of this thread's kPPC pairs at (frame, h, w) of the token: the frame
   // band from the by-value rows, the h and w bands from the table (one load per
@@ -101,13 +115,7 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
   }
 
   for (int h0 = 0; h0 < g.heads; h0 += hg_n * kNH) {
-    u32x4_t x[kNH];
-#pragma unroll
-    for (int k = 0; k < kNH; ++k) {
-      const int head = min(h0 + hg + k * hg_n, g.heads - 1);
-      const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
-      x[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + off));
-    }
+    if (h0 > 0) load_pass(h0);
     // keep the loads together (the compiler would otherwise sink some of them,
     // and the rotations, into the predicated store blocks)
 #pragma unroll
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
       const int head = h0 + hg + k * hg_n;
       if (head < g.heads) {
         const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
-        *reinterpret_cast<u32x4_t*>(dst + off) = y[k];
+        __builtin_nontemporal_store(y[k], reinterpret_cast<u32x4_t*>(dst + off));
       }
     }
   }

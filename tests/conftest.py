@@ -24,3 +24,11 @@ def golden():
         with open(os.path.join(GOLDEN, name)) as f:
             return json.load(f)
     return load
+
+
+# A host-sanitizer run of the CPU tests loads an instrumented build of the library
+# instead of the in-tree one (tests/test_host_sanitizers.py sets this variable in the
+# child process it starts).
+if os.environ.get("LA_TEST_LIB_PATH"):
+    from streaming_causal_video_amd import _lib as _la_lib
+    _la_lib.LIB_PATH = os.environ["LA_TEST_LIB_PATH"]

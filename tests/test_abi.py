@@ -142,6 +142,76 @@ def test_init_validation():
     assert lib.la_kvring_init(ctypes.byref(r), p, p, p, p, 4, 48, 16, 2, 128, 0, float("nan")) == _lib.LA_ERR_INVALID_ARG
 
 
+def test_staged_ring_places_blocks_beyond_the_window():
+    """A staged ring (W + 1 slots) keeps the window's rules (the same evictions as the
+    oracle's deque) and puts block b in slot (b - 1) mod (W + 1), so the next block's
+    slot never holds a block of the window."""
+    W, bt, H, d = 3, 48, 2, 128
+    slot_bytes = bt * H * d * 2
+    r = L.la_kvring()
+    L.la_kvring_init_staged(r, 0x100000, 0x800000, 0x30000, 0x40000, W, bt, 16, H, d, L.LA_BF16,
+                            0.5)
+    assert r.W == W and r.nslots == W + 1
+    ref = Ring(W, 0.5)
+    lib = L.lib()
+    for b in range(1, 3 * W + 3):
+        k, v = L.la_kvring_next_slot(r)
+        slot, ev = L.la_kvring_advance(r, b)
+        assert slot == (b - 1) % (W + 1)
+        assert (k, v) == (0x100000 + slot * slot_bytes, 0x800000 + slot * slot_bytes)
+        held = [int(r.slot_block[s]) for s in range(W + 1)]
+        assert held[slot] == 0 or held[slot] <= b - 1 - W  # free: empty or already evicted
+        ref_ev = ref.append(b, None, None, 0.5)
+        assert ev == (ref_ev or 0)
+        # the host-side index update of an append whose K and V are already in place
+        # (no copy is enqueued: both halves are the destination slot itself)
+        evo = ctypes.c_int64()
+        assert lib.la_kvcache_append_evict(ctypes.byref(r), ctypes.c_void_p(k), ctypes.c_void_p(v),
+                                           b, 0.5, ctypes.byref(evo), None) == _lib.LA_OK
+        assert evo.value == ev and r.last_block == b
+        assert L.la_kvring_count(r) == min(b, W)
+        held = [int(r.slot_block[s]) for s in range(W + 1)]
+        assert sorted(x for x in held if x > max(b - W, 0)) == ref.ids()
+    # W + 1 slots must fit the slot table
+    p = ctypes.c_void_p(0x10000)
+    assert lib.la_kvring_init_staged(ctypes.byref(L.la_kvring()), p, p, p, p, 64, 48, 16, 2, 128,
+                                     0, 0.5) == _lib.LA_ERR_SHAPE
+    assert lib.la_kvring_init_staged(ctypes.byref(L.la_kvring()), p, p, p, p, 63, 48, 16, 2, 128,
+                                     0, 0.5) == _lib.LA_OK
+
+
+def test_next_slot_of_a_full_plain_ring_is_refused():
+    """A ring of W slots reuses the evicted block's slot, which the next block's
+    attention still reads: its next slot is handed out only while the window has room."""
+    r = make_ring(2)
+    k, v = L.la_kvring_next_slot(r)
+    assert (k, v) == (0x10000, 0x20000)
+    lib = L.lib()
+    evo = ctypes.c_int64()
+    for b in (1, 2):
+        k, v = L.la_kvring_next_slot(r)
+        assert lib.la_kvcache_append_evict(ctypes.byref(r), ctypes.c_void_p(k), ctypes.c_void_p(v),
+                                           b, 0.75, ctypes.byref(evo), None) == _lib.LA_OK
+    with pytest.raises(L.LAError) as e:
+        L.la_kvring_next_slot(r)
+    assert e.value.status == _lib.LA_ERR_STATE
+
+
+def test_corrupt_slot_count_is_refused():
+    r = make_ring(4)
+    before = bytes(r)
+    for bad in (0, 3, 6, 65):
+        r.nslots = bad
+        with pytest.raises(L.LAError) as e:
+            L.la_kvring_advance(r, 1)
+        assert e.value.status == _lib.LA_ERR_STATE
+        p = ctypes.c_void_p(0x70000)
+        assert L.lib().la_block_attn_fwd(ctypes.byref(r), p, p, p, p, 48, ctypes.c_void_p(0x80000),
+                                         None, 0.1, 1.0, None, 0, None) == _lib.LA_ERR_STATE
+    r.nslots = 4
+    assert bytes(r) == before
+
+
 def test_attention_argument_checks_before_launch():
     lib = L.lib()
     r = make_ring(2)
@@ -328,6 +398,19 @@ def test_attention_refuses_segments_beyond_32_bit_offsets():
     ok8 = ring(838_700, L.LA_FP8_E4M3)
     assert lib.la_block_attn_fwd_fp8(ctypes.byref(ok8), p, p, p, p, p, 838_699, out, None,
                                      0.1, 1.0, 1.0, 1.0, None) == _lib.LA_ERR_SHAPE
+
+
+def test_ring_slots_must_be_whole_16_byte_vectors():
+    """An e4m3 ring whose slot (block_tokens x heads x head_dim bytes) is not a multiple
+    of 16 bytes is refused: its appends could not copy whole vectors and later slots
+    would lose their 16-byte alignment.  The same geometry in bf16 is fine."""
+    p = [0x10000, 0x20000, 0x30000, 0x40000]
+    r = L.la_kvring()
+    with pytest.raises(L.LAError) as e:
+        L.la_kvring_init(r, *p, 2, 3, 2, 1, 8, L.LA_FP8_E4M3, 0.5)  # 24-byte slots
+    assert e.value.status == _lib.LA_ERR_SHAPE
+    L.la_kvring_init(r, *p, 2, 4, 2, 1, 8, L.LA_FP8_E4M3, 0.5)  # 32-byte slots
+    L.la_kvring_init(r, *p, 2, 3, 2, 1, 8, L.LA_BF16, 0.5)      # 48-byte slots
 
 
 def test_scale_and_workspace_refusals():

@@ -163,6 +163,49 @@ def test_append_evict_last_w_blocks_bit_exact(L, shape):
     assert ring.state.last_block == b
 
 
+@pytest.mark.parametrize("shape", [si.SMALL_BF16, si.SMALL_F32])
+def test_staged_append_takes_halves_already_in_place(L, shape):
+    """A staged ring (W + 1 slots) places block b in slot (b - 1) mod (W + 1); an append
+    whose K and/or V is the destination slot itself (written there beforehand, as the
+    fused step does with K) copies only the other half.  The window's bytes and ids
+    match the oracle's deque bit for bit for every mix of in-place halves."""
+    t = torch()
+    dt = t.bfloat16 if shape.dtype == "bf16" else t.float32
+    W = shape.W
+    ring = L.KVRing(W, shape.block_tokens, shape.sink_tokens, shape.heads, shape.head_dim, dt,
+                    NOISE_LEVEL, staged=True)
+    model = Ring(W, NOISE_LEVEL)
+    blocks = {}
+    view = np.uint16 if shape.dtype == "bf16" else np.float32
+    tv = t.int16 if view is np.uint16 else t.float32
+    for b in range(1, 3 * W + 4):
+        _, k, v = shape.block_inputs(0, b)
+        kd, vd = to_dev(k), to_dev(v)
+        blocks[b] = (k.storage, v.storage)
+        slot = (b - 1) % (W + 1)
+        kptr, vptr = L.la_kvring_next_slot(ring.state)
+        assert kptr == ring.k_slots[slot].data_ptr() and vptr == ring.v_slots[slot].data_ptr()
+        mode = b % 3  # 0: both in place, 1: K in place, 2: V in place
+        ksrc, vsrc = kd, vd
+        if mode in (0, 1):
+            ring.k_slots[slot].copy_(kd)
+            ksrc = ring.k_slots[slot]
+        if mode in (0, 2):
+            ring.v_slots[slot].copy_(vd)
+            vsrc = ring.v_slots[slot]
+        ev = L.la_kvcache_append_evict(ring.state, ksrc, vsrc, b, NOISE_LEVEL)
+        assert ev == (model.append(b, k.storage, v.storage, NOISE_LEVEL) or 0)
+        t.cuda.synchronize()
+        ks = ring.k_slots.view(tv).cpu().numpy().view(view)
+        vs = ring.v_slots.view(tv).cpu().numpy().view(view)
+        assert ring.count == len(model)
+        for bid in model.ids():
+            s_ = (bid - 1) % (W + 1)
+            assert int(ring.state.slot_block[s_]) == bid
+            np.testing.assert_array_equal(ks[s_], blocks[bid][0])
+            np.testing.assert_array_equal(vs[s_], blocks[bid][1])
+
+
 def test_append_full_size_c5(L):
     t = torch()
     s = si.C5

@@ -45,11 +45,12 @@ def test_c3_200_blocks_checked_at_1_50_200(L):
             assert ids == list(range(max(1, b - shape.W + 1), b + 1))
 
 
-def _stage(L, shape, n_layers):
+def _stage(L, shape, n_layers, staged=False):
     t = torch()
     s = shape
     stack = L.KVRingStack(n_layers, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim,
-                          t.bfloat16 if s.dtype == "bf16" else t.float32, NOISE_LEVEL)
+                          t.bfloat16 if s.dtype == "bf16" else t.float32, NOISE_LEVEL,
+                          staged=staged)
     for l in range(n_layers):
         sk, sv = s.initial_sink(l)
         stack.sink_k_raw[l].copy_(to_dev(sk))
@@ -103,6 +104,59 @@ def test_denoise_step_matches_oracle_and_per_op_path(L):
         np.testing.assert_array_equal(x.cpu().numpy(), x_ref.astype(np.float32))
     for l in range(n_layers):
         assert stack.states[l].last_block == 6 and stack.states[l].sink_replaced == 1
+
+
+@pytest.mark.parametrize("case", ["mid_3_layers", "c2_1_layer"])
+def test_staged_rings_fuse_the_append_with_the_same_bits(L, case):
+    """Staged rings (W + 1 slots): la_denoise_step writes each layer's rotated K straight
+    into the ring's next slot and copies only V.  Outputs, and every window block's K
+    and V bytes, equal those of the plain rings (which rotate into a workspace and copy
+    both) bit for bit, through the sink replacement and W + 2 evictions; the oracle
+    checks the outputs at three blocks."""
+    t = torch()
+    s = si.MID_BF16 if case == "mid_3_layers" else si.C2
+    n_layers = 3 if case == "mid_3_layers" else 1
+    plain, table = _stage(L, s, n_layers)
+    staged, _ = _stage(L, s, n_layers, staged=True)
+    blk = (s.block_tokens, s.heads, s.head_dim)
+    ws = [[t.empty(blk, dtype=t.bfloat16, device="cuda") for _ in range(n_layers)]
+          for _ in range(2)]
+    qws, kws = t.empty(blk, dtype=t.bfloat16, device="cuda"), t.empty(blk, dtype=t.bfloat16, device="cuda")
+    sws = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+    aws = L.AttnWorkspace(s.block_tokens, s.heads)
+    oracles = [StreamOracle(s, layer=l) for l in range(n_layers)]
+    nsink = s.sink_tokens
+    last = s.W + 3
+    for b in range(1, last + 1):
+        dev = [tuple(to_dev(z) for z in s.block_inputs(l, b)) for l in range(n_layers)]
+        for stack, outs in ((plain, ws[0]), (staged, ws[1])):
+            L.la_denoise_step(
+                stack.states, b, [d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev],
+                outs, qws, kws, sws, table, s.Hl, s.Wl, FRAMES_PER_BLOCK, SINK_DELTA, THETA,
+                scale=softmax_scale(s.head_dim), attn_ws=aws,
+                sink_k_new=[d[1][:nsink] for d in dev] if b == 1 else None,
+                sink_v_new=[d[2][:nsink] for d in dev] if b == 1 else None)
+        t.cuda.synchronize()
+        for l in range(n_layers):
+            assert t.equal(ws[0][l].view(t.int16), ws[1][l].view(t.int16)), (b, l)
+            for bid in range(max(1, b - s.W + 1), b + 1):
+                ps, ss = (bid - 1) % s.W, (bid - 1) % (s.W + 1)
+                assert int(plain.states[l].slot_block[ps]) == bid
+                assert int(staged.states[l].slot_block[ss]) == bid
+                for a, c in ((plain.k_slots, staged.k_slots), (plain.v_slots, staged.v_slots)):
+                    assert t.equal(a[l, ps].view(t.int16), c[l, ss].view(t.int16)), (b, l, bid)
+            if b in (1, 2, last) and (case == "mid_3_layers" or b == last):
+                if case == "mid_3_layers":
+                    check_attention(to_f64(ws[1][l]), oracles[l].block_output(b),
+                                    f"staged layer {l} block {b}")
+                else:
+                    rows = np.unique(np.concatenate([[0, s.block_tokens - 1],
+                                                     np.random.default_rng(b).integers(
+                                                         0, s.block_tokens, 48)]))
+                    ref, _ = oracle_block_all_heads(s, b, rows=rows)
+                    check_attention(to_f64(ws[1][l])[rows], ref, f"staged C2 block {b}")
+    for l in range(n_layers):
+        assert staged.states[l].last_block == last and staged.states[l].sink_replaced == 1
 
 
 def test_denoise_step_refuses_before_any_launch(L):
