@@ -368,9 +368,11 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
               st[b][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[b][nt], 0, 0, 0);
           }
         if (h == 0 && more) vload(1 - cur);
-        if (nvalid < BN) {
+        if (__builtin_expect(nvalid < BN, 0)) {
           // the last tile of a segment: row 4 g + i of block 2 h + b holds key
-          // 32 h + 8 g + 4 b + i of the tile
+          // 32 h + 8 g + 4 b + i of the tile.  Marked unlikely so that it stays a
+          // branch: otherwise the compiler turned the second half's masking into 32
+          // selects and compares on every tile.
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll

@@ -4,7 +4,10 @@ Usage:
     python -m streaming_causal_video_amd.profsum <results.db | kernel_trace.csv> [--last N]
 
 ``--last N`` restricts each kernel to its last N dispatches (the steady-state
-part of a streamed run, after the ring has filled).  Reads the SQLite database
+part of a streamed run, after the ring has filled); ``--slice A:B`` to its
+dispatches A..B-1 in launch order (for a run that launches the same kernel again
+after the part of interest, e.g. bench.py's standalone HBM timings after the
+step).  Reads the SQLite database
 that rocprofv3 writes by default or the CSV kernel trace of
 ``--output-format csv``.
 """
@@ -39,13 +42,15 @@ def load(path: str):
     return out
 
 
-def summarise(rows, last=None):
+def summarise(rows, last=None, window=None):
     by = {}
     for name, s, e in rows:
         by.setdefault(name, []).append((e - s) / 1e3)
     res = []
     for name, d in by.items():
-        sel = d[-last:] if last else d
+        sel = d[window[0]:window[1]] if window else (d[-last:] if last else d)
+        if not sel:
+            continue
         res.append((short_name(name), len(d), len(sel), sum(sel), statistics.mean(sel),
                     statistics.median(sel), min(sel), max(sel)))
     res.sort(key=lambda r: -r[3])
@@ -56,8 +61,10 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("trace")
     ap.add_argument("--last", type=int, default=None)
+    ap.add_argument("--slice", default=None, help="A:B, dispatches A..B-1 of each kernel")
     a = ap.parse_args(argv)
-    rows = summarise(load(a.trace), a.last)
+    window = tuple(int(x) for x in a.slice.split(":")) if a.slice else None
+    rows = summarise(load(a.trace), a.last, window)
     tot = sum(r[3] for r in rows)
     print(f"{'kernel':60s} {'calls':>6s} {'used':>5s} {'avg_us':>10s} {'median_us':>10s} "
           f"{'min_us':>9s} {'max_us':>9s} {'pct':>6s}")
