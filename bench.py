@@ -63,7 +63,10 @@ def attn_flops(nq, nk, d, h):
 
 
 # --------------------------------------------------------------------------- GPU
-def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
+FP8_SCALE = 5.0 / 448.0  # per-tensor e4m3 scale of Q, K and V: |x| = 5 maps to 448
+
+
+def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
     import torch
     import streaming_causal_video_amd as L
 
@@ -80,7 +83,8 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
     staged = args.ring == "staged"
     log(f"setup: {n_layers} layers, Hl={Hl} Wl={Wl} W={W} H={H} d={d}, Nq={bt} Nk={nk}, "
         f"{args.ring} rings")
-    stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.bfloat16, NOISE, staged=staged)
+    stack = L.KVRingStack(n_layers, W, bt, st, H, d, torch.uint8 if fp8 else torch.bfloat16, NOISE,
+                          staged=staged)
     for l in range(n_layers):
         stack.sink_k_raw[l].copy_(randn((st, H, d)))
         stack.sink_v[l].copy_(randn((st, H, d)))
@@ -92,7 +96,12 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
     sws = torch.empty((st, H, d), dtype=torch.bfloat16, device=dev)
     table = torch.empty(L.la_rope_table_bytes(Hl, Wl, d) // 4, dtype=torch.float32, device=dev)
     L.la_rope_table_fill(table, Hl, Wl, d, THETA)
-    aws = L.AttnWorkspace(bt, H) if args.attn_schedule == "balanced" else None
+    aws = L.AttnWorkspace(bt, H) if args.attn_schedule == "balanced" and not fp8 else None
+    if fp8:
+        u8 = lambda shp: torch.empty(shp, dtype=torch.uint8, device=dev)
+        q8 = u8((bt, H, d))
+        k8, v8 = (None, None) if staged else (u8((bt, H, d)), u8((bt, H, d)))
+        sk8, sv8 = u8((st, H, d)), u8((st, H, d))
     lat_shape = (16, 3, 60, 104)
     x = torch.randn(lat_shape, device=dev, generator=gen) if with_euler else None
     vels = [torch.randn(lat_shape, device=dev, generator=gen) for _ in range(pool)] if with_euler else None
@@ -105,6 +114,13 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
         v = [ins[e][l][2] for l in range(n_layers)]
         skn = [t[:st] for t in k] if b == 1 else None
         svn = [t[:st] for t in v] if b == 1 else None
+        if fp8:
+            L.la_denoise_step_fp8(stack.states, b, q, k, v, outs, qws, kws, sws, q8, k8, v8, sk8,
+                                  sv8, table, Hl, Wl, FRAMES, DELTA, THETA, scale=d ** -0.5,
+                                  dq=FP8_SCALE, dk=FP8_SCALE, dv=FP8_SCALE, sink_k_new=skn,
+                                  sink_v_new=svn, x=x, vel=vels[e] if with_euler else None,
+                                  dt=DT, timing_events=events)
+            return
         L.la_denoise_step(stack.states, b, q, k, v, outs, qws, kws, sws, table, Hl, Wl, FRAMES,
                           DELTA, THETA, scale=d ** -0.5, sink_k_new=skn, sink_v_new=svn, x=x,
                           vel=vels[e] if with_euler else None, dt=DT, timing_events=events,
@@ -160,6 +176,11 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True):
     rope_bytes = 2 * (2 * bt + st) * H * d * 2
     # the fused append (staged rings) copies V only: RoPE wrote K into the slot
     app_bytes = (1 if staged else 2) * 2 * bt * H * d * 2
+    if fp8:
+        # RoPE and the quantisation of Q, K, V, sink K and sink V (bf16 in, e4m3 out);
+        # a staged e4m3 ring takes K and V codes in place, so the append copies nothing
+        rope_bytes += (3 * bt + 2 * st) * H * d * 3
+        app_bytes = 0 if staged else 2 * 2 * bt * H * d
     res = {
         "ms_per_step": ms_step,
         "blocks_per_s": 1e3 / ms_step,
@@ -558,6 +579,52 @@ def fp8_main(args):
     return 0
 
 
+def c4fp8_main(args):
+    """--workload c4fp8: the C4 step on e4m3 rings (la_denoise_step_fp8): RoPE, one
+    quantisation launch, e4m3 attention, the append of K/V codes, Euler."""
+    geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
+    r = gpu_step_bench(args, fp8=True, **geo)
+    version = kernel_version("fp8-")
+    tf = r["attn_tflops"]
+    out = {
+        "metric": "denoise-step blocks/s at 1 GPU with e4m3 attention; % fp8 MFMA peak",
+        "value": round(r["blocks_per_s"], 4),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3",
+        "data": ("synthetic N(0,1) Q/K/V (bf16), sinks, latent and velocity resident in HBM; "
+                 "Q, K, V quantised to e4m3 with per-tensor scale 5/448"),
+        "config": {"workload": ("C4 denoise step on e4m3 rings: 40 layers x (3D Rolling RoPE + "
+                                "e4m3 quantisation + e4m3 block attention 40x128, Nq 4680, Nk "
+                                "24960 + ring append/evict, W=4) + Euler on fp32 16x3x60x104"),
+                   "layers": 40, "heads": 40, "head_dim": 128, "block_tokens": r["nq"],
+                   "nk": r["nk"], "rings": args.ring,
+                   "parallelism": "none (1 GPU = 1 stage)"},
+        "attn_tflops": round(tf, 2),
+        "attn_ms": round(r["attn_ms"], 4),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fp8_kernel", "kernel_version": version,
+                     "flop_per_launch": r["attn_flop_per_launch"]},
+        "streaming_kernels": {
+            "method": ("in the step: HIP events around each launch, mean over layers and timed "
+                       "steps (includes the gap between launches)"),
+            "rope_and_quantise_us": round(r["rope_us"], 2),
+            "rope_and_quantise_GBps": round(r["rope_gbs"], 1),
+            "append_us": round(r["append_us"], 2), "append_bytes": r["append_bytes"],
+            "euler_us": round(r["euler_us"], 2),
+        },
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def gpu_refresh_bench(args, Hl, Wl, W, H, d, n_layers, n_steps=4):
     """The clean-cache baseline the pipeline replaces (NFE 5): per block, n_steps denoise
     passes attend to one shared clean cache without writing it (LA_STEP_ATTEND_ONLY), then a
@@ -680,7 +747,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["c4", "c2", "c3", "c5", "chain", "c2fp8", "refresh"],
+    ap.add_argument("--workload", choices=["c4", "c2", "c3", "c5", "chain", "c2fp8", "c4fp8",
+                                           "refresh"],
                     default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0,
@@ -708,6 +776,8 @@ def main():
         return fp8_main(args)
     if args.workload == "refresh":
         return refresh_main(args)
+    if args.workload == "c4fp8":
+        return c4fp8_main(args)
     if args.workload == "c4":
         geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
         name = ("C4 full denoise step: 40 layers x (3D Rolling RoPE + bf16 block attention "

@@ -404,6 +404,45 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
 #define LA_STEP_ATTEND_ONLY 1u
 
 /*
+ * la_denoise_step_fp8 - la_denoise_step with the attention on e4m3 operands, for
+ * rings of dtype LA_FP8_E4M3 (NOTES, Table 3: FP8 quantisation together with
+ * FlashAttention-3 and fused kernels).  For every layer l, in order, on `stream`:
+ *   1. la_rope3d_rolling as in la_denoise_step, bf16 out (no Q pre-scale), into
+ *      q_rot_ws, k_rot_ws and sink_k_rot_ws;
+ *   2. one launch quantises five bf16 tensors, each with its own per-tensor
+ *      scale as la_quantize_fp8 does (code = E4M3(x * fl32(1 / d))): the rotated
+ *      Q into q8_ws (dq), the rotated K (dk) and v_raw[l] (dv) into the ring's next
+ *      slot when the ring is staged and the step appends (else into k8_ws and
+ *      v8_ws), the rotated sink K into sink_k8_ws (dk) and the ring's sink V into
+ *      sink_v8_ws (dv);
+ *   3. la_block_attn_fwd_fp8 of these codes with (dq, dk, dv) and `scale` into
+ *      attn_out[l] (bf16);
+ *   4. la_kvcache_append_evict of the block's K and V codes as block block_id
+ *      (nothing is copied when they are already in the slot), and at block 1 the
+ *      sink replacement, as in la_denoise_step;
+ * then la_fm_euler_step(x, vel, n_latent, dt) if x != NULL.
+ * Every ring is LA_FP8_E4M3 with head_dim 128 (else LA_ERR_DTYPE / LA_ERR_SHAPE);
+ * dq, dk, dv finite and > 0 (else LA_ERR_INVALID_ARG).  Workspaces, 16-byte
+ * aligned, caller-owned: q8_ws, k8_ws, v8_ws [block_tokens][heads][head_dim]
+ * bytes (k8_ws and v8_ws may be NULL when every ring is staged and flags lacks
+ * LA_STEP_ATTEND_ONLY), sink_k8_ws and sink_v8_ws [sink_tokens][heads][head_dim]
+ * bytes; q_rot_ws, k_rot_ws and sink_k_rot_ws bf16 as in la_denoise_step.  The
+ * other arguments, flags, timing events (the quantisation is timed with RoPE)
+ * and errors are those of la_denoise_step (it takes no attention workspace).
+ */
+la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_id,
+                              const void* const* q_raw, const void* const* k_raw,
+                              const void* const* v_raw, void* const* attn_out, void* q_rot_ws,
+                              void* k_rot_ws, void* sink_k_rot_ws, void* q8_ws, void* k8_ws,
+                              void* v8_ws, void* sink_k8_ws, void* sink_v8_ws,
+                              const void* const* sink_k_new, const void* const* sink_v_new,
+                              const void* rope_table, int32_t Hl, int32_t Wl,
+                              int32_t frames_per_block, int64_t sink_delta, double theta,
+                              float scale, float dq, float dk, float dv, float* x,
+                              const float* vel, int64_t n_latent, float dt, uint32_t flags,
+                              void* const* timing_events, la_stream_t stream);
+
+/*
  * la_quantize_fp8 - per-tensor FP8 quantisation (NOTES, Table 3: FP8
  * quantisation).  out[i] = E4M3(in[i] * inv_scale) for 0 <= i < n, where the
  * product is one float32 multiplication and E4M3 rounds to the nearest

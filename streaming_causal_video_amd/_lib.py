@@ -28,7 +28,7 @@ EXPORTED = [
     "la_kvring_init_staged", "la_kvring_advance", "la_kvring_next_slot", "la_kvring_count", "la_rope_table_bytes", "la_rope_table_fill", "la_rope3d_rolling",
     "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
     "la_denoise_step", "la_denoise_chain", "la_quantize_fp8", "la_block_attn_fwd_fp8",
-    "la_attn_workspace_bytes", "la_block_attn_fwd_noalloc",
+    "la_attn_workspace_bytes", "la_block_attn_fwd_noalloc", "la_denoise_step_fp8",
 ]
 
 
@@ -143,6 +143,10 @@ def _load():
         "la_denoise_step": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP, VP,
                                            P(VP), P(VP), VP, I32, I32, I32, I64, D, F, VP, SZ,
                                            VP, VP, I64, F, ctypes.c_uint32, P(VP), VP]),
+        "la_denoise_step_fp8": (ctypes.c_int, [R, I32, I64, P(VP), P(VP), P(VP), P(VP), VP, VP,
+                                               VP, VP, VP, VP, VP, VP, P(VP), P(VP), VP, I32,
+                                               I32, I32, I64, D, F, F, F, F, VP, VP, I64, F,
+                                               ctypes.c_uint32, P(VP), VP]),
         "la_quantize_fp8": (ctypes.c_int, [VP, ctypes.c_int, VP, I64, F, VP]),
         "la_block_attn_fwd_fp8": (ctypes.c_int, [R, VP, VP, VP, VP, VP, I32, VP, VP, F, F, F, F,
                                                  VP]),
@@ -499,6 +503,60 @@ def la_denoise_step(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_w
         skn, svn, _ptr(rope_table, "rope_table"), Hl, Wl, frames_per_block, sink_delta, theta,
         scale, ws_p, ws_n, _ptr(x, "x"), _ptr(vel, "vel"), n_lat, dt, flags, timing_events,
         _stream()), "la_denoise_step")
+
+
+def la_denoise_step_fp8(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_rot_ws, k_rot_ws,
+                        sink_k_rot_ws, q8_ws, k8_ws, v8_ws, sink_k8_ws, sink_v8_ws, rope_table,
+                        Hl: int, Wl: int, frames_per_block: int = 3, sink_delta: int = -1,
+                        theta: float = 10000.0, *, scale: float, dq: float, dk: float,
+                        dv: float, sink_k_new=None, sink_v_new=None, x=None, vel=None,
+                        dt: float = -0.25, timing_events=None, flags: int = 0) -> None:
+    """la_denoise_step for e4m3 rings (KVRingStack(..., torch.uint8)): bf16 activations,
+    uint8 code workspaces (k8_ws / v8_ws may be None when the rings are staged and the
+    step appends).  dq, dk, dv: the per-tensor dequantisation scales."""
+    torch = _torch()
+    n = len(rings)
+    if n < 1:
+        raise ValueError("rings is empty")
+    r0 = rings[0]
+    if r0.dtype != LA_FP8_E4M3:
+        raise ValueError("la_denoise_step_fp8 runs e4m3 rings only")
+    bf, u8 = torch.bfloat16, torch.uint8
+    blk = (r0.block_tokens, r0.heads, r0.head_dim)
+    snk = (r0.sink_tokens, r0.heads, r0.head_dim)
+    for ts, name in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (attn_out, "attn_out")):
+        _check_list(ts, name, blk, bf, n)
+    for ts, name in ((sink_k_new, "sink_k_new"), (sink_v_new, "sink_v_new")):
+        if ts is not None:
+            _check_list(ts, name, snk, bf, n)
+    for t, name, shp, dt_ in ((q_rot_ws, "q_rot_ws", blk, bf), (k_rot_ws, "k_rot_ws", blk, bf),
+                              (sink_k_rot_ws, "sink_k_rot_ws", snk, bf), (q8_ws, "q8_ws", blk, u8),
+                              (sink_k8_ws, "sink_k8_ws", snk, u8),
+                              (sink_v8_ws, "sink_v8_ws", snk, u8)):
+        _check_tensor(t, name, shp, dt_)
+    for t, name in ((k8_ws, "k8_ws"), (v8_ws, "v8_ws")):
+        if t is not None:
+            _check_tensor(t, name, blk, u8)
+    n_lat = 0 if x is None else x.numel()
+    if x is not None:
+        if vel is None or vel.numel() != n_lat:
+            raise ValueError("vel must match x")
+        if x.dtype != torch.float32 or vel.dtype != torch.float32:
+            raise ValueError("x and vel must be float32")
+    if timing_events is not None and len(timing_events) != 6 * n + 2:
+        raise ValueError(f"timing_events needs {6 * n + 2} events")
+    _check_table(rope_table, Hl, Wl, r0.head_dim)
+    skn = _ptr_array(sink_k_new, "sink_k_new", snk, bf, n) if sink_k_new is not None else None
+    svn = _ptr_array(sink_v_new, "sink_v_new", snk, bf, n) if sink_v_new is not None else None
+    _check(_load().la_denoise_step_fp8(
+        rings, n, block_id, _ptr_array(q_raw, "q_raw", blk, bf, n),
+        _ptr_array(k_raw, "k_raw", blk, bf, n), _ptr_array(v_raw, "v_raw", blk, bf, n),
+        _ptr_array(attn_out, "attn_out", blk, bf, n), _ptr(q_rot_ws, "q_rot_ws"),
+        _ptr(k_rot_ws, "k_rot_ws"), _ptr(sink_k_rot_ws, "sink_k_rot_ws"), _ptr(q8_ws, "q8_ws"),
+        _ptr(k8_ws, "k8_ws"), _ptr(v8_ws, "v8_ws"), _ptr(sink_k8_ws, "sink_k8_ws"),
+        _ptr(sink_v8_ws, "sink_v8_ws"), skn, svn, _ptr(rope_table, "rope_table"), Hl, Wl,
+        frames_per_block, sink_delta, theta, scale, dq, dk, dv, _ptr(x, "x"), _ptr(vel, "vel"),
+        n_lat, dt, flags, timing_events, _stream()), "la_denoise_step_fp8")
 
 
 def la_denoise_chain(stages, block_id: int, q_rot_ws, k_rot_ws, sink_k_rot_ws, rope_table,

@@ -510,7 +510,8 @@ la_status validate_stage(const la_kvring* rings, int32_t n_layers, int64_t block
                          const void* const* q_raw, const void* const* k_raw,
                          const void* const* v_raw, void* const* attn_out,
                          const void* const* sink_k_new, const void* const* sink_v_new,
-                         int32_t Hl, int32_t Wl, int32_t frames_per_block, uint32_t flags) {
+                         int32_t Hl, int32_t Wl, int32_t frames_per_block, uint32_t flags,
+                         bool fp8 = false) {
   if (!rings || n_layers < 1 || !q_raw || !k_raw || !v_raw || !attn_out)
     return LA_ERR_INVALID_ARG;
   if ((!sink_k_new) != (!sink_v_new)) return LA_ERR_INVALID_ARG;
@@ -519,7 +520,12 @@ la_status validate_stage(const la_kvring* rings, int32_t n_layers, int64_t block
   if (frames_per_block < 1 || frames_per_block > LA_MAX_BLOCK_FRAMES || Hl < 1 || Wl < 1)
     return LA_ERR_SHAPE;
   const la_kvring& r0 = rings[0];
-  if (!valid_dtype(r0.dtype)) return LA_ERR_DTYPE;  // the step runs bf16 / f32 rings
+  if (fp8) {
+    if (r0.dtype != LA_FP8_E4M3) return LA_ERR_DTYPE;
+    if (r0.head_dim != 128) return LA_ERR_SHAPE;
+  } else if (!valid_dtype(r0.dtype)) {
+    return LA_ERR_DTYPE;  // la_denoise_step runs bf16 / f32 rings
+  }
   if ((int64_t)r0.block_tokens != (int64_t)frames_per_block * Hl * Wl ||
       (int64_t)r0.sink_tokens != (int64_t)Hl * Wl)
     return LA_ERR_SHAPE;
@@ -629,6 +635,96 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
                        k_rot_ws, sink_k_rot_ws, sink_k_new, sink_v_new, rope_table, Hl, Wl,
                        frames_per_block, sink_delta, theta, scale, attn_ws, attn_ws_bytes, x, vel,
                        n_latent, dt, flags, timing_events, stream);
+}
+
+la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_id,
+                              const void* const* q_raw, const void* const* k_raw,
+                              const void* const* v_raw, void* const* attn_out, void* q_rot_ws,
+                              void* k_rot_ws, void* sink_k_rot_ws, void* q8_ws, void* k8_ws,
+                              void* v8_ws, void* sink_k8_ws, void* sink_v8_ws,
+                              const void* const* sink_k_new, const void* const* sink_v_new,
+                              const void* rope_table, int32_t Hl, int32_t Wl,
+                              int32_t frames_per_block, int64_t sink_delta, double theta,
+                              float scale, float dq, float dk, float dv, float* x,
+                              const float* vel, int64_t n_latent, float dt, uint32_t flags,
+                              void* const* timing_events, la_stream_t stream) {
+  // ---- validate the whole step before enqueuing anything
+  if (!q_rot_ws || !k_rot_ws || !sink_k_rot_ws || !rope_table || !q8_ws || !sink_k8_ws ||
+      !sink_v8_ws)
+    return LA_ERR_INVALID_ARG;
+  const la_status v = validate_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out,
+                                     sink_k_new, sink_v_new, Hl, Wl, frames_per_block, flags,
+                                     true);
+  if (v != LA_OK) return v;
+  const bool append = !(flags & LA_STEP_ATTEND_ONLY);
+  for (int l = 0; l < n_layers; ++l)
+    if (!(append && rings[l].nslots == rings[l].W + 1) && (!k8_ws || !v8_ws))
+      return LA_ERR_INVALID_ARG;  // a plain ring (or no append) needs the K/V code workspaces
+  const float f[4] = {scale, dq, dk, dv};
+  for (float z : f)
+    if (!(z > 0.f) || !isfinite(z)) return LA_ERR_INVALID_ARG;
+  const void* ws[5] = {q8_ws, k8_ws, v8_ws, sink_k8_ws, sink_v8_ws};
+  for (const void* p : ws)
+    if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+  if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
+  if (timing_events)
+    for (int i = 0; i < 6 * n_layers + 2; ++i)
+      if (!timing_events[i]) return LA_ERR_INVALID_ARG;
+
+  const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> la_status {
+    if (!timing_events) return LA_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(timing_events[i]), hs));
+  };
+  // the reciprocals the quantisation multiplies by, as la_quantize_fp8 takes them
+  const float iq = 1.0f / dq, ik = 1.0f / dk, iv = 1.0f / dv;
+#define LA_TRY(expr)                 \
+  do {                               \
+    const la_status st_ = (expr);    \
+    if (st_ != LA_OK) return st_;    \
+  } while (0)
+  for (int l = 0; l < n_layers; ++l) {
+    la_kvring* r = &rings[l];
+    const int64_t blk = (int64_t)r->block_tokens * r->heads * r->head_dim;
+    const int64_t snk = (int64_t)r->sink_tokens * r->heads * r->head_dim;
+    void* k8 = k8_ws;
+    void* v8 = v8_ws;
+    if (append && r->nslots == r->W + 1) LA_TRY(la_kvring_next_slot(r, &k8, &v8));
+    LA_TRY(mark(6 * l));
+    LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
+                             r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
+                             r->heads, r->head_dim, LA_BF16, theta, 1.0f, stream));
+    la::QuantJobs jobs = {};
+    const void* ins[5] = {q_rot_ws, k_rot_ws, v_raw[l], sink_k_rot_ws, r->sink_v};
+    void* outs[5] = {q8_ws, k8, v8, sink_k8_ws, sink_v8_ws};
+    const int64_t ns[5] = {blk, blk, blk, snk, snk};
+    const float invs[5] = {iq, ik, iv, ik, iv};
+    for (int j = 0; j < 5; ++j) {
+      jobs.in[j] = ins[j];
+      jobs.out[j] = outs[j];
+      jobs.n[j] = ns[j];
+      jobs.inv[j] = invs[j];
+    }
+    jobs.count = 5;
+    LA_TRY(hip_status(la::launch_quantize_fp8_many(jobs, hs)));
+    LA_TRY(mark(6 * l + 1));
+    LA_TRY(mark(6 * l + 2));
+    LA_TRY(la_block_attn_fwd_fp8(r, q8_ws, sink_k8_ws, sink_v8_ws, k8, v8, r->block_tokens,
+                                 attn_out[l], nullptr, scale, dq, dk, dv, stream));
+    LA_TRY(mark(6 * l + 3));
+    LA_TRY(mark(6 * l + 4));
+    if (append)
+      LA_TRY(la_kvcache_append_evict(r, k8, v8, block_id, r->noise_level, nullptr, stream));
+    if (append && block_id == 1 && sink_k_new)
+      LA_TRY(la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream));
+    LA_TRY(mark(6 * l + 5));
+  }
+  LA_TRY(mark(6 * n_layers));
+  if (x && n_latent > 0) LA_TRY(la_fm_euler_step(x, vel, n_latent, dt, stream));
+  LA_TRY(mark(6 * n_layers + 1));
+#undef LA_TRY
+  return LA_OK;
 }
 
 la_status la_denoise_chain(la_stage* stages, int32_t n_stages, int32_t n_layers,

@@ -73,6 +73,17 @@ hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs&
                            hipStream_t s);
 hipError_t launch_quantize_fp8(const void* in, int in_dtype, void* out, int64_t n, float inv_scale,
                                hipStream_t s);
+// Several bf16 tensors to e4m3 in one launch (one grid row per tensor); every n is a
+// multiple of 16 and every pointer 16-byte aligned.
+constexpr int kMaxQuantJobs = 6;
+struct QuantJobs {
+  const void* in[kMaxQuantJobs];
+  void* out[kMaxQuantJobs];
+  int64_t n[kMaxQuantJobs];
+  float inv[kMaxQuantJobs];
+  int32_t count;
+};
+hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s);
 // la_block_attn_fwd with its workspace given explicitly: slot_cap > 0 limits the
 // persistent grid to that many workgroups; clear_counters zeroes the arrival counters
 // (with a small fill kernel) before the launch.

@@ -178,6 +178,31 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const void* __restr
   }
 }
 
+// The bf16 tensors of QuantJobs, each a multiple of 16 elements: grid row y is
+// tensor y, a bounded grid of workgroups loops over its 16-element chunks with the
+// element arithmetic of quant_fp8_kernel (so the codes are the same bits).
+__global__ __launch_bounds__(kThreads) void quant_fp8_many_kernel(QuantJobs jobs) {
+  const int j = blockIdx.y;
+  const u32x4_t* __restrict__ in = static_cast<const u32x4_t*>(jobs.in[j]);
+  uint4* __restrict__ out = static_cast<uint4*>(jobs.out[j]);
+  const int64_t n16 = jobs.n[j] / 16;
+  const float inv = jobs.inv[j];
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads) {
+    const u32x4_t a = __builtin_nontemporal_load(in + 2 * i);
+    const u32x4_t b = __builtin_nontemporal_load(in + 2 * i + 1);
+    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16) * inv;
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * inv;
+    }
+    out[i] = make_uint4(e4m3x4(x[0], x[1], x[2], x[3]), e4m3x4(x[4], x[5], x[6], x[7]),
+                        e4m3x4(x[8], x[9], x[10], x[11]), e4m3x4(x[12], x[13], x[14], x[15]));
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads)
@@ -208,6 +233,21 @@ hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size
   hipLaunchKernelGGL(copy2_kernel, grid, dim3(kThreads), 0, s, static_cast<u32x4_t*>(d0),
                      static_cast<const u32x4_t*>(s0), static_cast<u32x4_t*>(d1),
                      static_cast<const u32x4_t*>(s1), n16, tail);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s) {
+  if (jobs.count < 1 || jobs.count > kMaxQuantJobs) return hipErrorInvalidValue;
+  int64_t most = 0;
+  for (int j = 0; j < jobs.count; ++j) {
+    if (jobs.n[j] % 16 != 0) return hipErrorInvalidValue;
+    most = jobs.n[j] > most ? jobs.n[j] : most;
+  }
+  if (most == 0) return hipSuccess;
+  int64_t wgs = (most / 16 + kThreads - 1) / kThreads;
+  if (wgs > 2048) wgs = 2048;
+  hipLaunchKernelGGL(quant_fp8_many_kernel, dim3((unsigned)wgs, jobs.count), dim3(kThreads), 0,
+                     s, jobs);
   return hipGetLastError();
 }
 

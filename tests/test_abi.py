@@ -495,3 +495,45 @@ def test_step_wrapper_checks_every_tensor():
                  attn_out=[blk(), snk()], dt=-0.25)
     with pytest.raises(ValueError, match="stages\\[0\\]\\.attn_out\\[1\\] has shape"):
         L.la_denoise_chain([stage], 1, blk(), blk(), snk(), table, Hl, Wl, scale=0.1)
+
+
+def test_fp8_step_refusals_change_nothing():
+    """la_denoise_step_fp8 validates before any launch: e4m3 rings only (and
+    la_denoise_step refuses them), head_dim 128, positive finite scales, the K/V code
+    workspaces for plain rings, 16-byte aligned workspaces."""
+    lib = L.lib()
+    Hl = Wl = 4
+    n = 2
+
+    def rings_of(dtype, d=128, staged=False):
+        rings = (_lib.la_kvring * n)()
+        init = L.la_kvring_init_staged if staged else L.la_kvring_init
+        for l in range(n):
+            init(rings[l], 0x100000, 0x200000, 0x300000, 0x400000, 2, 3 * Hl * Wl, Hl * Wl, 2, d,
+                 dtype, 0.5)
+        return rings
+
+    arrs = [(ctypes.c_void_p * n)(*[0x1000000 * (i + 1) + 0x10000 * l for l in range(n)])
+            for i in range(4)]
+    p = ctypes.c_void_p(0x9000000)
+
+    def call(rings, k8=p, v8=p, q8=p, dq=0.01, flags=0):
+        return lib.la_denoise_step_fp8(rings, n, 1, *arrs, p, p, p, q8, k8, v8, p, p, None, None,
+                                       p, Hl, Wl, 3, -1, 1e4, 0.1, dq, 0.01, 0.01, None, None, 0,
+                                       -0.25, flags, None, None)
+
+    r8 = rings_of(L.LA_FP8_E4M3)
+    before = bytes(r8)
+    assert call(rings_of(L.LA_BF16)) == _lib.LA_ERR_DTYPE
+    assert call(rings_of(L.LA_FP8_E4M3, d=64)) == _lib.LA_ERR_SHAPE
+    assert call(r8, dq=0.0) == _lib.LA_ERR_INVALID_ARG
+    assert call(r8, dq=float("inf")) == _lib.LA_ERR_INVALID_ARG
+    assert call(r8, k8=None) == _lib.LA_ERR_INVALID_ARG          # plain ring: K codes need k8_ws
+    assert call(rings_of(L.LA_FP8_E4M3, staged=True), k8=None, v8=None,
+                flags=L.LA_STEP_ATTEND_ONLY) == _lib.LA_ERR_INVALID_ARG  # no append: needs them
+    assert call(r8, q8=ctypes.c_void_p(0x9000008)) == _lib.LA_ERR_INVALID_ARG  # misaligned
+    assert call(r8, flags=4) == _lib.LA_ERR_INVALID_ARG
+    assert bytes(r8) == before
+    # and the bf16 step refuses e4m3 rings
+    assert lib.la_denoise_step(r8, n, 1, *arrs, p, p, p, None, None, p, Hl, Wl, 3, -1, 1e4, 0.1,
+                               None, 0, None, None, 0, -0.25, 0, None, None) == _lib.LA_ERR_DTYPE

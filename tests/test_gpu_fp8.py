@@ -293,3 +293,106 @@ def test_fp8_attention_c5_sampled(L):
             check_lse(got_lse, lse, fs.lse_bar, f"fp8 C5 block {b}")
             say(f"fp8 C5 block {b}: rel-L2 {r:.4f}")
             say(f"fp8 C5 block {b}: rel-L2 {r:.4f}")
+
+
+# ------------------------------------------------------------------ the e4m3 step
+def _bf16(x):
+    """Round float64 values to bf16 (nearest even), as the step's activations are."""
+    return si.make_stored(x, "bf16").values
+
+
+def oracle_fp8_step_block(shape, layer, b, dq, dk, dv):
+    """The e4m3 step's attention for block b of one layer, from the definitions: each
+    operand rotated exactly (rotations as in StreamOracle), rounded to bf16 like the
+    step's activations, quantised with its own scale; the window's blocks the same way
+    at their own positions.  Returns (out, lse, bound_a, vmax, codes of K and V of b)."""
+    from oracle import StreamOracle, attention_lse
+    so = StreamOracle(shape, layer=layer)
+    q_raw, k_raw, v = so.raw_block(b)
+    f32 = np.float32
+    q8 = quantize(_bf16(so.rot_block(q_raw, b)).astype(f32), dq)
+    k8 = quantize(_bf16(so.rot_block(k_raw, b)).astype(f32), dk)
+    v8 = quantize(v.astype(f32), dv)
+    sk_raw, sv = so.sink_for(b)
+    keys = [quantize(_bf16(so.rot_sink(sk_raw, b)).astype(f32), dk)]
+    vals = [quantize(sv.astype(f32), dv)]
+    for b2 in so.window_ids(b):
+        _, k2, v2 = so.raw_block(b2)
+        keys.append(quantize(_bf16(so.rot_block(k2, b2)).astype(f32), dk))
+        vals.append(quantize(v2.astype(f32), dv))
+    keys.append(k8)
+    vals.append(v8)
+    K8, V8 = np.concatenate(keys), np.concatenate(vals)
+    scale = shape.head_dim ** -0.5
+    out, lse = attention_fp8(q8, K8, V8, dq, dk, dv, scale)
+    absv = np.abs(dequantize(V8, dv))
+    bound_a, _ = attention_lse(dequantize(q8, dq), dequantize(K8, dk), absv, scale)
+    return out, lse, bound_a, absv.max(), (k8, v8)
+
+
+def test_fp8_denoise_step_matches_oracle(L):
+    """la_denoise_step_fp8 over 2 layers and W + 2 blocks (sink replacement after block 1,
+    evictions, an Euler step per block): each layer's output against the oracle's e4m3
+    attention of the rotated, bf16-rounded and quantised operands (the fp8 bars above);
+    staged rings give the same bits as plain ones; the window's K/V codes equal the
+    oracle's except where RoPE's bf16 rounding differs by one ulp (then by one code)."""
+    t = torch()
+    s = si.SMALL_BF16
+    n_layers = 2
+    dq = dk = dv = SCALE_QKV
+    stacks = {}
+    for mode in ("staged", "plain"):
+        st = L.KVRingStack(n_layers, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim,
+                           t.uint8, 0.75, staged=(mode == "staged"))
+        for l in range(n_layers):
+            sk, sv = s.initial_sink(l)
+            st.sink_k_raw[l].copy_(to_dev(sk))
+            st.sink_v[l].copy_(to_dev(sv))
+        stacks[mode] = st
+    blk, snk = (s.block_tokens, s.heads, s.head_dim), (s.sink_tokens, s.heads, s.head_dim)
+    bf = lambda shp: t.empty(shp, dtype=t.bfloat16, device="cuda")
+    u8 = lambda shp: t.empty(shp, dtype=t.uint8, device="cuda")
+    table = t.empty(L.la_rope_table_bytes(s.Hl, s.Wl, s.head_dim) // 4, dtype=t.float32,
+                    device="cuda")
+    L.la_rope_table_fill(table, s.Hl, s.Wl, s.head_dim, 10000.0)
+    outs = {m: [bf(blk) for _ in range(n_layers)] for m in stacks}
+    lat = si.latent(s.cfg_id, 0, si.TID_X, (2, 3, 4, 5))
+    xs = {m: to_dev(lat) for m in stacks}
+    nsink = s.sink_tokens
+    for b in range(1, s.W + 3):
+        dev = [tuple(to_dev(z) for z in s.block_inputs(l, b)) for l in range(n_layers)]
+        vel = to_dev(si.latent(s.cfg_id, b, si.TID_VEL, (2, 3, 4, 5)))
+        for m, st in stacks.items():
+            L.la_denoise_step_fp8(
+                st.states, b, [d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev],
+                outs[m], bf(blk), bf(blk), bf(snk), u8(blk),
+                None if m == "staged" else u8(blk), None if m == "staged" else u8(blk),
+                u8(snk), u8(snk), table, s.Hl, s.Wl, 3, -1, 10000.0,
+                scale=s.head_dim ** -0.5, dq=dq, dk=dk, dv=dv,
+                sink_k_new=[d[1][:nsink] for d in dev] if b == 1 else None,
+                sink_v_new=[d[2][:nsink] for d in dev] if b == 1 else None,
+                x=xs[m], vel=vel, dt=-0.25)
+        t.cuda.synchronize()
+        for l in range(n_layers):
+            assert t.equal(outs["staged"][l].view(t.int16), outs["plain"][l].view(t.int16)), (b, l)
+            out, lse, a, vmax, (k8, v8) = oracle_fp8_step_block(s, l, b, dq, dk, dv)
+            r = check_fp8(to_f64(outs["staged"][l]), out, a, vmax, f"fp8 step layer {l} block {b}")
+            for m, st in stacks.items():
+                slot = (b - 1) % st.states[l].nslots
+                assert int(st.states[l].slot_block[slot]) == b
+                gk = st.k_slots[l, slot].cpu().numpy()
+                gv = st.v_slots[l, slot].cpu().numpy()
+                assert np.array_equal(gv, v8), f"{m} block {b} layer {l}: V codes differ"
+                diff = gk != k8
+                assert diff.mean() <= 1e-3, f"{m} block {b} layer {l}: {diff.sum()} K codes differ"
+                # a differing code is a neighbour of the oracle's: one bf16 ulp before the
+                # quantisation moves a value across at most one e4m3 rounding boundary
+                step_ = np.abs(dequantize(gk[diff], dk) - dequantize(k8[diff], dk))
+                ref_ = np.abs(dequantize(k8[diff], dk))
+                assert (step_ <= ref_ * 2.0 ** -2 + 2.0 ** -9 * dk).all(), m
+            say(f"fp8 step layer {l} block {b}: rel-L2 {r:.4f}, K codes differing from the "
+                f"oracle's {int(diff.sum())} of {diff.size}")
+    assert t.equal(xs["staged"], xs["plain"])
+    for m, st in stacks.items():
+        for l in range(n_layers):
+            assert st.states[l].last_block == s.W + 2 and st.states[l].sink_replaced == 1
