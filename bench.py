@@ -613,8 +613,8 @@ def c4fp8_main(args):
                      "traffic": None, "kernel": "attn_fp8_kernel", "kernel_version": version,
                      "flop_per_launch": r["attn_flop_per_launch"]},
         "streaming_kernels": {
-            "method": ("in the step: HIP events around each launch, mean over layers and timed "
-                       "steps (includes the gap between launches)"),
+            "method": ("in the step: each kernel's own begin and end timestamps (HIP events "
+                       "given to its launch), mean over layers and timed steps"),
             "rope_and_quantise_us": round(r["rope_us"], 2),
             "rope_and_quantise_GBps": round(r["rope_gbs"], 1),
             "append_us": round(r["append_us"], 2), "append_bytes": r["append_bytes"],
@@ -834,8 +834,8 @@ def main():
                      "traffic": traffic, "kernel": "attn_bf16_kernel", "kernel_version": version,
                      "flop_per_launch": r["attn_flop_per_launch"]},
         "streaming_kernels": {
-            "method": ("in the step: HIP events around each launch, mean over layers and timed "
-                       "steps (includes the gap between launches)"),
+            "method": ("in the step: each kernel's own begin and end timestamps (HIP events "
+                       "given to its launch), mean over layers and timed steps"),
             "rope_us": round(r["rope_us"], 2), "rope_GBps": round(r["rope_gbs"], 1),
             "rope_frac_hbm": round(r["rope_gbs"] / PEAK_HBM_GBS, 4),
             "append_us": round(r["append_us"], 2), "append_GBps": round(r["append_gbs"], 1),

@@ -383,10 +383,13 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *   attn_ws, attn_ws_bytes : the la_block_attn_fwd workspace shared by every
  *                            layer (NULL for none).
  *   timing_events          : NULL, or 6*n_layers + 2 caller-created hipEvent_t
- *                            (as void*) recorded on `stream` around each layer's
- *                            RoPE [6l, 6l+1], attention [6l+2, 6l+3] and append
- *                            (+ sink replacement) [6l+4, 6l+5], and around the
- *                            Euler update [6n, 6n+1]; for measuring kernels in place.
+ *                            (as void*) that take the begin and end timestamps of
+ *                            each layer's RoPE kernel [6l, 6l+1], attention kernel
+ *                            [6l+2, 6l+3] and append copy [6l+4, 6l+5] (the sink
+ *                            replacement is not included), and of the Euler kernel
+ *                            [6n, 6n+1]; they are given to the kernel launches
+ *                            themselves, so a span is the kernel's own duration (an
+ *                            operation that launches nothing records an empty span).
  * The whole step is validated before the first launch; on an error nothing is
  * enqueued and no ring changes.  Pointer arrays are host memory read at call
  * time.

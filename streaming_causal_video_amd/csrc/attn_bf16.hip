@@ -552,7 +552,7 @@ int attn_bf16_units(int nq, int heads) { return (nq + BM - 1) / BM * heads; }
 
 hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                             int nk, int heads, float qmul, const AttnWorkspace& ws,
-                            hipStream_t s) {
+                            hipStream_t s, const KernelTiming* tm) {
   const int qtiles = (nq + BM - 1) / BM;
   const int units = qtiles * heads;
   const int ntiles = segs.tend[segs.nseg - 1];
@@ -571,9 +571,9 @@ hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs
       nwg = units < P ? urem * cuts : P;
     }
   }
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(nwg), dim3(NTHREADS), 0, s,
-                     static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
-                     nk, heads, qmul, qtiles, nwg, wk);
+  launch_kernel(tm, attn_bf16_kernel, dim3(nwg), dim3(NTHREADS), 0, s,
+                static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq, nk,
+                heads, qmul, qtiles, nwg, wk);
   return hipGetLastError();
 }
 

@@ -89,17 +89,18 @@ attn_f32_kernel(const float* __restrict__ q, float* __restrict__ out, float* __r
 }  // namespace
 
 hipError_t launch_attn_f32(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
-                           int nk, int heads, int head_dim, float scale, hipStream_t s) {
+                           int nk, int heads, int head_dim, float scale, hipStream_t s,
+                           const KernelTiming* tm) {
   const int qtiles = (nq + 63) / 64;
   const float c2 = scale * 1.4426950408889634f;
   if (head_dim == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(qtiles * heads), dim3(64), 0, s,
-                       static_cast<const float*>(q), static_cast<float*>(out), lse, segs, nq, nk,
-                       heads, c2, qtiles);
+    launch_kernel(tm, attn_f32_kernel<64>, dim3(qtiles * heads), dim3(64), 0, s,
+                  static_cast<const float*>(q), static_cast<float*>(out), lse, segs, nq, nk, heads,
+                  c2, qtiles);
   else
-    hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(qtiles * heads), dim3(64), 0, s,
-                       static_cast<const float*>(q), static_cast<float*>(out), lse, segs, nq, nk,
-                       heads, c2, qtiles);
+    launch_kernel(tm, attn_f32_kernel<128>, dim3(qtiles * heads), dim3(64), 0, s,
+                  static_cast<const float*>(q), static_cast<float*>(out), lse, segs, nq, nk, heads,
+                  c2, qtiles);
   return hipGetLastError();
 }
 

@@ -333,12 +333,12 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
 
 hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, float scale, float dq, float dk, float dv,
-                           hipStream_t s) {
+                           hipStream_t s, const KernelTiming* tm) {
   const int qtiles = (nq + BM - 1) / BM;
   const float c2 = scale * dq * dk * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fp8_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
-                     static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
-                     nk, heads, c2, dv, 0.69314718055994531f, qtiles, qtiles * heads);
+  launch_kernel(tm, attn_fp8_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
+                static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq, nk,
+                heads, c2, dv, 0.69314718055994531f, qtiles, qtiles * heads);
   return hipGetLastError();
 }
 

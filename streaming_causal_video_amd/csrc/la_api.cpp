@@ -18,6 +18,19 @@ namespace {
 
 thread_local std::string g_last_hip_error;
 
+// Kernel timing of the operation the step driver is enqueuing on this thread (null
+// otherwise): the entry points pass it to their kernel launch, so that the driver's
+// timing events take the kernel's own begin and end timestamps.  Set only through
+// TimedOp, for the duration of one entry-point call.
+thread_local const la::KernelTiming* t_timing = nullptr;
+
+struct TimedOp {
+  explicit TimedOp(const la::KernelTiming* tm) { t_timing = tm; }
+  ~TimedOp() { t_timing = nullptr; }
+  TimedOp(const TimedOp&) = delete;
+  TimedOp& operator=(const TimedOp&) = delete;
+};
+
 la_status hip_status(hipError_t e) {
   if (e == hipSuccess) return LA_OK;
   g_last_hip_error = std::string(hipGetErrorName(e)) + ": " + hipGetErrorString(e);
@@ -247,7 +260,7 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
       {sink_k_in, sink_k_out, (int32_t)hwtok, n_frames, 1.0f},
   };
   return hip_status(la::launch_rope(t, 3, g, tc, static_cast<const float*>(dev_table), dtype,
-                                    static_cast<hipStream_t>(stream)));
+                                    static_cast<hipStream_t>(stream), t_timing));
 }
 
 size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads) {
@@ -267,7 +280,7 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
                    const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
                    float* lse_or_null, float scale, float q_scale, void* workspace,
                    size_t workspace_bytes, int slot_cap, bool clear_counters,
-                   la_stream_t stream) {
+                   la_stream_t stream, const KernelTiming* tm) {
   if (!r || !q_rot || !sink_k_rot || !k_cur_rot || !v_cur || !out) return LA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return LA_ERR_INVALID_ARG;
   if (ring_slots(r) == 0) return LA_ERR_STATE;
@@ -340,10 +353,10 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
         if (e != hipSuccess) return hip_status(e);
       }
     }
-    e = la::launch_attn_bf16(q_rot, out, lse_or_null, segs, n_q, end, r->heads, qmul, ws, s);
+    e = la::launch_attn_bf16(q_rot, out, lse_or_null, segs, n_q, end, r->heads, qmul, ws, s, tm);
   } else {
     e = la::launch_attn_f32(q_rot, out, lse_or_null, segs, n_q, end, r->heads, r->head_dim,
-                            scale / q_scale, s);
+                            scale / q_scale, s, tm);
   }
   return hip_status(e);
 }
@@ -361,7 +374,7 @@ la_status la_block_attn_fwd(const la_kvring* r, const void* q_rot, const void* s
                             float* lse_or_null, float scale, float q_scale, void* workspace,
                             size_t workspace_bytes, la_stream_t stream) {
   return la::attn_fwd(r, q_rot, sink_k_rot, k_cur_rot, v_cur, n_q, out, lse_or_null, scale,
-                      q_scale, workspace, workspace_bytes, 0, false, stream);
+                      q_scale, workspace, workspace_bytes, 0, false, stream, t_timing);
 }
 
 la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t n,
@@ -426,7 +439,7 @@ la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* 
   segs.end[n++] = end;
   segs.nseg = n;
   return hip_status(la::launch_attn_fp8(q8, out, lse_or_null, segs, n_q, end, r->heads, scale,
-                                        dq, dk, dv, static_cast<hipStream_t>(stream)));
+                                        dq, dk, dv, static_cast<hipStream_t>(stream), t_timing));
 }
 
 la_status la_kvcache_append_evict(la_kvring* r, const void* k_rot, const void* v,
@@ -454,11 +467,10 @@ la_status la_kvcache_append_evict(la_kvring* r, const void* k_rot, const void* v
   } else if (!vs) {
     vd = nullptr;
   }
-  if (ks) {
-    const hipError_t e =
-        la::launch_copy2(kd, ks, vd, vs, slot_bytes, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_status(e);
-  }
+  const hipError_t e =
+      ks ? la::launch_copy2(kd, ks, vd, vs, slot_bytes, static_cast<hipStream_t>(stream), t_timing)
+         : la::timing_without_kernel(t_timing, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e);
   r->slot_block[slot] = block_id;
   r->last_block = block_id;
   if (evicted_or_null) *evicted_or_null = evicted;
@@ -487,7 +499,7 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
     const uintptr_t xa = (uintptr_t)x, va = (uintptr_t)v, nb = (uintptr_t)n * 4;
     if (xa < va + nb && va < xa + nb) return LA_ERR_INVALID_ARG;  // partial overlap
   }
-  return hip_status(la::launch_euler(x, v, n, dt, static_cast<hipStream_t>(stream)));
+  return hip_status(la::launch_euler(x, v, n, dt, static_cast<hipStream_t>(stream), t_timing));
 }
 
 }  // extern "C"
@@ -563,9 +575,11 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
       rings[0].dtype == LA_BF16 ? (float)((double)scale * 1.4426950408889634) : 1.0f;
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> la_status {
-    if (!timing_events) return LA_OK;
-    return hip_status(hipEventRecord(static_cast<hipEvent_t>(timing_events[i]), hs));
+  // timing events i, i + 1 as the begin and end of the kernel of one operation
+  auto span = [&](int i) -> la::KernelTiming {
+    return timing_events ? la::KernelTiming{static_cast<hipEvent_t>(timing_events[i]),
+                                            static_cast<hipEvent_t>(timing_events[i + 1])}
+                         : la::KernelTiming{nullptr, nullptr};
   };
 #define LA_TRY(expr)                 \
   do {                               \
@@ -580,27 +594,38 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
       void* v_slot;
       LA_TRY(la_kvring_next_slot(r, &k_rot, &v_slot));
     }
-    LA_TRY(mark(6 * l));
-    LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot, frames_per_block, f0,
-                             r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
-                             r->heads, r->head_dim, (la_dtype)r->dtype, theta, q_scale, stream));
-    LA_TRY(mark(6 * l + 1));
-    LA_TRY(mark(6 * l + 2));
-    LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
-                             attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes,
-                             stream));
-    LA_TRY(mark(6 * l + 3));
-    LA_TRY(mark(6 * l + 4));
-    if (append)
+    const la::KernelTiming t_rope = span(6 * l), t_attn = span(6 * l + 2),
+                           t_app = span(6 * l + 4);
+    {
+      TimedOp op(&t_rope);
+      LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot, frames_per_block, f0,
+                               r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
+                               r->heads, r->head_dim, (la_dtype)r->dtype, theta, q_scale,
+                               stream));
+    }
+    {
+      TimedOp op(&t_attn);
+      LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
+                               attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes,
+                               stream));
+    }
+    if (append) {
+      TimedOp op(&t_app);
       LA_TRY(la_kvcache_append_evict(r, k_rot, v_raw[l], block_id, r->noise_level, nullptr,
                                      stream));
+    } else {
+      LA_TRY(hip_status(la::timing_without_kernel(&t_app, hs)));
+    }
     if (append && block_id == 1 && sink_k_new)
       LA_TRY(la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream));
-    LA_TRY(mark(6 * l + 5));
   }
-  LA_TRY(mark(6 * n_layers));
-  if (x && n_latent > 0) LA_TRY(la_fm_euler_step(x, vel, n_latent, dt, stream));
-  LA_TRY(mark(6 * n_layers + 1));
+  const la::KernelTiming t_euler = span(6 * n_layers);
+  if (x && n_latent > 0) {
+    TimedOp op(&t_euler);
+    LA_TRY(la_fm_euler_step(x, vel, n_latent, dt, stream));
+  } else {
+    LA_TRY(hip_status(la::timing_without_kernel(&t_euler, hs)));
+  }
 #undef LA_TRY
   return LA_OK;
 }
@@ -673,9 +698,8 @@ la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_
 
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> la_status {
-    if (!timing_events) return LA_OK;
-    return hip_status(hipEventRecord(static_cast<hipEvent_t>(timing_events[i]), hs));
+  auto ev = [&](int i) -> hipEvent_t {
+    return timing_events ? static_cast<hipEvent_t>(timing_events[i]) : nullptr;
   };
   // the reciprocals the quantisation multiplies by, as la_quantize_fp8 takes them
   const float iq = 1.0f / dq, ik = 1.0f / dk, iv = 1.0f / dv;
@@ -691,10 +715,16 @@ la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_
     void* k8 = k8_ws;
     void* v8 = v8_ws;
     if (append && r->nslots == r->W + 1) LA_TRY(la_kvring_next_slot(r, &k8, &v8));
-    LA_TRY(mark(6 * l));
-    LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
-                             r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
-                             r->heads, r->head_dim, LA_BF16, theta, 1.0f, stream));
+    // RoPE and the quantisation are timed as one span: RoPE's begin, the quantisation's end
+    const la::KernelTiming t_rope = {ev(6 * l), nullptr}, t_quant = {nullptr, ev(6 * l + 1)},
+                           t_attn = {ev(6 * l + 2), ev(6 * l + 3)},
+                           t_app = {ev(6 * l + 4), ev(6 * l + 5)};
+    {
+      TimedOp op(&t_rope);
+      LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
+                               r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
+                               r->heads, r->head_dim, LA_BF16, theta, 1.0f, stream));
+    }
     la::QuantJobs jobs = {};
     const void* ins[5] = {q_rot_ws, k_rot_ws, v_raw[l], sink_k_rot_ws, r->sink_v};
     void* outs[5] = {q8_ws, k8, v8, sink_k8_ws, sink_v8_ws};
@@ -707,22 +737,28 @@ la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_
       jobs.inv[j] = invs[j];
     }
     jobs.count = 5;
-    LA_TRY(hip_status(la::launch_quantize_fp8_many(jobs, hs)));
-    LA_TRY(mark(6 * l + 1));
-    LA_TRY(mark(6 * l + 2));
-    LA_TRY(la_block_attn_fwd_fp8(r, q8_ws, sink_k8_ws, sink_v8_ws, k8, v8, r->block_tokens,
-                                 attn_out[l], nullptr, scale, dq, dk, dv, stream));
-    LA_TRY(mark(6 * l + 3));
-    LA_TRY(mark(6 * l + 4));
-    if (append)
+    LA_TRY(hip_status(la::launch_quantize_fp8_many(jobs, hs, &t_quant)));
+    {
+      TimedOp op(&t_attn);
+      LA_TRY(la_block_attn_fwd_fp8(r, q8_ws, sink_k8_ws, sink_v8_ws, k8, v8, r->block_tokens,
+                                   attn_out[l], nullptr, scale, dq, dk, dv, stream));
+    }
+    if (append) {
+      TimedOp op(&t_app);
       LA_TRY(la_kvcache_append_evict(r, k8, v8, block_id, r->noise_level, nullptr, stream));
+    } else {
+      LA_TRY(hip_status(la::timing_without_kernel(&t_app, hs)));
+    }
     if (append && block_id == 1 && sink_k_new)
       LA_TRY(la_sink_replace(r, sink_k_new[l], sink_v_new[l], stream));
-    LA_TRY(mark(6 * l + 5));
   }
-  LA_TRY(mark(6 * n_layers));
-  if (x && n_latent > 0) LA_TRY(la_fm_euler_step(x, vel, n_latent, dt, stream));
-  LA_TRY(mark(6 * n_layers + 1));
+  const la::KernelTiming t_euler = {ev(6 * n_layers), ev(6 * n_layers + 1)};
+  if (x && n_latent > 0) {
+    TimedOp op(&t_euler);
+    LA_TRY(la_fm_euler_step(x, vel, n_latent, dt, stream));
+  } else {
+    LA_TRY(hip_status(la::timing_without_kernel(&t_euler, hs)));
+  }
 #undef LA_TRY
   return LA_OK;
 }

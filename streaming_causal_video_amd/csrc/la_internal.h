@@ -1,12 +1,40 @@
 // Internal declarations shared by the host library and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "la.h"
 
 namespace la {
+
+// Events that take the begin (start) and end (stop) timestamps of a kernel itself,
+// through the launch (hipExtLaunchKernelGGL), not as separate stream packets around
+// it; either may be null.  A launcher given one passes it to its (only) kernel.
+struct KernelTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+// A timed operation that launches nothing still completes its events (an empty span).
+inline hipError_t timing_without_kernel(const KernelTiming* tm, hipStream_t s) {
+  if (!tm) return hipSuccess;
+  if (tm->start) {
+    const hipError_t e = hipEventRecord(tm->start, s);
+    if (e != hipSuccess) return e;
+  }
+  return tm->stop ? hipEventRecord(tm->stop, s) : hipSuccess;
+}
+
+template <typename F, typename... Args>
+inline void launch_kernel(const KernelTiming* tm, F kernel, const dim3& grid, const dim3& block,
+                          uint32_t lds, hipStream_t s, Args... args) {
+  if (tm && (tm->start || tm->stop))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, tm->start, tm->stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 // Segment table of one attention call: keys [end[s-1], end[s]) come from
 // segment s, whose rows start at k[s] / v[s] with a row stride of
@@ -43,12 +71,14 @@ struct RopeGeom {
 };
 
 hipError_t launch_rope(const RopeTensor* t, int nt, const RopeGeom& g, const RopeTemporal& tc,
-                       const float* table, la_dtype dt, hipStream_t s);
+                       const float* table, la_dtype dt, hipStream_t s,
+                       const KernelTiming* tm = nullptr);
 hipError_t launch_rope_table(float* table, int Hl, int Wl, int hpairs, int wpairs, int hw,
                              double theta, hipStream_t s);
 hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size_t bytes,
-                        hipStream_t s);
-hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream_t s);
+                        hipStream_t s, const KernelTiming* tm = nullptr);
+hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream_t s,
+                        const KernelTiming* tm = nullptr);
 // Workspace of the bf16 attention's persistent schedule: an arrival counter per unit
 // (zero between calls) and one partial record of kAttnRecFloats floats per slot.
 constexpr int kAttnRecFloats = 4 * (8 * 3 * 64 * 4 + 2 * 3 * 64);
@@ -67,10 +97,10 @@ int attn_bf16_units(int nq, int heads);
 // are Q K^T; 1.0f when the caller's Q is already scaled.
 hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                             int nk, int heads, float qmul, const AttnWorkspace& ws,
-                            hipStream_t s);
+                            hipStream_t s, const KernelTiming* tm = nullptr);
 hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, float scale, float dq, float dk, float dv,
-                           hipStream_t s);
+                           hipStream_t s, const KernelTiming* tm = nullptr);
 hipError_t launch_quantize_fp8(const void* in, int in_dtype, void* out, int64_t n, float inv_scale,
                                hipStream_t s);
 // Several bf16 tensors to e4m3 in one launch (one grid row per tensor); every n is a
@@ -83,7 +113,8 @@ struct QuantJobs {
   float inv[kMaxQuantJobs];
   int32_t count;
 };
-hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s);
+hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s,
+                                    const KernelTiming* tm = nullptr);
 // la_block_attn_fwd with its workspace given explicitly: slot_cap > 0 limits the
 // persistent grid to that many workgroups; clear_counters zeroes the arrival counters
 // (with a small fill kernel) before the launch.
@@ -91,7 +122,7 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
                    const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
                    float* lse_or_null, float scale, float q_scale, void* workspace,
                    size_t workspace_bytes, int slot_cap, bool clear_counters,
-                   la_stream_t stream);
+                   la_stream_t stream, const KernelTiming* tm = nullptr);
 // Bytes of an attention workspace for `slots` persistent workgroups.
 size_t attn_workspace_bytes(int n_q, int heads, int slots);
 // Status of a HIP error (records its text as the thread's last HIP error).
@@ -99,6 +130,7 @@ la_status status_of(hipError_t e);
 // Zero `bytes` (a multiple of 4) of device memory on stream s.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_attn_f32(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
-                           int nk, int heads, int head_dim, float scale, hipStream_t s);
+                           int nk, int heads, int head_dim, float scale, hipStream_t s,
+                           const KernelTiming* tm = nullptr);
 
 }  // namespace la

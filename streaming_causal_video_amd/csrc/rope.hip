@@ -178,11 +178,11 @@ __global__ void rope_table_kernel(float* __restrict__ table, int Hl, int Wl, int
 template <bool kBF16>
 static void launch_rope_nh(int nh, dim3 grid, hipStream_t s, const RopeTensor* tt,
                            const RopeGeom& g, const RopeTemporal& tc, const float* table, int wg0,
-                           int wg1) {
+                           int wg1, const KernelTiming* tm) {
 #define LA_ROPE_NH(N)                                                                        \
   case N:                                                                                    \
-    hipLaunchKernelGGL((rope3d_kernel<kBF16, N>), grid, dim3(kThreads), 0, s, tt[0],   \
-                       tt[1], tt[2], g, tc, table, wg0, wg1);                                \
+    launch_kernel(tm, rope3d_kernel<kBF16, N>, grid, dim3(kThreads), 0, s, tt[0], tt[1],     \
+                  tt[2], g, tc, table, wg0, wg1);                                            \
     break;
   switch (nh) {
     LA_ROPE_NH(1) LA_ROPE_NH(2) LA_ROPE_NH(3) LA_ROPE_NH(4)
@@ -192,7 +192,7 @@ static void launch_rope_nh(int nh, dim3 grid, hipStream_t s, const RopeTensor* t
 }
 
 hipError_t launch_rope(const RopeTensor* t, int nt, const RopeGeom& g, const RopeTemporal& tc,
-                       const float* table, la_dtype dt, hipStream_t s) {
+                       const float* table, la_dtype dt, hipStream_t s, const KernelTiming* tm) {
   RopeTensor tt[3] = {};
   int wg[3] = {0, 0, 0};
   for (int i = 0; i < nt && i < 3; ++i) {
@@ -200,14 +200,14 @@ hipError_t launch_rope(const RopeTensor* t, int nt, const RopeGeom& g, const Rop
     if (t[i].in) wg[i] = t[i].tokens;
   }
   const int total = wg[0] + wg[1] + wg[2];
-  if (total == 0) return hipSuccess;
+  if (total == 0) return timing_without_kernel(tm, s);
   const int cpr = g.head_dim / (dt == LA_BF16 ? 8 : 4);
   const int hg_n = kThreads / cpr;
   const int nh = (g.heads + hg_n - 1) / hg_n;
   if (dt == LA_BF16)
-    launch_rope_nh<true>(nh, dim3(total), s, tt, g, tc, table, wg[0], wg[1]);
+    launch_rope_nh<true>(nh, dim3(total), s, tt, g, tc, table, wg[0], wg[1], tm);
   else
-    launch_rope_nh<false>(nh, dim3(total), s, tt, g, tc, table, wg[0], wg[1]);
+    launch_rope_nh<false>(nh, dim3(total), s, tt, g, tc, table, wg[0], wg[1], tm);
   return hipGetLastError();
 }
 

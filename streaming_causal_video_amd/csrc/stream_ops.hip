@@ -222,32 +222,32 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size_t bytes,
-                        hipStream_t s) {
+                        hipStream_t s, const KernelTiming* tm) {
   const int64_t n16 = (int64_t)(bytes / 16);
   const int tail = (int)(bytes - 16 * (size_t)n16);
-  if (bytes == 0) return hipSuccess;
+  if (bytes == 0) return timing_without_kernel(tm, s);
   const int64_t per_wg = kThreads * kUnroll;
   int64_t wgs = n16 > 0 ? (n16 + per_wg - 1) / per_wg : 1;
   if (wgs > 4096) wgs = 4096;
   dim3 grid((unsigned)wgs, d1 ? 2 : 1);
-  hipLaunchKernelGGL(copy2_kernel, grid, dim3(kThreads), 0, s, static_cast<u32x4_t*>(d0),
+  launch_kernel(tm, copy2_kernel, grid, dim3(kThreads), 0, s, static_cast<u32x4_t*>(d0),
                      static_cast<const u32x4_t*>(s0), static_cast<u32x4_t*>(d1),
                      static_cast<const u32x4_t*>(s1), n16, tail);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s) {
+hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s, const KernelTiming* tm) {
   if (jobs.count < 1 || jobs.count > kMaxQuantJobs) return hipErrorInvalidValue;
   int64_t most = 0;
   for (int j = 0; j < jobs.count; ++j) {
     if (jobs.n[j] % 16 != 0) return hipErrorInvalidValue;
     most = jobs.n[j] > most ? jobs.n[j] : most;
   }
-  if (most == 0) return hipSuccess;
+  if (most == 0) return timing_without_kernel(tm, s);
   int64_t wgs = (most / 16 + kThreads - 1) / kThreads;
   if (wgs > 2048) wgs = 2048;
-  hipLaunchKernelGGL(quant_fp8_many_kernel, dim3((unsigned)wgs, jobs.count), dim3(kThreads), 0,
-                     s, jobs);
+  launch_kernel(tm, quant_fp8_many_kernel, dim3((unsigned)wgs, jobs.count), dim3(kThreads), 0, s,
+                jobs);
   return hipGetLastError();
 }
 
@@ -265,8 +265,9 @@ hipError_t launch_quantize_fp8(const void* in, int in_dtype, void* out, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream_t s) {
-  if (n == 0) return hipSuccess;
+hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream_t s,
+                        const KernelTiming* tm) {
+  if (n == 0) return timing_without_kernel(tm, s);
   const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)v % 16 == 0);
   if (aligned) {
     const int64_t n4 = n / 4;
@@ -277,18 +278,17 @@ hipError_t launch_euler(float* x, const float* v, int64_t n, float dt, hipStream
     // beyond 64 M elements (x and v 512 MB together, twice the 256 MB last-level cache)
     // the update streams through HBM: non-temporal accesses
     if (n >= ((int64_t)1 << 26))
-      hipLaunchKernelGGL(euler_vec_kernel<true>, dim3((unsigned)wgs), dim3(kThreads), 0, s,
-                         reinterpret_cast<float4*>(x), reinterpret_cast<const float4*>(v), n4,
-                         x + 4 * n4, v + 4 * n4, tail, dt);
+      launch_kernel(tm, euler_vec_kernel<true>, dim3((unsigned)wgs), dim3(kThreads), 0, s,
+                    reinterpret_cast<float4*>(x), reinterpret_cast<const float4*>(v), n4,
+                    x + 4 * n4, v + 4 * n4, tail, dt);
     else
-      hipLaunchKernelGGL(euler_vec_kernel<false>, dim3((unsigned)wgs), dim3(kThreads), 0, s,
-                         reinterpret_cast<float4*>(x), reinterpret_cast<const float4*>(v), n4,
-                         x + 4 * n4, v + 4 * n4, tail, dt);
+      launch_kernel(tm, euler_vec_kernel<false>, dim3((unsigned)wgs), dim3(kThreads), 0, s,
+                    reinterpret_cast<float4*>(x), reinterpret_cast<const float4*>(v), n4,
+                    x + 4 * n4, v + 4 * n4, tail, dt);
   } else {
     int64_t wgs = (n + kThreads - 1) / kThreads;
     if (wgs > 65536) wgs = 65536;
-    hipLaunchKernelGGL(euler_scalar_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, x, v, n,
-                       dt);
+    launch_kernel(tm, euler_scalar_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, s, x, v, n, dt);
   }
   return hipGetLastError();
 }
