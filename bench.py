@@ -746,7 +746,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=6,
+                    help="untimed steps after the ring has filled (the first blocks after a "
+                         "cold start run up to 4 %% slower while the clock settles)")
     ap.add_argument("--workload", choices=["c4", "c2", "c3", "c5", "chain", "c2fp8", "c4fp8",
                                            "refresh"],
                     default="c4")
