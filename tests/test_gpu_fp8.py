@@ -396,3 +396,61 @@ def test_fp8_denoise_step_matches_oracle(L):
     for m, st in stacks.items():
         for l in range(n_layers):
             assert st.states[l].last_block == s.W + 2 and st.states[l].sink_replaced == 1
+
+
+@pytest.mark.timeout(900)
+def test_fp8_denoise_step_c2_sampled(L):
+    """The e4m3 step at the C2 shape (one layer, staged ring, blocks 1..W+1: the ring
+    full at the last one, Nk 24960): sampled rows of three heads against the oracle's
+    e4m3 attention, and the last block's window V codes bit for bit."""
+    t = torch()
+    s = si.C2
+    dq = dk = dv = SCALE_QKV
+    st = L.KVRingStack(1, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, t.uint8, 0.75,
+                       staged=True)
+    sk, sv = s.initial_sink(0)
+    st.sink_k_raw[0].copy_(to_dev(sk))
+    st.sink_v[0].copy_(to_dev(sv))
+    blk, snk = (s.block_tokens, s.heads, s.head_dim), (s.sink_tokens, s.heads, s.head_dim)
+    bf = lambda shp: t.empty(shp, dtype=t.bfloat16, device="cuda")
+    u8 = lambda shp: t.empty(shp, dtype=t.uint8, device="cuda")
+    table = t.empty(L.la_rope_table_bytes(s.Hl, s.Wl, s.head_dim) // 4, dtype=t.float32,
+                    device="cuda")
+    L.la_rope_table_fill(table, s.Hl, s.Wl, s.head_dim, 10000.0)
+    out = [bf(blk)]
+    ws = (bf(blk), bf(blk), bf(snk), u8(blk), None, None, u8(snk), u8(snk))
+    last = s.W + 1
+    for b in range(1, last + 1):
+        q, k, v = (to_dev(z) for z in s.block_inputs(0, b))
+        L.la_denoise_step_fp8(st.states, b, [q], [k], [v], out, *ws, table, s.Hl, s.Wl, 3, -1,
+                              10000.0, scale=s.head_dim ** -0.5, dq=dq, dk=dk, dv=dv,
+                              sink_k_new=[k[:s.sink_tokens]] if b == 1 else None,
+                              sink_v_new=[v[:s.sink_tokens]] if b == 1 else None)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(23)
+    rows = np.unique(np.concatenate([[0, s.block_tokens - 1], rng.integers(0, s.block_tokens, 40)]))
+    heads = [0, 21, 39]
+    from oracle import StreamOracle, attention_lse
+    so = StreamOracle(s, layer=0, heads=heads)
+    f32 = np.float32
+    q_raw, k_raw, v = so.raw_block(last)
+    q8 = quantize(_bf16(so.rot_block(q_raw, last)).astype(f32), dq)
+    keys = [quantize(_bf16(so.rot_sink(so.sink_for(last)[0], last)).astype(f32), dk)]
+    vals = [quantize(so.sink_for(last)[1].astype(f32), dv)]
+    for b2 in so.window_ids(last):
+        _, k2, v2 = so.raw_block(b2)
+        keys.append(quantize(_bf16(so.rot_block(k2, b2)).astype(f32), dk))
+        vals.append(quantize(v2.astype(f32), dv))
+    keys.append(quantize(_bf16(so.rot_block(k_raw, last)).astype(f32), dk))
+    vals.append(quantize(v.astype(f32), dv))
+    K8, V8 = np.concatenate(keys), np.concatenate(vals)
+    scale = s.head_dim ** -0.5
+    ref, _ = attention_fp8(q8[rows], K8, V8, dq, dk, dv, scale)
+    absv = np.abs(dequantize(V8, dv))
+    bound_a, _ = attention_lse(dequantize(q8[rows], dq), dequantize(K8, dk), absv, scale)
+    got = to_f64(out[0])[rows][:, heads]
+    r = check_fp8(got, ref, bound_a, absv.max(), "fp8 step C2")
+    slot = (last - 1) % (s.W + 1)
+    gv = st.v_slots[0, slot].cpu().numpy()[:, heads]
+    assert np.array_equal(gv, vals[-1]), "C2 last block: V codes differ"
+    say(f"fp8 step C2 block {last}: rel-L2 {r:.4f}")
