@@ -25,9 +25,12 @@
 //    of the row blocks 2h and 2h+1 hold keys 32h + 8g .. 32h + 8g + 7, so the
 //    probabilities P^T come out of the score accumulators already in the
 //    B-operand layout of O^T = V^T P^T, with no shuffle.
-//  * Each 64-key tile is processed as two 32-key halves (scores, softmax,
-//    P V): 24 score and 24 output registers per half instead of 48, which
-//    keeps the kernel within the 256 registers of two waves per SIMD.
+//  * Each 64-key tile is processed as two 32-key halves: the scores of both
+//    halves first, then the first half's softmax and P V, then the second's,
+//    so that the first half's P V MFMAs share a block with the second half's
+//    softmax.  Probabilities and the P V operands are held for one half at a
+//    time, which keeps the kernel within the 256 registers of two waves per
+//    SIMD.
 //  * Softmax in base 2 with the score scale folded into Q: the kernel takes Q
 //    already multiplied by c = scale * log2(e) (the RoPE kernel of the step
 //    emits it that way, rounded to bf16 once; a caller's plain Q is multiplied
@@ -38,8 +41,8 @@
 //    against the running reference without a per-tile max; only when a
 //    query's sum over the half leaves [0, 2^64] (and always on the first half
 //    of a piece) is the reference raised by the half's excess, the scores
-//    moved down by it, O and the row sum rescaled and the half's
-//    probabilities recomputed.  Exact: numerator and denominator use the same
+//    moved down by it (after the first half, the second half's as well), O
+//    and the row sum rescaled and the half's probabilities recomputed.  Exact: numerator and denominator use the same
 //    reference, and P <= 2^64 keeps the float32 accumulators far from
 //    overflow.  P is rounded to bf16 for the second product
 //    (v_cvt_pk_bf16_f32) and the row sum is taken from those same bf16 pairs
@@ -349,14 +352,20 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       // sits in LDS row 32 h + 16 (g >> 1) + 8 B + 4 (g & 1) + (c >> 2)
       const char* vt = reinterpret_cast<const char*>(vbuf(cur));
 
+      // Scores of both halves first (S^T[key][query] - m, keys 32 h .. 32 h + 31 in row
+      // blocks 2 h and 2 h + 1): the first half's P V MFMAs then share a block with the
+      // second half's softmax, which they can run beside (measured 1 % faster than
+      // scores, softmax and P V half by half, and faster than the second half's scores
+      // beside the first half's softmax).
+      f32x4_t st[2][2][NQT];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // S^T[key][query] - m for keys 32 h .. 32 h + 31: row blocks 2 h and 2 h + 1.
-        f32x4_t st[2][NQT];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int nt = 0; nt < NQT; ++nt) st[b][nt] = cm[nt];
+          for (int nt = 0; nt < NQT; ++nt) st[h][b][nt] = cm[nt];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -365,25 +374,29 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                 kr + 16 * (2 * h + b) * KP + (((4 * s + g) ^ c) * 8));
 #pragma unroll
             for (int nt = 0; nt < NQT; ++nt)
-              st[b][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[b][nt], 0, 0, 0);
+              st[h][b][nt] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nt][s], st[h][b][nt], 0, 0, 0);
           }
         if (h == 0 && more) vload(1 - cur);
-        if (__builtin_expect(nvalid < BN, 0)) {
-          // the last tile of a segment: row 4 g + i of block 2 h + b holds key
-          // 32 h + 8 g + 4 b + i of the tile.  Marked unlikely so that it stays a
-          // branch: otherwise the compiler turned the second half's masking into 32
-          // selects and compares on every tile.
+      }
+      if (__builtin_expect(nvalid < BN, 0)) {
+        // the last tile of a segment: row 4 g + i of block 2 h + b holds key
+        // 32 h + 8 g + 4 b + i of the tile
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               if (32 * h + 8 * g + 4 * b + i >= nvalid) {
 #pragma unroll
-                for (int nt = 0; nt < NQT; ++nt) st[b][nt][i] = -INFINITY;
+                for (int nt = 0; nt < NQT; ++nt) st[h][b][nt][i] = -INFINITY;
               }
             }
-        }
+      }
 
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
         // P^T fragment of query tile nt: keys 32 h + 8 g .. +7, i.e. rows
         // 4 g .. 4 g + 3 of both row blocks; tsum = this lane's sum of them.
         bf16x8_t pf[NQT];
@@ -395,8 +408,8 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
             float ts = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float p0 = __builtin_amdgcn_exp2f(st[e >> 1][nt][2 * (e & 1)]);
-              const float p1 = __builtin_amdgcn_exp2f(st[e >> 1][nt][2 * (e & 1) + 1]);
+              const float p0 = __builtin_amdgcn_exp2f(st[h][e >> 1][nt][2 * (e & 1)]);
+              const float p1 = __builtin_amdgcn_exp2f(st[h][e >> 1][nt][2 * (e & 1) + 1]);
               w[e] = pack_bf16(p0, p1);
               ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w[e]), ones, ts,
                                                    false);
@@ -406,27 +419,27 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
           }
         };
         probs();
-        // The first half of a piece always sets the reference (it starts at 0, not at
-        // a key's score).
         const bool first = h == 0 && j == kt0;
         bool over = first;
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt)  // on the bits (sums are >= +0): also inf and any NaN,
-          over |= __float_as_uint(tsum[nt]) > kSumLimitBits;  // whatever the NaN flags
+        for (int nt = 0; nt < NQT; ++nt)
+          over |= __float_as_uint(tsum[nt]) > kSumLimitBits;
         if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
           for (int nt = 0; nt < NQT; ++nt) {
-            // a = max over the half of c s - m: the reference becomes m + a on the first
-            // half of a piece and m + max(a, 0) afterwards; the scores move down by as much
-            const float a =
-                fmaxf(fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3])),
-                      fmaxf(fmaxf(st[1][nt][0], st[1][nt][1]), fmaxf(st[1][nt][2], st[1][nt][3])));
+            const float a = fmaxf(
+                fmaxf(fmaxf(st[h][0][nt][0], st[h][0][nt][1]), fmaxf(st[h][0][nt][2], st[h][0][nt][3])),
+                fmaxf(fmaxf(st[h][1][nt][0], st[h][1][nt][1]), fmaxf(st[h][1][nt][2], st[h][1][nt][3])));
             const float am = max4_lanes(a);
             const float delta = first ? am : fmaxf(am, 0.f);
             const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-delta);
             cm[nt] -= delta;
-            st[0][nt] -= delta;
-            st[1][nt] -= delta;
+            // this half's scores and, when it is the first half, the second's as well
+#pragma unroll
+            for (int h2 = h; h2 < 2; ++h2) {
+              st[h2][0][nt] -= delta;
+              st[h2][1][nt] -= delta;
+            }
             l_run[nt] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
