@@ -174,7 +174,10 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
     eul = [objs[6 * n_layers].elapsed_time(objs[6 * n_layers + 1]) for objs in ev_objs]
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall / args.steps * 1e3:.3f} ms/step)")
     fl = attn_flops(bt, nk, d, H)
-    rope_bytes = 2 * (2 * bt + st) * H * d * 2
+    # the bf16 step's RoPE launch rotates K and the sink K and writes the block tokens'
+    # float32 cos/sin for Q (d * 4 bytes a token; the attention kernel rotates Q as it
+    # loads it); the e4m3 step's rotates Q as well
+    rope_bytes = (2 * ((2 * bt if fp8 else bt) + st) * H * d * 2) + (0 if fp8 else bt * d * 4)
     # the fused append (staged rings) copies V only: RoPE wrote K into the slot
     app_bytes = (1 if staged else 2) * 2 * bt * H * d * 2
     if fp8:
@@ -264,18 +267,20 @@ def hbm_kernels_bench(Hl, Wl, W, H, d, reps=24, euler_elems=1 << 28):
     qs = float(np.float32(d ** -0.5 * np.log2(np.e)))
     statuses = []
     rope_args = []
+    # the bf16 step's RoPE work on K and the sink K (Q is rotated inside the attention;
+    # the step's launch also writes 2.4 MB of Q's cos/sin at this shape, 2 % more bytes)
     for j in range(nsets):
         a, b = ins[j], outs[j]
-        L.la_rope3d_rolling(a[0], b[0], a[1], b[1], FRAMES, 300 + 3 * j, a[2], b[2], DELTA, table,
+        L.la_rope3d_rolling(None, None, a[1], b[1], FRAMES, 300 + 3 * j, a[2], b[2], DELTA, table,
                             Hl, Wl, H, d, THETA, q_scale=qs)
-        rope_args.append((ptr(a[0]), ptr(b[0]), ptr(a[1]), ptr(b[1]), FRAMES, 300 + 3 * j,
+        rope_args.append((None, None, ptr(a[1]), ptr(b[1]), FRAMES, 300 + 3 * j,
                           ptr(a[2]), ptr(b[2]), DELTA, ptr(table), Hl, Wl, H, d, L.LA_BF16, THETA,
                           qs, stream))
 
     def rope(i):
         statuses.append(lib.la_rope3d_rolling(*rope_args[i % nsets]))
 
-    rope_bytes = 2 * (2 * bt + st) * H * d * 2
+    rope_bytes = 2 * (bt + st) * H * d * 2
     us = timed(rope)
     res.update(rope_us=us, rope_GBps=rope_bytes / (us * 1e-6) / 1e9)
     del outs

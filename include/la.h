@@ -354,6 +354,13 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  * rotated K straight into the ring's next slot (la_kvring_next_slot) instead of
  * k_rot_ws, step 2 reads it there, and step 3 copies only V.  The results and
  * the window's contents are the same bits as with k_rot_ws.
+ * Fused Q rotation (NOTES, Table 3, fused kernels; RoPE as in la_rope3d_rolling):
+ * for bf16 rings with heads >= 2, step 1 rotates only K and the sink K and writes
+ * the cos/sin of every block token's head_dim pairs, times q_scale (float32,
+ * head_dim * 4 bytes a token), into q_rot_ws instead of the rotated Q; step 2's
+ * attention kernel rotates the raw q_raw[l] with them as it loads its Q fragments,
+ * with la_rope3d_rolling's arithmetic (one fma per output, bf16 round to nearest
+ * even), so the results are the same bits as with the rotated Q.
  *
  * flags (bitwise or):
  *   LA_STEP_ATTEND_ONLY : skip steps 3 and 4 (no append, no sink replacement);
@@ -377,9 +384,9 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *                            block_tokens must equal frames_per_block*Hl*Wl and
  *                            sink_tokens Hl*Wl.
  *   scale                  : softmax scale (1/sqrt(head_dim) for the model).  For
- *                            bf16 rings step 1 writes Q times scale * log2(e)
- *                            (la_rope3d_rolling's q_scale) and step 2 takes it as
- *                            given.
+ *                            bf16 rings the rotated Q is multiplied by
+ *                            scale * log2(e) (la_rope3d_rolling's q_scale) and the
+ *                            attention takes it as given.
  *   attn_ws, attn_ws_bytes : the la_block_attn_fwd workspace shared by every
  *                            layer (NULL for none).
  *   timing_events          : NULL, or 6*n_layers + 2 caller-created hipEvent_t

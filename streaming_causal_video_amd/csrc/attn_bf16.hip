@@ -108,6 +108,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int D = 128;
@@ -151,17 +152,48 @@ __device__ __forceinline__ int key_of_krow(int r) {
   return (r & 32) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
 
+// Rotate a wave's Q fragments in place (see the kRotQ path of the kernel): pair
+// (a, b) with the token's scaled cos/sin (cs, sn) from qcs becomes
+// (fma(a, cs, -b sn), fma(a, sn, b cs)), rounded to bf16 (nearest even).
+__device__ __forceinline__ void rope_q(bf16x8_t (&qf)[NQT][4], const float* __restrict__ qcs,
+                                       int qrow0, int nq, int c, int g) {
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    // rows past nq hold zeros and stay zero; their lookup is clamped into the table
+    const int tok = min(qrow0 + 16 * nt + c, nq - 1);
+    const float* row = qcs + (int64_t)tok * D;  // D / 2 pairs x (cos, sin)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // pairs 16 s + 4 g .. +3: (cos, sin) x 4 = 32 contiguous bytes
+      const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(row + 32 * s + 8 * g);
+      const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(row + 32 * s + 8 * g + 4);
+      const float cs[4] = {e0[0], e0[2], e1[0], e1[2]};
+      const float sn[4] = {e0[1], e0[3], e1[1], e1[3]};
+      const u32x4_t x = __builtin_bit_cast(u32x4_t, qf[nt][s]);
+      u32x4_t y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __uint_as_float(x[i] << 16), b = __uint_as_float(x[i] & 0xffff0000u);
+        y[i] = pack_bf16(fmaf(a, cs[i], -b * sn[i]), fmaf(a, sn[i], b * cs[i]));
+      }
+      qf[nt][s] = __builtin_bit_cast(bf16x8_t, y);
+    }
+  }
+}
+
 // Partial record of one piece (floats): per wave, O as f32x4 per (d-tile, query
 // tile, lane), then m and the row sum l per (query tile, lane).
 constexpr int kRecO = 8 * NQT * 64 * 4;
 constexpr int kRecWave = kRecO + 2 * NQT * 64;
 static_assert(NWAVES * kRecWave == kAttnRecFloats, "partial record size");
 
+template <bool kRotQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                  float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
-                 float qmul, int qtiles, int nwg, AttnWork wk) {
+                 float qmul, int qtiles, int nwg, AttnWork wk,
+                 const float* __restrict__ qcs) {
   // The K and V buffers of the two stages are separate objects, so that the compiler
   // can tell a DMA into one stage from the fragment reads of the other and does not
   // wait for the DMA before those reads.
@@ -261,6 +293,12 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
 #pragma unroll
         for (int s = 0; s < 4; ++s) qf[nt][s] = bf16x8_t{};
       }
+    }
+    if constexpr (kRotQ) {
+      // Rolling RoPE of the raw Q (the step's path): this lane's elements
+      // 32 s + 8 g .. +7 are the head_dim pairs 16 s + 4 g + i (i = 0..3), rotated
+      // with the row's cos/sin from qcs as the RoPE kernel rotates Q
+      rope_q(qf, qcs, qbase, nq, c, g);
     }
     if (qmul != 1.0f) {
 #pragma unroll
@@ -396,14 +434,18 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
       __builtin_amdgcn_s_setprio(1);
       if (__builtin_expect(nvalid < BN, 0)) {
         // the last tile of a segment: row 4 g + i of block 2 h + b holds key
-        // 32 h + 8 g + 4 b + i of the tile
+        // 32 h + 8 g + 4 b + i of the tile.  The lane's first key is formed here from
+        // a copy of g that the compiler cannot see through, so that it does not keep
+        // the sixteen key indexes live (in scratch) across the tile loop.
+        int key0 = 8 * g;
+        asm volatile("" : "+v"(key0));
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              if (32 * h + 8 * g + 4 * b + i >= nvalid) {
+              if (key0 + 32 * h + 4 * b + i >= nvalid) {
 #pragma unroll
                 for (int nt = 0; nt < NQT; ++nt) st[h][b][nt][i] = -INFINITY;
               }
@@ -596,7 +638,7 @@ int attn_bf16_units(int nq, int heads) { return (nq + BM - 1) / BM * heads; }
 
 hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                             int nk, int heads, float qmul, const AttnWorkspace& ws,
-                            hipStream_t s, const KernelTiming* tm) {
+                            hipStream_t s, const KernelTiming* tm, const float* qcs) {
   const int qtiles = (nq + BM - 1) / BM;
   const int units = qtiles * heads;
   const int ntiles = segs.tend[segs.nseg - 1];
@@ -615,9 +657,14 @@ hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs
       nwg = units < P ? urem * cuts : P;
     }
   }
-  launch_kernel(tm, attn_bf16_kernel, dim3(nwg), dim3(NTHREADS), 0, s,
-                static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq, nk,
-                heads, qmul, qtiles, nwg, wk);
+  if (qcs != nullptr)
+    launch_kernel(tm, attn_bf16_kernel<true>, dim3(nwg), dim3(NTHREADS), 0, s,
+                  static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
+                  nk, heads, qmul, qtiles, nwg, wk, qcs);
+  else
+    launch_kernel(tm, attn_bf16_kernel<false>, dim3(nwg), dim3(NTHREADS), 0, s,
+                  static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
+                  nk, heads, qmul, qtiles, nwg, wk, static_cast<const float*>(nullptr));
   return hipGetLastError();
 }
 

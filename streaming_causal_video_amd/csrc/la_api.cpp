@@ -54,6 +54,14 @@ void bands(int d, int* t, int* hw) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Frame-axis cos/sin of pair k at position pos: float64 on the host, rounded to float32
+// (positions are unbounded over a long stream).
+void frame_cs(int64_t pos, int k, int tband, double theta, float* c, float* s) {
+  const double ang = (double)pos * pow(theta, -2.0 * (double)k / (double)tband);
+  *c = (float)cos(ang);
+  *s = (float)sin(ang);
+}
+
 // Compute units of the current device (cached per device); 0 if it cannot be read.
 int device_cus() {
   static int cache[64];
@@ -79,7 +87,7 @@ size_t attn_ws_bytes(int n_q, int heads, int slots) {
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v15 fp8-v6"; }
+const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v16 fp8-v6"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -211,11 +219,19 @@ la_status la_rope_table_fill(void* dev_table, int32_t Hl, int32_t Wl, int32_t he
                                           hw, theta, static_cast<hipStream_t>(stream)));
 }
 
-la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, void* k_out,
-                            int32_t n_frames, int64_t f0, const void* sink_k_in,
-                            void* sink_k_out, int64_t sink_delta, const void* dev_table,
-                            int32_t Hl, int32_t Wl, int32_t heads, int32_t head_dim,
-                            la_dtype dtype, double theta, float q_scale, la_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// la_rope3d_rolling, and optionally (q_cs_out != NULL, with k_in) the cos/sin of every
+// block token's pairs times q_scale into q_cs_out[token][head_dim / 2][2]: what the
+// rotation of a Q at those positions multiplies by (the step hands it to the bf16
+// attention, which then rotates its raw Q itself).
+la_status rope_rolling(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                       int32_t n_frames, int64_t f0, const void* sink_k_in, void* sink_k_out,
+                       int64_t sink_delta, const void* dev_table, int32_t Hl, int32_t Wl,
+                       int32_t heads, int32_t head_dim, la_dtype dtype, double theta,
+                       float q_scale, float* q_cs_out, la_stream_t stream) {
   if (!valid_dtype(dtype)) return LA_ERR_DTYPE;
   if (!dev_table || !(theta > 1.0)) return LA_ERR_INVALID_ARG;
   if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
@@ -239,11 +255,8 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
   memset(&tc, 0, sizeof(tc));
   for (int row = 0; row <= n_frames; ++row) {
     const int64_t pos = row < n_frames ? f0 + row : f0 + sink_delta;
-    for (int k = 0; k < tpairs; ++k) {
-      const double a = (double)pos * pow(theta, -2.0 * (double)k / (double)tband);
-      tc.cs[row][k][0] = (float)cos(a);
-      tc.cs[row][k][1] = (float)sin(a);
-    }
+    for (int k = 0; k < tpairs; ++k)
+      frame_cs(pos, k, tband, theta, &tc.cs[row][k][0], &tc.cs[row][k][1]);
   }
   la::RopeGeom g;
   g.HW = (int32_t)hwtok;
@@ -254,13 +267,27 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
   g.tpairs = tpairs;
   g.hpairs = hw / 2;
   g.wpairs = hw / 2;
+  if (q_cs_out && (!k_in || !aligned16(q_cs_out))) return LA_ERR_INVALID_ARG;
   la::RopeTensor t[3] = {
-      {q_in, q_out, (int32_t)(hwtok * n_frames), 0, q_scale},
-      {k_in, k_out, (int32_t)(hwtok * n_frames), 0, 1.0f},
-      {sink_k_in, sink_k_out, (int32_t)hwtok, n_frames, 1.0f},
+      {q_in, q_out, (int32_t)(hwtok * n_frames), 0, q_scale, nullptr, 1.0f},
+      {k_in, k_out, (int32_t)(hwtok * n_frames), 0, 1.0f, q_cs_out, q_scale},
+      {sink_k_in, sink_k_out, (int32_t)hwtok, n_frames, 1.0f, nullptr, 1.0f},
   };
   return hip_status(la::launch_rope(t, 3, g, tc, static_cast<const float*>(dev_table), dtype,
                                     static_cast<hipStream_t>(stream), t_timing));
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                            int32_t n_frames, int64_t f0, const void* sink_k_in,
+                            void* sink_k_out, int64_t sink_delta, const void* dev_table,
+                            int32_t Hl, int32_t Wl, int32_t heads, int32_t head_dim,
+                            la_dtype dtype, double theta, float q_scale, la_stream_t stream) {
+  return rope_rolling(q_in, q_out, k_in, k_out, n_frames, f0, sink_k_in, sink_k_out, sink_delta,
+                      dev_table, Hl, Wl, heads, head_dim, dtype, theta, q_scale, nullptr, stream);
 }
 
 size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads) {
@@ -280,8 +307,9 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
                    const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
                    float* lse_or_null, float scale, float q_scale, void* workspace,
                    size_t workspace_bytes, int slot_cap, bool clear_counters,
-                   la_stream_t stream, const KernelTiming* tm) {
+                   la_stream_t stream, const KernelTiming* tm, const float* qcs) {
   if (!r || !q_rot || !sink_k_rot || !k_cur_rot || !v_cur || !out) return LA_ERR_INVALID_ARG;
+  if (qcs && (r->dtype != LA_BF16 || !aligned16(qcs))) return LA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return LA_ERR_INVALID_ARG;
   if (ring_slots(r) == 0) return LA_ERR_STATE;
   if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
@@ -353,7 +381,8 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
         if (e != hipSuccess) return hip_status(e);
       }
     }
-    e = la::launch_attn_bf16(q_rot, out, lse_or_null, segs, n_q, end, r->heads, qmul, ws, s, tm);
+    e = la::launch_attn_bf16(q_rot, out, lse_or_null, segs, n_q, end, r->heads, qmul, ws, s, tm,
+                             qcs);
   } else {
     e = la::launch_attn_f32(q_rot, out, lse_or_null, segs, n_q, end, r->heads, r->head_dim,
                             scale / q_scale, s, tm);
@@ -586,6 +615,11 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
     const la_status st_ = (expr);    \
     if (st_ != LA_OK) return st_;    \
   } while (0)
+  // bf16 rings with at least two heads: RoPE writes the block tokens' cos/sin (times
+  // q_scale, 512 bytes a token) into q_rot_ws instead of rotating Q, and the attention
+  // rotates the raw Q with them as it loads it (the same bits as rotating Q first)
+  const bool fuse_q = rings[0].dtype == LA_BF16 && rings[0].heads >= 2;
+  float* q_cs = fuse_q ? static_cast<float*>(q_rot_ws) : nullptr;
   for (int l = 0; l < n_layers; ++l) {
     la_kvring* r = &rings[l];
     // fused append: a staged ring takes the rotated K in its next slot directly
@@ -598,16 +632,21 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
                            t_app = span(6 * l + 4);
     {
       TimedOp op(&t_rope);
-      LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot, frames_per_block, f0,
-                               r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
-                               r->heads, r->head_dim, (la_dtype)r->dtype, theta, q_scale,
-                               stream));
+      LA_TRY(rope_rolling(fuse_q ? nullptr : q_raw[l], fuse_q ? nullptr : q_rot_ws, k_raw[l],
+                          k_rot, frames_per_block, f0, r->sink_k_raw, sink_k_rot_ws, sink_delta,
+                          rope_table, Hl, Wl, r->heads, r->head_dim, (la_dtype)r->dtype, theta,
+                          q_scale, q_cs, stream));
     }
     {
       TimedOp op(&t_attn);
-      LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
-                               attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes,
-                               stream));
+      if (fuse_q)
+        LA_TRY(la::attn_fwd(r, q_raw[l], sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
+                            attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes, 0,
+                            false, stream, t_timing, q_cs));
+      else
+        LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
+                                 attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes,
+                                 stream));
     }
     if (append) {
       TimedOp op(&t_app);

@@ -64,6 +64,10 @@ struct RopeTensor {
   int32_t tokens;
   int32_t trow0;  // temporal row of this tensor's frame 0
   float scale;    // factor applied to the rotated values before the store
+  // optional: cs_out[tok][pair][2] receives each token's cos and sin times cs_scale
+  // (the values a Q at the same positions, with scale cs_scale, is rotated with)
+  float* cs_out;
+  float cs_scale;
 };
 
 struct RopeGeom {
@@ -95,9 +99,14 @@ struct AttnWork {  // as passed to the kernel
 int attn_bf16_units(int nq, int heads);
 // qmul: factor applied to Q (then rounded to bf16) so that the kernel's base-2 scores
 // are Q K^T; 1.0f when the caller's Q is already scaled.
+// qcs: nullptr when q is already rotated; else q is the raw Q and qcs[tok][pair][2]
+// holds the cos and sin of each token's head_dim pairs, already multiplied by the
+// factor RoPE applies to Q (rope3d_kernel writes it, see RopeTensor::cs_out): the kernel
+// rotates each pair with them exactly as rope3d_kernel rotates Q.
 hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                             int nk, int heads, float qmul, const AttnWorkspace& ws,
-                            hipStream_t s, const KernelTiming* tm = nullptr);
+                            hipStream_t s, const KernelTiming* tm = nullptr,
+                            const float* qcs = nullptr);
 hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, float scale, float dq, float dk, float dv,
                            hipStream_t s, const KernelTiming* tm = nullptr);
@@ -122,7 +131,8 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
                    const void* k_cur_rot, const void* v_cur, int32_t n_q, void* out,
                    float* lse_or_null, float scale, float q_scale, void* workspace,
                    size_t workspace_bytes, int slot_cap, bool clear_counters,
-                   la_stream_t stream, const KernelTiming* tm = nullptr);
+                   la_stream_t stream, const KernelTiming* tm = nullptr,
+                   const float* qcs = nullptr);
 // Bytes of an attention workspace for `slots` persistent workgroups.
 size_t attn_workspace_bytes(int n_q, int heads, int slots);
 // Status of a HIP error (records its text as the thread's last HIP error).

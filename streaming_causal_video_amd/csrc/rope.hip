@@ -34,6 +34,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 constexpr int kThreads = 128;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // One workgroup rotates one token row (all heads) of one tensor.  Thread
 // (hg, ch) owns 16-byte chunk ch of a head row and heads hg, hg + HG, ...
@@ -103,6 +104,21 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
     const bool temporal = gp < g.tpairs;
     cs[i] = temporal ? tc.cs[trow][ti][0] : e.x;
     sn[i] = temporal ? tc.cs[trow][ti][1] : e.y;
+  }
+  // The token's cos/sin for a Q at the same positions (the step's bf16 attention
+  // rotates its raw Q with them): times cs_scale, as the scaled rotation below
+  // multiplies them (the product is exact for a scale of 1).
+  if (T.cs_out != nullptr && hg == 0) {
+    float e[2 * kPPC];
+#pragma unroll
+    for (int i = 0; i < kPPC; ++i) {
+      e[2 * i] = cs[i] * T.cs_scale;
+      e[2 * i + 1] = sn[i] * T.cs_scale;
+    }
+    float* dst_cs = T.cs_out + (size_t)tok * g.head_dim + ch * 2 * kPPC;
+#pragma unroll
+    for (int i = 0; i < 2 * kPPC; i += 4)
+      *reinterpret_cast<f32x4_t*>(dst_cs + i) = f32x4_t{e[i], e[i + 1], e[i + 2], e[i + 3]};
   }
   // An output scale (the attention's score scale folded into Q) multiplies the
   // pair's cos/sin once per thread; with scale 1 the products are exact.

@@ -106,6 +106,39 @@ def test_denoise_step_matches_oracle_and_per_op_path(L):
         assert stack.states[l].last_block == 6 and stack.states[l].sink_replaced == 1
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("shape_name", ["C2", "C5"])
+def test_step_rotates_q_in_the_attention_with_the_same_bits(L, shape_name):
+    """For bf16 rings la_denoise_step leaves Q's Rolling RoPE to the attention kernel:
+    RoPE writes the block tokens' cos/sin (times q_scale) into q_rot_ws and the attention
+    rotates the raw Q with them as it loads it.  At full size every output element
+    equals the per-op path's (la_rope3d_rolling of Q into a workspace, then
+    la_block_attn_fwd) bit for bit, over W + 2 blocks: the sink replacement, the ring
+    filling and evicting, and each block's own frame positions."""
+    t = torch()
+    s = getattr(si, shape_name)
+    stack, table = _stage(L, s, 1, staged=True)
+    per_op = GpuLayerStream(s)
+    blk = (s.block_tokens, s.heads, s.head_dim)
+    out = t.empty(blk, dtype=t.bfloat16, device="cuda")
+    qws = t.empty(blk, dtype=t.bfloat16, device="cuda")
+    kws = t.empty(blk, dtype=t.bfloat16, device="cuda")
+    sws = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+    aws = L.AttnWorkspace(s.block_tokens, s.heads)
+    nsink = s.sink_tokens
+    for b in range(1, s.W + 3):
+        q, k, v = per_op.block_dev(b)
+        say(f"{shape_name} block {b}")
+        L.la_denoise_step(stack.states, b, [q], [k], [v], [out], qws, kws, sws, table, s.Hl,
+                          s.Wl, FRAMES_PER_BLOCK, SINK_DELTA, THETA,
+                          scale=softmax_scale(s.head_dim), attn_ws=aws,
+                          sink_k_new=[k[:nsink]] if b == 1 else None,
+                          sink_v_new=[v[:nsink]] if b == 1 else None)
+        per_op.step(b)
+        t.cuda.synchronize()
+        assert t.equal(out.view(t.int16), per_op.out.view(t.int16)), (shape_name, b)
+
+
 @pytest.mark.parametrize("case", ["mid_3_layers", "c2_1_layer"])
 def test_staged_rings_fuse_the_append_with_the_same_bits(L, case):
     """Staged rings (W + 1 slots): la_denoise_step writes each layer's rotated K straight
