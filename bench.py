@@ -47,7 +47,7 @@ DT = -0.25
 # keyed by the attention kernel version the library reports; any other version
 # reports null (the counters were taken on a different kernel).
 ATTN_TRAFFIC_BYTES = {"attn-v9": 8.618e8, "attn-v12": 9.031e8, "attn-v13": 9.128e8, "attn-v14": 9.047e8,
-                      "attn-v15": 8.118e8}
+                      "attn-v15": 8.118e8, "attn-v16": 8.916e8}
 # The same for the e4m3 attention kernel at the C2 shape (--workload c2fp8).
 FP8_TRAFFIC_BYTES = {"fp8-v6": 5.337e+08}
 
@@ -143,6 +143,11 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
         for o in objs:
             o.record()  # creates the underlying HIP event
         arr = (ctypes.c_void_p * nev)(*[o.cuda_event for o in objs])
+        if staged:
+            # a staged ring's append launches nothing (the RoPE launch staged K and V):
+            # its span is not taken, which keeps two event packets per layer off the stream
+            for l in range(n_layers):
+                arr[6 * l + 4] = arr[6 * l + 5] = None
         ev_objs.append(objs)
         ev_arrays.append(arr)
     t0 = torch.cuda.Event(enable_timing=True)
@@ -166,7 +171,7 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
 
     rope_ms, _ = avg(0)
     attn_ms, attn_sd = avg(2)
-    app_ms, _ = avg(4)
+    app_ms = 0.0 if staged else avg(4)[0]
     # per timed block: attention time of each layer's launch, averaged over the layers
     per_block = [float(np.mean([objs[6 * l + 2].elapsed_time(objs[6 * l + 3])
                                 for l in range(n_layers)])) for objs in ev_objs]
@@ -178,8 +183,12 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
     # float32 cos/sin for Q (d * 4 bytes a token; the attention kernel rotates Q as it
     # loads it); the e4m3 step's rotates Q as well
     rope_bytes = (2 * ((2 * bt if fp8 else bt) + st) * H * d * 2) + (0 if fp8 else bt * d * 4)
-    # the fused append (staged rings) copies V only: RoPE wrote K into the slot
-    app_bytes = (1 if staged else 2) * 2 * bt * H * d * 2
+    # plain rings: the append copies K and V after the attention; staged rings: the
+    # RoPE launch also writes K into the next slot and copies V there, so the append
+    # only records the block
+    app_bytes = 0 if staged else 2 * 2 * bt * H * d * 2
+    if staged and not fp8:
+        rope_bytes += 2 * bt * H * d * 2
     if fp8:
         # RoPE and the quantisation of Q, K, V, sink K and sink V (bf16 in, e4m3 out);
         # a staged e4m3 ring takes K and V codes in place, so the append copies nothing
@@ -193,7 +202,8 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
         "attn_flop_per_launch": fl,
         "rope_us": rope_ms * 1e3, "rope_gbs": rope_bytes / (rope_ms * 1e-3) / 1e9,
         "rope_bytes": rope_bytes,
-        "append_us": app_ms * 1e3, "append_gbs": app_bytes / (app_ms * 1e-3) / 1e9,
+        "append_us": app_ms * 1e3,
+        "append_gbs": app_bytes / (app_ms * 1e-3) / 1e9 if app_bytes else 0.0,
         "append_bytes": app_bytes,
         "euler_us": float(np.mean(eul)) * 1e3,
         "nq": bt, "nk": nk,
@@ -267,20 +277,20 @@ def hbm_kernels_bench(Hl, Wl, W, H, d, reps=24, euler_elems=1 << 28):
     qs = float(np.float32(d ** -0.5 * np.log2(np.e)))
     statuses = []
     rope_args = []
-    # the bf16 step's RoPE work on K and the sink K (Q is rotated inside the attention;
-    # the step's launch also writes 2.4 MB of Q's cos/sin at this shape, 2 % more bytes)
+    # the whole la_rope3d_rolling call (Q, K and the sink K): 224 MB at C2, about the
+    # bytes of the step's fused launch (K, the sink K, Q's cos/sin and the V staging)
     for j in range(nsets):
         a, b = ins[j], outs[j]
-        L.la_rope3d_rolling(None, None, a[1], b[1], FRAMES, 300 + 3 * j, a[2], b[2], DELTA, table,
+        L.la_rope3d_rolling(a[0], b[0], a[1], b[1], FRAMES, 300 + 3 * j, a[2], b[2], DELTA, table,
                             Hl, Wl, H, d, THETA, q_scale=qs)
-        rope_args.append((None, None, ptr(a[1]), ptr(b[1]), FRAMES, 300 + 3 * j,
+        rope_args.append((ptr(a[0]), ptr(b[0]), ptr(a[1]), ptr(b[1]), FRAMES, 300 + 3 * j,
                           ptr(a[2]), ptr(b[2]), DELTA, ptr(table), Hl, Wl, H, d, L.LA_BF16, THETA,
                           qs, stream))
 
     def rope(i):
         statuses.append(lib.la_rope3d_rolling(*rope_args[i % nsets]))
 
-    rope_bytes = 2 * (bt + st) * H * d * 2
+    rope_bytes = 2 * (2 * bt + st) * H * d * 2
     us = timed(rope)
     res.update(rope_us=us, rope_GBps=rope_bytes / (us * 1e-6) / 1e9)
     del outs
@@ -829,8 +839,9 @@ def main():
         "config": {"workload": name, "layers": geo["n_layers"], "heads": geo["H"],
                    "head_dim": geo["d"], "block_tokens": r["nq"], "sink_tokens": geo["Hl"] * geo["Wl"],
                    "window_blocks": geo["W"], "nk": r["nk"],
-                   "rings": ("staged: W + 1 slots, RoPE writes K into the next slot, the append "
-                             "copies V (fused)" if args.ring == "staged" else
+                   "rings": ("staged: W + 1 slots; the RoPE launch writes the rotated K into "
+                             "the next slot and copies V there, the append only records the "
+                             "block (fused)" if args.ring == "staged" else
                              "plain: W slots, the append copies K and V"),
                    "parallelism": "none (1 GPU = 1 stage)"},
         "attn_tflops": round(r["attn_tflops"], 2),
@@ -846,8 +857,15 @@ def main():
                        "given to its launch), mean over layers and timed steps"),
             "rope_us": round(r["rope_us"], 2), "rope_GBps": round(r["rope_gbs"], 1),
             "rope_frac_hbm": round(r["rope_gbs"] / PEAK_HBM_GBS, 4),
-            "append_us": round(r["append_us"], 2), "append_GBps": round(r["append_gbs"], 1),
-            "append_frac_hbm": round(r["append_gbs"] / PEAK_HBM_GBS, 4),
+            "rope_bytes": r["rope_bytes"],
+            "rope_launch": ("K and the sink K rotated, the block tokens' cos/sin for Q (the "
+                            "attention rotates Q), and the block's V copied into the ring's "
+                            "next slot (the append's copy)" if args.ring == "staged" else
+                            "K and the sink K rotated, the block tokens' cos/sin for Q"),
+            "append_us": round(r["append_us"], 2) if r["append_bytes"] else None,
+            "append_GBps": round(r["append_gbs"], 1) if r["append_bytes"] else None,
+            "append_frac_hbm": (round(r["append_gbs"] / PEAK_HBM_GBS, 4)
+                                if r["append_bytes"] else None),
             "append_bytes": r["append_bytes"],
             "euler_us": round(r["euler_us"], 2),
         },

@@ -350,10 +350,12 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *      (sink_k_new[l], sink_v_new[l]) (Adaptive Attention Sink, NOTES 关键设计 3);
  * then la_fm_euler_step(x, vel, n_latent, dt) if x != NULL.
  * Fused append (NOTES, Table 3, fused kernels): for a staged ring
- * (la_kvring_init_staged) and without LA_STEP_ATTEND_ONLY, step 1 writes the
- * rotated K straight into the ring's next slot (la_kvring_next_slot) instead of
- * k_rot_ws, step 2 reads it there, and step 3 copies only V.  The results and
- * the window's contents are the same bits as with k_rot_ws.
+ * (la_kvring_init_staged) and without LA_STEP_ATTEND_ONLY, step 1's launch writes
+ * the rotated K straight into the ring's next slot (la_kvring_next_slot) instead
+ * of k_rot_ws and copies v_raw[l] into the same slot (no block of the window uses
+ * that slot, and step 2 reads V from v_raw[l]); step 2 reads K there, and step 3
+ * only records the block (nothing is left to copy).  The results and the window's
+ * contents are the same bits as with k_rot_ws.
  * Fused Q rotation (NOTES, Table 3, fused kernels; RoPE as in la_rope3d_rolling):
  * for bf16 rings with heads >= 2, step 1 rotates only K and the sink K and writes
  * the cos/sin of every block token's head_dim pairs, times q_scale (float32,
@@ -396,7 +398,10 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  *                            replacement is not included), and of the Euler kernel
  *                            [6n, 6n+1]; they are given to the kernel launches
  *                            themselves, so a span is the kernel's own duration (an
- *                            operation that launches nothing records an empty span).
+ *                            operation that launches nothing records an empty span,
+ *                            two event packets on the stream).  An entry may be
+ *                            NULL: that timestamp is not taken (e.g. the append of
+ *                            a staged ring, which launches nothing).
  * The whole step is validated before the first launch; on an error nothing is
  * enqueued and no ring changes.  Pointer arrays are host memory read at call
  * time.

@@ -223,15 +223,19 @@ la_status la_rope_table_fill(void* dev_table, int32_t Hl, int32_t Wl, int32_t he
 
 namespace {
 
-// la_rope3d_rolling, and optionally (q_cs_out != NULL, with k_in) the cos/sin of every
-// block token's pairs times q_scale into q_cs_out[token][head_dim / 2][2]: what the
-// rotation of a Q at those positions multiplies by (the step hands it to the bf16
-// attention, which then rotates its raw Q itself).
+// la_rope3d_rolling, and optionally in the same launch:
+//  * q_cs_out != NULL (with k_in): the cos/sin of every block token's pairs times
+//    q_scale into q_cs_out[token][head_dim / 2][2], what the rotation of a Q at those
+//    positions multiplies by (the step hands it to the bf16 attention, which then
+//    rotates its raw Q itself);
+//  * v_in, v_out != NULL: a plain copy of the block's V (the step stages it in a ring
+//    slot).
 la_status rope_rolling(const void* q_in, void* q_out, const void* k_in, void* k_out,
                        int32_t n_frames, int64_t f0, const void* sink_k_in, void* sink_k_out,
                        int64_t sink_delta, const void* dev_table, int32_t Hl, int32_t Wl,
                        int32_t heads, int32_t head_dim, la_dtype dtype, double theta,
-                       float q_scale, float* q_cs_out, la_stream_t stream) {
+                       float q_scale, float* q_cs_out, const void* v_in, void* v_out,
+                       la_stream_t stream) {
   if (!valid_dtype(dtype)) return LA_ERR_DTYPE;
   if (!dev_table || !(theta > 1.0)) return LA_ERR_INVALID_ARG;
   if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
@@ -268,12 +272,15 @@ la_status rope_rolling(const void* q_in, void* q_out, const void* k_in, void* k_
   g.hpairs = hw / 2;
   g.wpairs = hw / 2;
   if (q_cs_out && (!k_in || !aligned16(q_cs_out))) return LA_ERR_INVALID_ARG;
-  la::RopeTensor t[3] = {
-      {q_in, q_out, (int32_t)(hwtok * n_frames), 0, q_scale, nullptr, 1.0f},
-      {k_in, k_out, (int32_t)(hwtok * n_frames), 0, 1.0f, q_cs_out, q_scale},
-      {sink_k_in, sink_k_out, (int32_t)hwtok, n_frames, 1.0f, nullptr, 1.0f},
+  if ((!v_in) != (!v_out) || (v_in && (!aligned16(v_in) || !aligned16(v_out))))
+    return LA_ERR_INVALID_ARG;
+  la::RopeTensor t[4] = {
+      {q_in, q_out, (int32_t)(hwtok * n_frames), 0, q_scale, nullptr, 1.0f, 0},
+      {k_in, k_out, (int32_t)(hwtok * n_frames), 0, 1.0f, q_cs_out, q_scale, 0},
+      {sink_k_in, sink_k_out, (int32_t)hwtok, n_frames, 1.0f, nullptr, 1.0f, 0},
+      {v_in, v_out, (int32_t)(hwtok * n_frames), 0, 1.0f, nullptr, 1.0f, 1},
   };
-  return hip_status(la::launch_rope(t, 3, g, tc, static_cast<const float*>(dev_table), dtype,
+  return hip_status(la::launch_rope(t, 4, g, tc, static_cast<const float*>(dev_table), dtype,
                                     static_cast<hipStream_t>(stream), t_timing));
 }
 
@@ -287,7 +294,8 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
                             int32_t Hl, int32_t Wl, int32_t heads, int32_t head_dim,
                             la_dtype dtype, double theta, float q_scale, la_stream_t stream) {
   return rope_rolling(q_in, q_out, k_in, k_out, n_frames, f0, sink_k_in, sink_k_out, sink_delta,
-                      dev_table, Hl, Wl, heads, head_dim, dtype, theta, q_scale, nullptr, stream);
+                      dev_table, Hl, Wl, heads, head_dim, dtype, theta, q_scale, nullptr, nullptr,
+                      nullptr, stream);
 }
 
 size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads) {
@@ -622,12 +630,13 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
   float* q_cs = fuse_q ? static_cast<float*>(q_rot_ws) : nullptr;
   for (int l = 0; l < n_layers; ++l) {
     la_kvring* r = &rings[l];
-    // fused append: a staged ring takes the rotated K in its next slot directly
+    // fused append: a staged ring takes the rotated K in its next slot directly, and
+    // the same launch copies the block's V into the slot (the attention reads V from
+    // v_raw and no window slot is the next one, so staging V before the attention is
+    // safe); the append then only records the block
     void* k_rot = k_rot_ws;
-    if (append && r->nslots == r->W + 1) {
-      void* v_slot;
-      LA_TRY(la_kvring_next_slot(r, &k_rot, &v_slot));
-    }
+    void* v_stage = nullptr;
+    if (append && r->nslots == r->W + 1) LA_TRY(la_kvring_next_slot(r, &k_rot, &v_stage));
     const la::KernelTiming t_rope = span(6 * l), t_attn = span(6 * l + 2),
                            t_app = span(6 * l + 4);
     {
@@ -635,7 +644,7 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
       LA_TRY(rope_rolling(fuse_q ? nullptr : q_raw[l], fuse_q ? nullptr : q_rot_ws, k_raw[l],
                           k_rot, frames_per_block, f0, r->sink_k_raw, sink_k_rot_ws, sink_delta,
                           rope_table, Hl, Wl, r->heads, r->head_dim, (la_dtype)r->dtype, theta,
-                          q_scale, q_cs, stream));
+                          q_scale, q_cs, v_stage ? v_raw[l] : nullptr, v_stage, stream));
     }
     {
       TimedOp op(&t_attn);
@@ -650,8 +659,8 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
     }
     if (append) {
       TimedOp op(&t_app);
-      LA_TRY(la_kvcache_append_evict(r, k_rot, v_raw[l], block_id, r->noise_level, nullptr,
-                                     stream));
+      LA_TRY(la_kvcache_append_evict(r, k_rot, v_stage ? v_stage : v_raw[l], block_id,
+                                     r->noise_level, nullptr, stream));
     } else {
       LA_TRY(hip_status(la::timing_without_kernel(&t_app, hs)));
     }
@@ -692,9 +701,6 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
     const la_status w = validate_attn_ws(rings[0], scale, attn_ws, attn_ws_bytes);
     if (w != LA_OK) return w;
   }
-  if (timing_events)
-    for (int i = 0; i < 6 * n_layers + 2; ++i)
-      if (!timing_events[i]) return LA_ERR_INVALID_ARG;
   return enqueue_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out, q_rot_ws,
                        k_rot_ws, sink_k_rot_ws, sink_k_new, sink_v_new, rope_table, Hl, Wl,
                        frames_per_block, sink_delta, theta, scale, attn_ws, attn_ws_bytes, x, vel,
@@ -731,9 +737,6 @@ la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_
   for (const void* p : ws)
     if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
   if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
-  if (timing_events)
-    for (int i = 0; i < 6 * n_layers + 2; ++i)
-      if (!timing_events[i]) return LA_ERR_INVALID_ARG;
 
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -68,7 +68,10 @@ struct RopeTensor {
   // (the values a Q at the same positions, with scale cs_scale, is rotated with)
   float* cs_out;
   float cs_scale;
+  int32_t copy_only;  // 1: copy the rows unrotated (no cos/sin use)
 };
+// One launch serves up to this many tensors (rows of each in order).
+constexpr int kMaxRopeTensors = 4;
 
 struct RopeGeom {
   int32_t HW, Wl, Hl, heads, head_dim, tpairs, hpairs, wpairs;

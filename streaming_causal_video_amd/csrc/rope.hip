@@ -48,19 +48,23 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // ordinary stores, and no change inside the step).  Neither one workgroup per
 // several rows nor more threads per row was faster (measured).  In-place calls are
 // safe: a thread writes exactly the chunks it read.
+//
+// A tensor marked copy_only is copied as it is (the step stages the block's V in
+// the ring's next slot within the same launch).
 template <bool kBF16, int kNH>
 __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTensor t1,
-                                                          RopeTensor t2, RopeGeom g,
-                                                          RopeTemporal tc,
+                                                          RopeTensor t2, RopeTensor t3,
+                                                          RopeGeom g, RopeTemporal tc,
                                                           const float* __restrict__ table,
-                                                          int wg0, int wg1) {
+                                                          int wg0, int wg1, int wg2) {
   constexpr int kPPC = kBF16 ? 4 : 2;  // pairs per 16-byte chunk
   constexpr int kEB = kBF16 ? 2 : 4;   // element bytes
   const int bid = __builtin_amdgcn_workgroup_id_x();
   const int tid = __builtin_amdgcn_workitem_id_x();
-  const int which = bid < wg0 ? 0 : (bid < wg0 + wg1 ? 1 : 2);
-  const RopeTensor T = which == 0 ? t0 : (which == 1 ? t1 : t2);
-  const int tok = bid - (which == 0 ? 0 : (which == 1 ? wg0 : wg0 + wg1));
+  const int e1 = wg0 + wg1, e2 = e1 + wg2;
+  const int which = bid < wg0 ? 0 : (bid < e1 ? 1 : (bid < e2 ? 2 : 3));
+  const RopeTensor T = which == 0 ? t0 : (which == 1 ? t1 : (which == 2 ? t2 : t3));
+  const int tok = bid - (which == 0 ? 0 : (which == 1 ? wg0 : (which == 2 ? e1 : e2)));
   const int cpr = g.head_dim / (2 * kPPC);  // chunks per head row
   const int hg_n = kThreads / cpr;          // head groups
   const int ch = tid % cpr;
@@ -83,6 +87,20 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
   // The first pass's loads go out before the cos/sin lookups, so that one memory
   // latency covers both (the lookups' wait would otherwise come first).
   load_pass(0);
+  if (T.copy_only) {
+    for (int h0 = 0; h0 < g.heads; h0 += hg_n * kNH) {
+      if (h0 > 0) load_pass(h0);
+#pragma unroll
+      for (int k = 0; k < kNH; ++k) {
+        const int head = h0 + hg + k * hg_n;
+        if (head < g.heads) {
+          const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
+          __builtin_nontemporal_store(x[k], reinterpret_cast<u32x4_t*>(dst + off));
+        }
+      }
+    }
+    return;
+  }
 
   // cos/sin of this thread's kPPC pairs at (frame, h, w) of the token: the frame
   // band from the by-value rows, the h and w bands from the table (one load per
@@ -193,12 +211,12 @@ __global__ void rope_table_kernel(float* __restrict__ table, int Hl, int Wl, int
 
 template <bool kBF16>
 static void launch_rope_nh(int nh, dim3 grid, hipStream_t s, const RopeTensor* tt,
-                           const RopeGeom& g, const RopeTemporal& tc, const float* table, int wg0,
-                           int wg1, const KernelTiming* tm) {
+                           const RopeGeom& g, const RopeTemporal& tc, const float* table,
+                           const int* wg, const KernelTiming* tm) {
 #define LA_ROPE_NH(N)                                                                        \
   case N:                                                                                    \
     launch_kernel(tm, rope3d_kernel<kBF16, N>, grid, dim3(kThreads), 0, s, tt[0], tt[1],     \
-                  tt[2], g, tc, table, wg0, wg1);                                            \
+                  tt[2], tt[3], g, tc, table, wg[0], wg[1], wg[2]);                          \
     break;
   switch (nh) {
     LA_ROPE_NH(1) LA_ROPE_NH(2) LA_ROPE_NH(3) LA_ROPE_NH(4)
@@ -209,21 +227,21 @@ static void launch_rope_nh(int nh, dim3 grid, hipStream_t s, const RopeTensor* t
 
 hipError_t launch_rope(const RopeTensor* t, int nt, const RopeGeom& g, const RopeTemporal& tc,
                        const float* table, la_dtype dt, hipStream_t s, const KernelTiming* tm) {
-  RopeTensor tt[3] = {};
-  int wg[3] = {0, 0, 0};
-  for (int i = 0; i < nt && i < 3; ++i) {
+  RopeTensor tt[kMaxRopeTensors] = {};
+  int wg[kMaxRopeTensors] = {};
+  for (int i = 0; i < nt && i < kMaxRopeTensors; ++i) {
     tt[i] = t[i];
     if (t[i].in) wg[i] = t[i].tokens;
   }
-  const int total = wg[0] + wg[1] + wg[2];
+  const int total = wg[0] + wg[1] + wg[2] + wg[3];
   if (total == 0) return timing_without_kernel(tm, s);
   const int cpr = g.head_dim / (dt == LA_BF16 ? 8 : 4);
   const int hg_n = kThreads / cpr;
   const int nh = (g.heads + hg_n - 1) / hg_n;
   if (dt == LA_BF16)
-    launch_rope_nh<true>(nh, dim3(total), s, tt, g, tc, table, wg[0], wg[1], tm);
+    launch_rope_nh<true>(nh, dim3(total), s, tt, g, tc, table, wg, tm);
   else
-    launch_rope_nh<false>(nh, dim3(total), s, tt, g, tc, table, wg[0], wg[1], tm);
+    launch_rope_nh<false>(nh, dim3(total), s, tt, g, tc, table, wg, tm);
   return hipGetLastError();
 }
 

@@ -141,11 +141,12 @@ def test_step_rotates_q_in_the_attention_with_the_same_bits(L, shape_name):
 
 @pytest.mark.parametrize("case", ["mid_3_layers", "c2_1_layer"])
 def test_staged_rings_fuse_the_append_with_the_same_bits(L, case):
-    """Staged rings (W + 1 slots): la_denoise_step writes each layer's rotated K straight
-    into the ring's next slot and copies only V.  Outputs, and every window block's K
-    and V bytes, equal those of the plain rings (which rotate into a workspace and copy
-    both) bit for bit, through the sink replacement and W + 2 evictions; the oracle
-    checks the outputs at three blocks."""
+    """Staged rings (W + 1 slots): la_denoise_step's RoPE launch writes each layer's
+    rotated K straight into the ring's next slot and copies V there before the
+    attention, and the append only records the block.  Outputs, and every window
+    block's K and V bytes, equal those of the plain rings (which rotate into a workspace
+    and copy both after the attention) bit for bit, through the sink replacement and
+    W + 2 evictions; the oracle checks the outputs at three blocks."""
     t = torch()
     s = si.MID_BF16 if case == "mid_3_layers" else si.C2
     n_layers = 3 if case == "mid_3_layers" else 1
