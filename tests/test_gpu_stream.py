@@ -139,6 +139,41 @@ def test_step_rotates_q_in_the_attention_with_the_same_bits(L, shape_name):
         assert t.equal(out.view(t.int16), per_op.out.view(t.int16)), (shape_name, b)
 
 
+@pytest.mark.parametrize("heads,staged", [(1, False), (1, True), (2, False), (2, True)])
+def test_step_q_rotation_edge_heads(L, heads, staged):
+    """The smallest head counts: with one head the step rotates Q in the RoPE launch (Q's
+    cos/sin table, 512 bytes a token, would not fit the 256-byte rows of q_rot_ws); with
+    two the table fills q_rot_ws exactly.  Plain and staged rings, W + 2 blocks of a
+    ragged shape (390 rows: a partial query tile and partial key tiles in every segment),
+    each block's output equal to the per-op path bit for bit and to the oracle within
+    tolerance at three blocks."""
+    t = torch()
+    s = si.LayerShape(120 + heads, "bf16", heads=heads, head_dim=128, Hl=10, Wl=13, W=2)
+    stack, table = _stage(L, s, 1, staged=staged)
+    per_op = GpuLayerStream(s)
+    oracle = StreamOracle(s)
+    blk = (s.block_tokens, s.heads, s.head_dim)
+    out = t.empty(blk, dtype=t.bfloat16, device="cuda")
+    qws = t.empty(blk, dtype=t.bfloat16, device="cuda")
+    kws = t.empty(blk, dtype=t.bfloat16, device="cuda")
+    sws = t.empty((s.sink_tokens, s.heads, s.head_dim), dtype=t.bfloat16, device="cuda")
+    aws = L.AttnWorkspace(s.block_tokens, s.heads)
+    nsink = s.sink_tokens
+    last = s.W + 2
+    for b in range(1, last + 1):
+        q, k, v = per_op.block_dev(b)
+        L.la_denoise_step(stack.states, b, [q], [k], [v], [out], qws, kws, sws, table, s.Hl,
+                          s.Wl, FRAMES_PER_BLOCK, SINK_DELTA, THETA,
+                          scale=softmax_scale(s.head_dim), attn_ws=aws,
+                          sink_k_new=[k[:nsink]] if b == 1 else None,
+                          sink_v_new=[v[:nsink]] if b == 1 else None)
+        per_op.step(b)
+        t.cuda.synchronize()
+        assert t.equal(out.view(t.int16), per_op.out.view(t.int16)), (heads, staged, b)
+        if b in (1, 2, last):
+            check_attention(to_f64(out), oracle.block_output(b), f"heads {heads} block {b}")
+
+
 @pytest.mark.parametrize("case", ["mid_3_layers", "c2_1_layer"])
 def test_staged_rings_fuse_the_append_with_the_same_bits(L, case):
     """Staged rings (W + 1 slots): la_denoise_step's RoPE launch writes each layer's
