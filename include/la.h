@@ -231,12 +231,12 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
  * K/V at the block's own noise level).  For every head:
  *
  *     out = softmax(scale * Q K_all^T) V_all,
- *     K_all = [sink_k_rot ; cached blocks of r (oldest first) ; k_cur_rot]
- *     V_all = [r->sink_v  ; cached blocks of r               ; v_cur]
+ *     K_all = [sink_k_rot ; cached blocks of r ; k_cur_rot]
+ *     V_all = [r->sink_v  ; cached blocks of r ; v_cur]
  *
  * with no mask (the block sees itself bidirectionally; later blocks do not
- * exist yet).  Reads la_kvring_count(r) cached blocks; call it before
- * appending the current block.
+ * exist yet; the order of the keys does not change the attention).  Reads
+ * la_kvring_count(r) cached blocks; call it before appending the current block.
  *
  *   q_rot, k_cur_rot, v_cur, out : [n_q][heads][head_dim]; n_q = r->block_tokens.
  *       q_rot holds q_scale times the rotated query (q_scale as given to
@@ -262,7 +262,12 @@ la_status la_rope3d_rolling(const void* q_in, void* q_out, const void* k_in, voi
  *            softmax in base 2, bf16 output (round-to-nearest-even); head_dim ==
  *            128.  The products take Q times scale * log2(e) / q_scale rounded to
  *            bf16, or q_rot unchanged when that factor is 1 in float32 (q_scale ==
- *            scale * log2(e) rounded to float32).
+ *            scale * log2(e) rounded to float32).  The keys are visited as the
+ *            sink, then the cached blocks in slot (address) order, then the
+ *            current block, with blocks whose K and V both continue in memory
+ *            where the previous one ends (neighbouring slots; k_cur_rot and
+ *            v_cur staged in the ring's next slot) taken as one run: the result
+ *            is the same attention, rounded along that order.
  *   LA_F32 : float32 throughout; head_dim 64 or 128.
  *   Pointers 16-byte aligned; `out` must not alias an input.
  */
@@ -353,9 +358,10 @@ la_status la_fm_euler_step(float* x, const float* v, int64_t n, float dt, la_str
  * (la_kvring_init_staged) and without LA_STEP_ATTEND_ONLY, step 1's launch writes
  * the rotated K straight into the ring's next slot (la_kvring_next_slot) instead
  * of k_rot_ws and copies v_raw[l] into the same slot (no block of the window uses
- * that slot, and step 2 reads V from v_raw[l]); step 2 reads K there, and step 3
- * only records the block (nothing is left to copy).  The results and the window's
- * contents are the same bits as with k_rot_ws.
+ * that slot); step 2 reads the block's K and V there, and step 3 only records the
+ * block (nothing is left to copy).  The window's contents are the same bits as
+ * with k_rot_ws; the outputs are the same bits as la_block_attn_fwd given the
+ * slot's K and V.
  * Fused Q rotation (NOTES, Table 3, fused kernels; RoPE as in la_rope3d_rolling):
  * for bf16 rings with heads >= 2, step 1 rotates only K and the sink K and writes
  * the cos/sin of every block token's head_dim pairs, times q_scale (float32,

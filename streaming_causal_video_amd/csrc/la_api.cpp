@@ -87,7 +87,7 @@ size_t attn_ws_bytes(int n_q, int heads, int slots) {
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v16 fp8-v6"; }
+const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v6"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -349,19 +349,63 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
   segs.v[n] = r->sink_v;
   end += r->sink_tokens;
   segs.end[n++] = end;
-  // cached blocks, oldest first
   const int ns = ring_slots(r);
-  for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b) {
-    const int slot = (int)((b - 1) % ns);
-    segs.k[n] = static_cast<const char*>(r->k_slots) + slot * slot_bytes;
-    segs.v[n] = static_cast<const char*>(r->v_slots) + slot * slot_bytes;
+  if (r->dtype == LA_BF16) {
+    // The bf16 kernel tiles each segment on its own, so a segment's last tile is
+    // partial (at 4680 rows, 8 of its 64 keys valid).  Softmax attention does not
+    // depend on the order of the keys: the cached blocks are taken in slot (address)
+    // order, and segments whose K and V both continue where the previous one ends
+    // (neighbouring slots; the current block when the caller staged it in the ring's
+    // next slot) are joined, as long as the kernel's 32-bit byte offsets still reach
+    // past the joined segment's end.
+    bool in_window[LA_MAX_WINDOW + 1] = {};
+    for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b)
+      in_window[(b - 1) % ns] = true;
+    const size_t row_bytes = (size_t)r->heads * r->head_dim * elem_size(r->dtype);
+    int64_t rows = 0;  // rows of segment n - 1 when it may still grow
+    auto add = [&](const void* k, const void* v, int len) {
+      const bool joins =
+          n > 1 && static_cast<const char*>(segs.k[n - 1]) + rows * row_bytes == k &&
+          static_cast<const char*>(segs.v[n - 1]) + rows * row_bytes == v &&
+          (rows + len + 64) * (int64_t)row_bytes < ((int64_t)1 << 32);
+      end += len;
+      if (joins) {
+        rows += len;
+        segs.end[n - 1] = end;
+      } else {
+        rows = len;
+        segs.k[n] = k;
+        segs.v[n] = v;
+        segs.end[n++] = end;
+      }
+    };
+    // the current block staged in the ring's next slot (K and V) takes its place
+    // among the slots
+    const int next = (int)(r->last_block % ns);
+    const bool cur_in_slot =
+        !in_window[next] &&
+        k_cur_rot == static_cast<const char*>(r->k_slots) + next * slot_bytes &&
+        v_cur == static_cast<const char*>(r->v_slots) + next * slot_bytes;
+    if (cur_in_slot) in_window[next] = true;
+    for (int slot = 0; slot < ns; ++slot)
+      if (in_window[slot])
+        add(static_cast<const char*>(r->k_slots) + slot * slot_bytes,
+            static_cast<const char*>(r->v_slots) + slot * slot_bytes, r->block_tokens);
+    if (!cur_in_slot) add(k_cur_rot, v_cur, r->block_tokens);
+  } else {
+    // cached blocks, oldest first
+    for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b) {
+      const int slot = (int)((b - 1) % ns);
+      segs.k[n] = static_cast<const char*>(r->k_slots) + slot * slot_bytes;
+      segs.v[n] = static_cast<const char*>(r->v_slots) + slot * slot_bytes;
+      end += r->block_tokens;
+      segs.end[n++] = end;
+    }
+    segs.k[n] = k_cur_rot;
+    segs.v[n] = v_cur;
     end += r->block_tokens;
     segs.end[n++] = end;
   }
-  segs.k[n] = k_cur_rot;
-  segs.v[n] = v_cur;
-  end += r->block_tokens;
-  segs.end[n++] = end;
   segs.nseg = n;
   for (int i = 0, t = 0; i < n; ++i) {
     t += (segs.end[i] - (i ? segs.end[i - 1] : 0) + 63) / 64;
@@ -631,9 +675,8 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
   for (int l = 0; l < n_layers; ++l) {
     la_kvring* r = &rings[l];
     // fused append: a staged ring takes the rotated K in its next slot directly, and
-    // the same launch copies the block's V into the slot (the attention reads V from
-    // v_raw and no window slot is the next one, so staging V before the attention is
-    // safe); the append then only records the block
+    // the same launch copies the block's V into the slot (no window block uses that
+    // slot); the attention reads both there, and the append only records the block
     void* k_rot = k_rot_ws;
     void* v_stage = nullptr;
     if (append && r->nslots == r->W + 1) LA_TRY(la_kvring_next_slot(r, &k_rot, &v_stage));
@@ -648,12 +691,15 @@ la_status enqueue_stage(la_kvring* rings, int32_t n_layers, int64_t block_id,
     }
     {
       TimedOp op(&t_attn);
+      // a staged block is read from its slot (its K and V then continue the
+      // neighbouring slots, which the attention joins into one segment)
+      const void* v_cur = v_stage ? v_stage : v_raw[l];
       if (fuse_q)
-        LA_TRY(la::attn_fwd(r, q_raw[l], sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
+        LA_TRY(la::attn_fwd(r, q_raw[l], sink_k_rot_ws, k_rot, v_cur, r->block_tokens,
                             attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes, 0,
                             false, stream, t_timing, q_cs));
       else
-        LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot, v_raw[l], r->block_tokens,
+        LA_TRY(la_block_attn_fwd(r, q_rot_ws, sink_k_rot_ws, k_rot, v_cur, r->block_tokens,
                                  attn_out[l], nullptr, scale, q_scale, attn_ws, attn_ws_bytes,
                                  stream));
     }

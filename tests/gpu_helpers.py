@@ -112,10 +112,13 @@ class GpuLayerStream:
     """
 
     def __init__(self, shape: si.LayerShape, layer: int = 0, keep_lse: bool = False,
-                 fused: bool = True, workspace: bool = True):
+                 fused: bool = True, workspace: bool = True, staged: bool = False):
         """fused: RoPE writes Q times q_prescale and the attention takes it as given (the
         step's form); else the plain rotation and q_scale 1.  workspace: run the
-        attention's balanced schedule (bf16 only)."""
+        attention's balanced schedule (bf16 only).  staged: a ring of W + 1 slots whose
+        next slot receives the block's rotated K (from RoPE) and its V (a copy) before
+        the attention, which reads them there; the append then only records the block
+        (the layout of la_denoise_step's staged rings)."""
         import streaming_causal_video_amd as L
         t = torch()
         self.L = L
@@ -123,8 +126,9 @@ class GpuLayerStream:
         self.layer = layer
         self.dtype = t.bfloat16 if shape.dtype == "bf16" else t.float32
         s = shape
+        self.staged = staged
         self.ring = L.KVRing(s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, self.dtype,
-                             NOISE_LEVEL)
+                             NOISE_LEVEL, staged=staged)
         sk, sv = s.initial_sink(layer)
         self.ring.sink_k_raw.copy_(to_dev(sk))
         self.ring.sink_v.copy_(to_dev(sv))
@@ -154,19 +158,28 @@ class GpuLayerStream:
         L, s = self.L, self.shape
         q, k, v = self.block_dev(block)
         f0 = block_f0(block)
-        L.la_rope3d_rolling(q, self.q_rot, k, self.k_rot, FRAMES_PER_BLOCK, f0,
+        k_dst, v_cur = self.k_rot, v
+        if self.staged:
+            ka, va = L.la_kvring_next_slot(self.ring.state)
+            slot = (ka - self.ring.k_slots.data_ptr()) // self.ring.k_slots[0].nbytes
+            k_dst, v_cur = self.ring.k_slots[slot], self.ring.v_slots[slot]
+            assert k_dst.data_ptr() == ka and v_cur.data_ptr() == va
+            v_cur.copy_(v)
+        L.la_rope3d_rolling(q, self.q_rot, k, k_dst, FRAMES_PER_BLOCK, f0,
                             self.ring.sink_k_raw, self.sink_k_rot, SINK_DELTA, self.table, s.Hl,
                             s.Wl, s.heads, s.head_dim, THETA, q_scale=self.q_scale)
-        self.attend(v)
-        ev = L.la_kvcache_append_evict(self.ring.state, self.k_rot, v, block, NOISE_LEVEL)
+        self.attend(v_cur, k_dst)
+        ev = L.la_kvcache_append_evict(self.ring.state, k_dst, v_cur, block, NOISE_LEVEL)
         if block == 1:
             n = s.sink_tokens
             L.la_sink_replace(self.ring.state, k[:n], v[:n])
         return ev
 
-    def attend(self, v_cur):
-        """la_block_attn_fwd of the rotated Q/K in place over the ring (before the append)."""
-        self.L.la_block_attn_fwd(self.ring.state, self.q_rot, self.sink_k_rot, self.k_rot, v_cur,
+    def attend(self, v_cur, k_cur=None):
+        """la_block_attn_fwd of the rotated Q/K in place over the ring (before the append);
+        k_cur defaults to the rotated-K workspace."""
+        self.L.la_block_attn_fwd(self.ring.state, self.q_rot, self.sink_k_rot,
+                                 self.k_rot if k_cur is None else k_cur, v_cur,
                                  self.out, self.lse, scale=self.scale, q_scale=self.q_scale,
                                  workspace=self.ws)
 

@@ -112,13 +112,14 @@ def test_step_rotates_q_in_the_attention_with_the_same_bits(L, shape_name):
     """For bf16 rings la_denoise_step leaves Q's Rolling RoPE to the attention kernel:
     RoPE writes the block tokens' cos/sin (times q_scale) into q_rot_ws and the attention
     rotates the raw Q with them as it loads it.  At full size every output element
-    equals the per-op path's (la_rope3d_rolling of Q into a workspace, then
-    la_block_attn_fwd) bit for bit, over W + 2 blocks: the sink replacement, the ring
-    filling and evicting, and each block's own frame positions."""
+    equals the per-op path's (la_rope3d_rolling of Q into a workspace and of K into the
+    ring's next slot, V copied there, then la_block_attn_fwd) bit for bit, over W + 2
+    blocks: the sink replacement, the ring filling and evicting, and each block's own
+    frame positions."""
     t = torch()
     s = getattr(si, shape_name)
     stack, table = _stage(L, s, 1, staged=True)
-    per_op = GpuLayerStream(s)
+    per_op = GpuLayerStream(s, staged=True)
     blk = (s.block_tokens, s.heads, s.head_dim)
     out = t.empty(blk, dtype=t.bfloat16, device="cuda")
     qws = t.empty(blk, dtype=t.bfloat16, device="cuda")
@@ -145,12 +146,12 @@ def test_step_q_rotation_edge_heads(L, heads, staged):
     cos/sin table, 512 bytes a token, would not fit the 256-byte rows of q_rot_ws); with
     two the table fills q_rot_ws exactly.  Plain and staged rings, W + 2 blocks of a
     ragged shape (390 rows: a partial query tile and partial key tiles in every segment),
-    each block's output equal to the per-op path bit for bit and to the oracle within
-    tolerance at three blocks."""
+    each block's output equal to the per-op path on the same kind of ring bit for bit
+    and to the oracle within tolerance at three blocks."""
     t = torch()
     s = si.LayerShape(120 + heads, "bf16", heads=heads, head_dim=128, Hl=10, Wl=13, W=2)
     stack, table = _stage(L, s, 1, staged=staged)
-    per_op = GpuLayerStream(s)
+    per_op = GpuLayerStream(s, staged=staged)
     oracle = StreamOracle(s)
     blk = (s.block_tokens, s.heads, s.head_dim)
     out = t.empty(blk, dtype=t.bfloat16, device="cuda")
@@ -178,10 +179,12 @@ def test_step_q_rotation_edge_heads(L, heads, staged):
 def test_staged_rings_fuse_the_append_with_the_same_bits(L, case):
     """Staged rings (W + 1 slots): la_denoise_step's RoPE launch writes each layer's
     rotated K straight into the ring's next slot and copies V there before the
-    attention, and the append only records the block.  Outputs, and every window
-    block's K and V bytes, equal those of the plain rings (which rotate into a workspace
-    and copy both after the attention) bit for bit, through the sink replacement and
-    W + 2 evictions; the oracle checks the outputs at three blocks."""
+    attention, and the append only records the block.  Every window block's K and V
+    bytes equal those of the plain rings (which rotate into a workspace and copy both
+    after the attention) bit for bit, through the sink replacement and W + 2
+    evictions.  The outputs agree with the plain rings' within the attention bars (the
+    staged block and its neighbouring slots are one run of keys, so the sums are
+    rounded in another order), and the oracle checks them at three blocks."""
     t = torch()
     s = si.MID_BF16 if case == "mid_3_layers" else si.C2
     n_layers = 3 if case == "mid_3_layers" else 1
@@ -207,7 +210,7 @@ def test_staged_rings_fuse_the_append_with_the_same_bits(L, case):
                 sink_v_new=[d[2][:nsink] for d in dev] if b == 1 else None)
         t.cuda.synchronize()
         for l in range(n_layers):
-            assert t.equal(ws[0][l].view(t.int16), ws[1][l].view(t.int16)), (b, l)
+            check_attention(to_f64(ws[1][l]), to_f64(ws[0][l]), f"staged vs plain {b} {l}")
             for bid in range(max(1, b - s.W + 1), b + 1):
                 ps, ss = (bid - 1) % s.W, (bid - 1) % (s.W + 1)
                 assert int(plain.states[l].slot_block[ps]) == bid
