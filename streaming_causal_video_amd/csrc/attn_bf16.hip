@@ -38,9 +38,11 @@
 //    the scores and the P V blocks: the SIMD's other wave then fills the
 //    matrix core while this wave's exp2 chain gets the issue slots first.
 //  * Softmax in base 2 with the score scale folded into Q: the kernel takes Q
-//    already multiplied by c = scale * log2(e) (the RoPE kernel of the step
-//    emits it that way, rounded to bf16 once; a caller's plain Q is multiplied
-//    and rounded here when its Q fragments are loaded), and the running
+//    already multiplied by c = scale * log2(e), rounded to bf16 once (in the
+//    step the kRotQ instantiation loads the raw Q and rotates it with per-token
+//    cos/sin that already carry c, with the RoPE kernel's arithmetic; a caller's
+//    rotated but plain Q is multiplied and rounded here when its Q fragments are
+//    loaded), and the running
 //    reference m of each query enters the first score MFMA of a half as its C
 //    operand, so the accumulators leave the matrix core as c s - m and the
 //    probability of each score is a single v_exp_f32.  Probabilities are taken
@@ -64,8 +66,11 @@
 //    segment: its DMA uses one buffer descriptor whose record count ends at
 //    the segment's last row (rows past it load as zeros) and its missing keys
 //    are masked.  No per-row path for tiles that straddle two segments, and no
-//    per-tile segment search beyond one compare.  At 1560 + 5 x 4680 keys this
-//    computes 1.3 % masked keys; at 3520 + 5 x 10560 none.
+//    per-tile segment search beyond one compare.  The host joins segments that
+//    continue in memory (neighbouring ring slots), so in the step the window
+//    and the block are one segment: at 1560 + 5 x 4680 keys 0.2 % of the
+//    computed keys are masked (1.3 % with six segments); at 3520 + 5 x 10560
+//    none.
 //  * V stays key-major in LDS (64 rows of 128 dims, 256-byte pitch) and the A
 //    operand of the second product (V^T: 16 dims x 8 keys per lane) is read
 //    with two ds_read_b64_tr_b16: in each 16-lane group lane i receives, as
