@@ -68,7 +68,7 @@
 //    are masked.  No per-row path for tiles that straddle two segments, and no
 //    per-tile segment search beyond one compare.  The host joins segments that
 //    continue in memory (neighbouring ring slots), so in the step the window
-//    and the block are one segment: at 1560 + 5 x 4680 keys 0.2 % of the
+//    and the block are one segment: at 1560 + 5 x 4680 keys 0.3 % of the
 //    computed keys are masked (1.3 % with six segments); at 3520 + 5 x 10560
 //    none.
 //  * V stays key-major in LDS (64 rows of 128 dims, 256-byte pitch) and the A
