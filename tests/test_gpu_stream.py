@@ -107,7 +107,7 @@ def test_denoise_step_matches_oracle_and_per_op_path(L):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("shape_name", ["C2", "C5"])
+@pytest.mark.parametrize("shape_name", ["C2", "C3", "C5"])
 def test_step_rotates_q_in_the_attention_with_the_same_bits(L, shape_name):
     """For bf16 rings la_denoise_step leaves Q's Rolling RoPE to the attention kernel:
     RoPE writes the block tokens' cos/sin (times q_scale) into q_rot_ws and the attention
@@ -115,7 +115,8 @@ def test_step_rotates_q_in_the_attention_with_the_same_bits(L, shape_name):
     equals the per-op path's (la_rope3d_rolling of Q into a workspace and of K into the
     ring's next slot, V copied there, then la_block_attn_fwd) bit for bit, over W + 2
     blocks: the sink replacement, the ring filling and evicting, and each block's own
-    frame positions."""
+    frame positions.  C3's window (W = 8) makes the longest joined run of keys, nine
+    slots."""
     t = torch()
     s = getattr(si, shape_name)
     stack, table = _stage(L, s, 1, staged=True)
