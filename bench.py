@@ -761,10 +761,14 @@ def chain_main(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=6,
-                    help="untimed steps after the ring has filled (the first blocks after a "
-                         "cold start run up to 4 %% slower while the clock settles)")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20 for c4, c2 and c4fp8; 192 for c3, blocks "
+                         "9-200; 1000 for c5; 10 for the other workloads)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps after the ring has filled (default 20; 0 for c3).  "
+                         "After a cold start the first blocks run up to 4 %% slower while the "
+                         "clock settles, and six warm-up steps left the first timed one 3.7 %% "
+                         "slower than the last")
     ap.add_argument("--workload", choices=["c4", "c2", "c3", "c5", "chain", "c2fp8", "c4fp8",
                                            "refresh"],
                     default="c4")
@@ -773,8 +777,9 @@ def main():
                     help="layers per stage for the chain / refresh workloads (default 40)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--ring", choices=["staged", "plain"], default="staged",
-                    help="staged: W + 1 slots per ring, RoPE writes K into the next slot and the "
-                         "append copies only V (fused); plain: W slots, K and V copied")
+                    help="staged: W + 1 slots per ring, the RoPE launch writes K into the next "
+                         "slot and copies V there, the append only records the block (fused); "
+                         "plain: W slots, the append copies K and V")
     ap.add_argument("--attn-schedule", choices=["balanced", "grid"], default="balanced",
                     help="attention work schedule: persistent balanced grid with a workspace "
                          "(default) or one workgroup per query tile")
@@ -786,6 +791,12 @@ def main():
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py is single-process; WORLD_SIZE > 1 is not supported.", file=sys.stderr)
         return 2
+
+    default_steps = {"c4": 20, "c2": 20, "c4fp8": 20, "c3": 192, "c5": 1000}
+    if args.steps is None:
+        args.steps = default_steps.get(args.workload, 10)
+    if args.warmup is None:
+        args.warmup = 0 if args.workload == "c3" else 20
 
     # workloads with their own driver (they take --steps as given)
     if args.workload == "chain":
@@ -808,14 +819,11 @@ def main():
         geo = dict(Hl=30, Wl=52, W=8, H=40, d=128, n_layers=1)
         name = ("C3 one layer, window of 8 blocks, 200 streamed blocks: bf16 block attention "
                 "40x128, Nq 4680, Nk 43680 (+RoPE, append, Euler)")
-        if args.steps == 10:  # blocks 1..8 fill the ring; blocks 9..200 are timed
-            args.warmup, args.steps = 0, 192
+        # by default blocks 1..8 fill the ring and blocks 9..200 are timed
     elif args.workload == "c5":
         geo = dict(Hl=44, Wl=80, W=4, H=40, d=128, n_layers=1)
         name = ("C5 720p-shaped layer: 44x80 tokens/frame, Nq 10560, Nk 56320 (sink + 4 cached "
                 "blocks + block), streamed blocks")
-        if args.steps == 10:
-            args.steps = 1000
     else:
         raise AssertionError(args.workload)
     r = gpu_step_bench(args, **geo)
