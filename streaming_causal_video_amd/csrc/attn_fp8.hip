@@ -10,15 +10,21 @@
 // Design (gfx950-native):
 //  * 4 waves x 32 query rows per workgroup, 64-key tiles double-buffered in LDS,
 //    one barrier per tile, Q fragments and the output accumulator in registers.
-//    Two waves per SIMD (<= 256 registers, 39 KB of LDS per workgroup).  At
-//    three per SIMD (168 registers) the loop-invariant addresses spilled to
-//    scratch, and the reload after each barrier waited (one in-order counter)
-//    for the next tile's prefetch as well (1.82 ms against 1.58 ms at two per SIMD).
-//  * Tile loads are buffer loads from a scalar descriptor (segment base + tile
-//    row + head, record count = the segment's remaining bytes) with one lane
-//    offset for K and one for V; the other rows of a thread differ by uniform
-//    multiples of the row stride, passed as the scalar offset.  No 64-bit
-//    address registers, and a wrong offset reads zeros instead of faulting.
+//    Three waves per SIMD (<= 168 registers, 32 KB of LDS per workgroup, three
+//    workgroups per CU): with the tiles arriving by DMA the kernel needs no
+//    staging registers and fits 168 without spilling, and the third wave hides
+//    more of the LDS latency (10 % faster than two waves per SIMD with the tiles
+//    loaded through registers).
+//  * K and V tiles go global -> LDS by DMA (buffer_load ... lds), issued for the
+//    next tile right after the barrier: a DMA writes each wave's 1 KB
+//    contiguously, so tile rows have no padding (128-byte pitch) and each
+//    16-byte chunk c of a row sits at chunk c ^ swizzle(row), which keeps the
+//    fragment reads free of bank conflicts.  One scalar buffer descriptor per
+//    tile (segment base + tile row + head, record count = the segment's
+//    remaining bytes): rows past a segment's end read as zeros.
+//  * Each segment of the key table is tiled on its own (the last tile of a
+//    segment partial, its missing keys masked), so no tile straddles two
+//    segments.
 //  * Both products run on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, float32
 //    accumulate): S^T = K Q^T is 4 MFMAs per tile, O^T += V^T P^T another 4.
 //  * The MFMA takes A[i][k] and B[k][j] from lane bytes under one fixed (lane,
@@ -28,14 +34,13 @@
 //  * K rows are fed to the score MFMA in the order that makes accumulator row
 //    i of key block b hold key 32 ((i / 4) % 2) + 16 b + 4 (i / 8) + i % 4.
 //    Then lane l's 32 scores are keys 32 (l / 32) .. +31 in byte order, so P
-//    packs straight into the B operand of the second product.
-//  * V stays key-major in LDS (64 rows of 128 bytes, 160-byte pitch: the 8
-//    consecutive keys one half-wave reads land on disjoint banks) and the A
-//    operand of the second product (32 dims x 32 keys per lane) is read with
-//    four ds_read_b64_tr_b8: in each 16-lane group lane i receives, as byte j,
-//    byte i & 7 of the 8 bytes lane 2j + (i >> 3) addresses (measured on
-//    gfx950), so lanes addressing 8 dims of one key hand every lane the 8 keys
-//    of its dim.  The loader stores V rows as it loads them (no transpose).
+//    packs straight into the B operand of the second product.  The DMA places
+//    each key in that order directly.
+//  * V stays key-major in LDS and the A operand of the second product (32 dims
+//    x 32 keys per lane) is read with four ds_read_b64_tr_b8: in each 16-lane
+//    group lane i receives, as byte j, byte i & 7 of the 8 bytes lane
+//    2j + (i >> 3) addresses (measured on gfx950), so lanes addressing 8 dims
+//    of one key hand every lane the 8 keys of its dim.
 //  * Softmax in float32 with scale * dq * dk * log2(e) folded into the exponent;
 //    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
 //    of the subnormal range).
@@ -69,11 +74,10 @@ constexpr int kBufWord3 = 0x00020000;
 constexpr int BN = 64;   // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int KP = 144;  // K row pitch in LDS (bytes): 16 rows hit 16 disjoint bank quads
-constexpr int VP = 160;  // V row pitch in LDS (bytes), key-major: 8 consecutive rows, disjoint banks
-constexpr int KBUF = BN * KP;
-constexpr int VBUF = BN * VP;
-constexpr int STAGE = KBUF + VBUF;
+// K and V tiles in LDS: 64 rows of 128 bytes (no padding: a DMA writes each
+// wave's 1 KB contiguously), 16-byte chunks XOR-swizzled per row.
+constexpr int KBUF = BN * D;
+constexpr int VBUF = BN * D;
 constexpr float kPLift = 6.f;         // P is computed as exp2(s - m + 6)
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -86,29 +90,37 @@ __device__ __forceinline__ float swap_halves_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// LDS row of the K tile that holds key kk (inverse of the feed order above).
-__device__ __forceinline__ int k_lds_row(int kk) {
-  const int h = (kk >> 5) & 1, b = (kk >> 4) & 1, g = (kk >> 2) & 3, t = kk & 3;
-  return 32 * b + 8 * g + 4 * h + t;
+// Key held by LDS row R of a K tile (the rows are in the order that makes
+// accumulator row i of key block b hold key 32 ((i / 4) % 2) + 16 b + 4 (i / 8) + i % 4).
+__device__ __forceinline__ int k_row_key(int R) {
+  return 32 * ((R >> 2) & 1) + 16 * (R >> 5) + 4 * ((R >> 3) & 3) + (R & 3);
 }
-
-// 32 bytes from a 16-byte aligned address (two 16-byte reads)
-__device__ __forceinline__ i32x8_t ld32(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
-  return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-}
+// 16-byte chunk swizzles: chunk c of K row R sits at c ^ kswz(R); chunk c of V key
+// row k at c ^ vswz(k).  16 lanes reading one chunk of 16 consecutive K rows, and
+// 32 lanes reading two neighbouring chunks of 8 consecutive V keys, then cover the
+// 64 banks once.
+__device__ __forceinline__ int kswz(int R) { return (R >> 1) & 7; }
+__device__ __forceinline__ int vswz(int k) { return ((k >> 1) & 3) << 1; }
 
 __device__ __forceinline__ f32x16_t mma(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
-                          amdgpu_waves_per_eu(2, 2))) void
+                          amdgpu_waves_per_eu(3, 3))) void
 attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
-                float* __restrict__ lse, const AttnSegs segs, int nq, int nk, int heads,
+                float* __restrict__ lse, const AttnSegs segs, int nq, int heads,
                 float c2, float dv, float ln_scale, int qtiles, int nwg) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  // The K and V buffers of the two stages are separate objects, so that the compiler
+  // can tell a DMA into one stage from the fragment reads of the other.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[KBUF], lds_v0[VBUF], lds_k1[KBUF],
+      lds_v1[VBUF];
+  auto kbuf = [&](int buf) __attribute__((always_inline)) -> uint8_t* {
+    return buf ? lds_k1 : lds_k0;
+  };
+  auto vbuf = [&](int buf) __attribute__((always_inline)) -> uint8_t* {
+    return buf ? lds_v1 : lds_v0;
+  };
 
   // XCD-aware renumbering: consecutive logical ids on one XCD.
   const int pid = __builtin_amdgcn_workgroup_id_x();
@@ -125,14 +137,22 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t rs = (int64_t)heads * D;  // row stride in bytes
+  const uint32_t rs32 = (uint32_t)rs;
+  const uint32_t hoff = (uint32_t)(head * D);
+  const int ntiles = segs.tend[segs.nseg - 1];
 
   // Q^T B-operand fragments: lane holds bytes 64 ks + 32 hh .. +31 of its query row.
   const int qrow = qt * BM + wave * 32 + l32;
   i32x8_t qf[2];
   if (qrow < nq) {
-    const uint8_t* qp = q + qrow * rs + head * D + 32 * hh;
+    const uint8_t* qp = q + qrow * rs + hoff + 32 * hh;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qf[ks] = ld32(qp + 64 * ks);
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(qp + 64 * ks);
+      const uint4 b = *reinterpret_cast<const uint4*>(qp + 64 * ks + 16);
+      qf[ks] = i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z,
+                       (int)b.w};
+    }
   } else {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) qf[ks] = i32x8_t{};
@@ -146,113 +166,133 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
   const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
-  // Loader.  K and V alike: thread covers 16-byte chunk kc of key rows kr0 and
-  // kr0 + 32 (8 lanes read one 128-byte row).
-  const int kc = tid & 7;
-  const int kr0 = tid >> 3;
-  const int ntiles = (nk + BN - 1) / BN;
-  const uint32_t rs32 = (uint32_t)rs;
-  // Lane offset of the tile loads (K and V) relative to the tile's first row of
-  // this head; the other row of a thread is 32 row strides further (passed as the
-  // buffer loads' scalar offset).
-  const uint32_t koff = (uint32_t)kr0 * rs32 + (uint32_t)(kc * 16);
-  uint4 kreg[2];
-  uint4 vreg[2];
-  // Segment holding the first key of the tile being loaded, with its key range
-  // and base pointers kept in scalar registers: the segment table is read only
-  // when a tile crosses into the next segment (a scalar load would also wait
-  // for every LDS read in flight).
-  int seg = 0, seg_start = 0, seg_end = segs.end[0];
+  // DMA geometry.  Wave w fills LDS rows 16 w + 8 n + (lane >> 3) (n = 0, 1) of each
+  // tile; lane slot p = lane & 7 of a row receives chunk p ^ swizzle(row) of its key.
+  // K: LDS row R holds key k_row_key(R); V: row k holds key k.
+  uint32_t kdoff[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int R = 16 * wave + 8 * n + (lane >> 3);
+    kdoff[n] = (uint32_t)k_row_key(R) * rs32 + 16u * (uint32_t)((lane & 7) ^ kswz(R));
+  }
+  const int vk = 16 * wave + (lane >> 3);  // row of n = 0; n = 1 is 8 rows (same swizzle) on
+  const uint32_t vdoff = (uint32_t)vk * rs32 + 16u * (uint32_t)((lane & 7) ^ vswz(vk));
+
+  // Fragment reads.  K (A operand of S^T): row 32 b + l32, logical chunks 4 ks + 2 hh
+  // and + 1 (bytes 64 ks + 32 hh .. +31), each at its swizzled place.
+  const int ks_sw = kswz(l32);
+  uint32_t kro[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      kro[ks][e] = (uint32_t)(l32 * D + 16 * ((4 * ks + 2 * hh + e) ^ ks_sw));
+  // V^T (A operand of O^T): in each 16-lane group lane s addresses key
+  // 32 hh + 8 r + (s >> 1), dims 32 db + 16 ((lane >> 4) & 1) + 8 (s & 1) .. +7, i.e.
+  // chunk 2 db + ((lane >> 4) & 1) of that key at its swizzled place
+  const int s16 = lane & 15;
+  const int vsw = vswz(s16 >> 1);  // the key's swizzle (8 r and 32 hh leave it unchanged)
+  uint32_t vro[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    vro[db] = (uint32_t)((32 * hh + (s16 >> 1)) * D +
+                         16 * ((2 * db + ((lane >> 4) & 1)) ^ vsw) + 8 * (s16 & 1));
+
+  // Segment of the tile being loaded (scalar registers): each segment is tiled on
+  // its own, its last tile partial.
+  int seg = 0, seg_t1 = segs.tend[0], seg_len = segs.end[0], seg_t0 = 0;
   const uint8_t* seg_k = static_cast<const uint8_t*>(segs.k[0]);
   const uint8_t* seg_v = static_cast<const uint8_t*>(segs.v[0]);
-
-  auto gload = [&](int tile) {
-    const int t0 = tile * BN;
-    while (t0 >= seg_end) {
+  uint32_t sbase = 0, nbytes = 0;
+  int valid = BN;
+  auto locate = [&](int tile) __attribute__((always_inline)) {
+    while (tile >= seg_t1) {
+      seg_len = segs.end[seg + 1] - segs.end[seg];
       ++seg;
-      seg_start = seg_end;
-      seg_end = segs.end[seg];
+      seg_t0 = seg_t1;
+      seg_t1 = segs.tend[seg];
       seg_k = static_cast<const uint8_t*>(segs.k[seg]);
       seg_v = static_cast<const uint8_t*>(segs.v[seg]);
     }
-    if (t0 + BN <= seg_end) {
-      // whole tile inside one segment: buffer loads from a scalar base with the
-      // precomputed 32-bit offsets (no 64-bit address registers); the record
-      // count ends the descriptor at the segment's end
-      const uint32_t sbase = (uint32_t)(t0 - seg_start) * rs32 + (uint32_t)(head * D);
-      const uint32_t nbytes = (uint32_t)(seg_end - t0) * rs32 - (uint32_t)(head * D);
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff, 32 * i * rs32, 0);
-        kreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, koff, 32 * i * rs32, 0);
-        vreg[i] = make_uint4(x[0], x[1], x[2], x[3]);
-      }
-    } else {
-      // straddles a segment boundary or runs past the last key: per-row lookup,
-      // rows past the last key are clamped to it (their scores are masked)
-      auto row_base = [&](int r, bool is_v) -> const uint8_t* {
-        const int key = min(t0 + r, nk - 1);
-        int s = seg;
-        while (key >= segs.end[s]) ++s;
-        const int st = s ? segs.end[s - 1] : 0;
-        return static_cast<const uint8_t*>(is_v ? segs.v[s] : segs.k[s]) +
-               (int64_t)(key - st) * rs + head * D;
-      };
-      kreg[0] = *reinterpret_cast<const uint4*>(row_base(kr0, false) + kc * 16);
-      kreg[1] = *reinterpret_cast<const uint4*>(row_base(kr0 + 32, false) + kc * 16);
-      vreg[0] = *reinterpret_cast<const uint4*>(row_base(kr0, true) + kc * 16);
-      vreg[1] = *reinterpret_cast<const uint4*>(row_base(kr0 + 32, true) + kc * 16);
-    }
+    const int r0 = (tile - seg_t0) * BN;
+    valid = seg_len - r0 < BN ? seg_len - r0 : BN;
+    sbase = (uint32_t)r0 * rs32 + hoff;
+    nbytes = (uint32_t)(seg_len - r0) * rs32 - hoff;
   };
-  auto lstore = [&](int buf) {
-    uint8_t* kb = lds + buf * STAGE;
-    uint8_t* vt = kb + KBUF;
+  auto kload = [&](int buf) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(seg_k + sbase), 0, nbytes, kBufWord3);
+    uint8_t* kb = kbuf(buf);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4*>(kb + k_lds_row(kr0 + 32 * i) * KP + kc * 16) = kreg[i];
+    for (int n = 0; n < 2; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          kr, (__attribute__((address_space(3))) void*)(kb + (16 * wave + 8 * n) * D), 16,
+          kdoff[n], 0, 0, 0);
+  };
+  auto vload = [&](int buf) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(seg_v + sbase), 0, nbytes, kBufWord3);
+    uint8_t* vb = vbuf(buf);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4*>(vt + (kr0 + 32 * i) * VP + kc * 16) = vreg[i];
+    for (int n = 0; n < 2; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vr, (__attribute__((address_space(3))) void*)(vb + (16 * wave + 8 * n) * D), 16,
+          vdoff, 8 * n * rs32, 0, 0);
+  };
+  auto kvload = [&](int buf) __attribute__((always_inline)) {
+    kload(buf);
+    vload(buf);
   };
 
-  gload(0);
-  // One 64-key tile j from LDS buffer `cur` (its K/V registers are stored there
-  // first, then tile j + 1 is loaded into registers).  The loop runs two tiles per
-  // trip so that both buffers are compile-time constants (immediate LDS offsets).
+  // Zero both V buffers once: the rows of a segment's partial last tile past its end
+  // are masked (P = 0 exactly) but still enter P V, so they must hold finite codes;
+  // the DMA leaves either zeros there (rows outside the buffer descriptor) or the V
+  // rows of an earlier tile.
+#pragma unroll
+  for (int i = 0; i < VBUF / (16 * NTHREADS); ++i) {
+    reinterpret_cast<uint4*>(lds_v0)[i * NTHREADS + tid] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(lds_v1)[i * NTHREADS + tid] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  locate(0);
+  int valid_next = valid;
+  kvload(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the first tile's DMA has landed
+
+  // One 64-key tile j from LDS buffer `cur` while tile j + 1 is staged into
+  // 1 - cur.  The loop runs two tiles per trip so that both buffers are
+  // compile-time constants (immediate LDS offsets).
   auto tile = [&](const int j, const int cur) __attribute__((always_inline)) {
-    lstore(cur);
-    if (j + 1 < ntiles) gload(j + 1);
     __syncthreads();
-    const uint8_t* kb = lds + cur * STAGE;
-    // V operand by transposing reads: in each 16-lane group lane s addresses key
-    // 32 hh + 8 r + (s >> 1), dims 32 db + 16 ((lane >> 4) & 1) + 8 (s & 1) .. +7
-    const uint8_t* vt = kb + KBUF + (32 * hh + ((lane & 15) >> 1)) * VP + 16 * ((lane >> 4) & 1) +
-                        8 * (lane & 1);
+    const int nvalid = valid_next;
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      locate(j + 1);
+      valid_next = valid;
+      kvload(1 - cur);
+    }
+    const uint8_t* kb = kbuf(cur);
+    const uint8_t* vb = vbuf(cur);
 
-    // S^T for the two 32-row key blocks: A = LDS row 32 b + lane % 32, bytes 64 ks + 32 hh ..
+    // S^T for the two 32-row key blocks: A = LDS row 32 b + l32, bytes 64 ks + 32 hh ..
     f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const i32x8_t a = ld32(kb + (32 * b + l32) * KP + 64 * ks + 32 * hh);
+        const uint4 x0 = *reinterpret_cast<const uint4*>(kb + b * 32 * D + kro[ks][0]);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(kb + b * 32 * D + kro[ks][1]);
+        const i32x8_t a = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                           (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         st[b] = mma(a, qf[ks], st[b]);
       }
-    if ((j + 1) * BN > nk) {
-      // last tile: mask keys past the end (st[b][r] holds key 32 hh + 16 b + r)
+    if (__builtin_expect(nvalid < BN, 0)) {
+      // the last tile of a segment: st[b][r] holds key 32 hh + 16 b + r of the tile
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (j * BN + 32 * hh + 16 * b + r >= nk) st[b][r] = -INFINITY;
+          if (32 * hh + 16 * b + r >= nvalid) st[b][r] = -INFINITY;
     }
 
     // P^T fragment against the current reference max: byte 16 b + r = key
@@ -301,11 +341,13 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
       i32x2_t part[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        part[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vt + 8 * r * VP + 32 * db));
+        part[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2_t*)(vb + vro[db] + 8 * r * D));
       const i32x8_t a = {part[0][0], part[0][1], part[1][0], part[1][1],
                          part[2][0], part[2][1], part[3][0], part[3][1]};
       o[db] = mma(a, pf, o[db]);
     }
+    if (more) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile has landed
   };
   for (int j = 0; j < ntiles; j += 2) {
     tile(j, 0);
@@ -334,10 +376,11 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
 hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, float scale, float dq, float dk, float dv,
                            hipStream_t s, const KernelTiming* tm) {
+  (void)nk;
   const int qtiles = (nq + BM - 1) / BM;
   const float c2 = scale * dq * dk * 1.4426950408889634f;
   launch_kernel(tm, attn_fp8_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
-                static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq, nk,
+                static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
                 heads, c2, dv, 0.69314718055994531f, qtiles, qtiles * heads);
   return hipGetLastError();
 }

@@ -87,7 +87,7 @@ size_t attn_ws_bytes(int n_q, int heads, int slots) {
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v6"; }
+const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v7"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -519,6 +519,10 @@ la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* 
   end += r->block_tokens;
   segs.end[n++] = end;
   segs.nseg = n;
+  for (int i = 0, t = 0; i < n; ++i) {
+    t += (segs.end[i] - (i ? segs.end[i - 1] : 0) + 63) / 64;
+    segs.tend[i] = t;
+  }
   return hip_status(la::launch_attn_fp8(q8, out, lse_or_null, segs, n_q, end, r->heads, scale,
                                         dq, dk, dv, static_cast<hipStream_t>(stream), t_timing));
 }
