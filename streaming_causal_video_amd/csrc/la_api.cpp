@@ -87,7 +87,7 @@ size_t attn_ws_bytes(int n_q, int heads, int slots) {
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v7"; }
+const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v8"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -307,6 +307,68 @@ size_t la_attn_workspace_bytes(int32_t n_q, int32_t heads) {
 
 }  // extern "C"
 
+namespace {
+
+// Segment table of an attention call for the kernels that tile each segment on its
+// own (bf16, e4m3), whose last tile is then partial (at 4680 rows, 8 of its 64 keys
+// valid): the sink, then the cached blocks in slot (address) order -- softmax
+// attention does not depend on the order of the keys -- then the current block.
+// Segments whose K and V both continue where the previous one ends (neighbouring
+// slots; the current block when the caller staged it in the ring's next slot, where
+// it takes its place among the slots) are joined, as long as the kernels' 32-bit byte
+// offsets still reach past the joined segment's end.  Fills segs (with the tile ends
+// tend) and returns the number of keys.
+int joined_segments(const la_kvring* r, int count, const void* sink_k, const void* sink_v,
+                    const void* k_cur, const void* v_cur, la::AttnSegs& segs) {
+  memset(&segs, 0, sizeof(segs));
+  const size_t row_bytes = (size_t)r->heads * r->head_dim * elem_size(r->dtype);
+  const size_t slot_bytes = (size_t)r->block_tokens * row_bytes;
+  int n = 0, end = 0;
+  int64_t rows = 0;  // rows of segment n - 1 while it may still grow
+  auto add = [&](const void* k, const void* v, int len, bool may_join) {
+    const bool joins =
+        may_join && n > 0 && static_cast<const char*>(segs.k[n - 1]) + rows * row_bytes == k &&
+        static_cast<const char*>(segs.v[n - 1]) + rows * row_bytes == v &&
+        (rows + len + 64) * (int64_t)row_bytes < ((int64_t)1 << 32);
+    end += len;
+    if (joins) {
+      rows += len;
+      segs.end[n - 1] = end;
+    } else {
+      rows = len;
+      segs.k[n] = k;
+      segs.v[n] = v;
+      segs.end[n++] = end;
+    }
+  };
+  add(sink_k, sink_v, r->sink_tokens, false);
+  const int ns = ring_slots(r);
+  bool in_window[LA_MAX_WINDOW + 1] = {};
+  for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b)
+    in_window[(b - 1) % ns] = true;
+  const int next = (int)(r->last_block % ns);
+  const bool cur_in_slot = !in_window[next] &&
+                           k_cur == static_cast<const char*>(r->k_slots) + next * slot_bytes &&
+                           v_cur == static_cast<const char*>(r->v_slots) + next * slot_bytes;
+  if (cur_in_slot) in_window[next] = true;
+  bool first = true;  // the first cached run never joins the sink
+  for (int slot = 0; slot < ns; ++slot)
+    if (in_window[slot]) {
+      add(static_cast<const char*>(r->k_slots) + slot * slot_bytes,
+          static_cast<const char*>(r->v_slots) + slot * slot_bytes, r->block_tokens, !first);
+      first = false;
+    }
+  if (!cur_in_slot) add(k_cur, v_cur, r->block_tokens, !first);
+  segs.nseg = n;
+  for (int i = 0, t = 0; i < n; ++i) {
+    t += (segs.end[i] - (i ? segs.end[i - 1] : 0) + 63) / 64;
+    segs.tend[i] = t;
+  }
+  return end;
+}
+
+}  // namespace
+
 namespace la {
 
 la_status status_of(hipError_t e) { return hip_status(e); }
@@ -341,59 +403,21 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
     return LA_ERR_SHAPE;
 
   la::AttnSegs segs;
-  memset(&segs, 0, sizeof(segs));
-  const size_t slot_bytes =
-      (size_t)r->block_tokens * r->heads * r->head_dim * elem_size(r->dtype);
-  int n = 0, end = 0;
-  segs.k[n] = sink_k_rot;
-  segs.v[n] = r->sink_v;
-  end += r->sink_tokens;
-  segs.end[n++] = end;
-  const int ns = ring_slots(r);
+  int end;
   if (r->dtype == LA_BF16) {
-    // The bf16 kernel tiles each segment on its own, so a segment's last tile is
-    // partial (at 4680 rows, 8 of its 64 keys valid).  Softmax attention does not
-    // depend on the order of the keys: the cached blocks are taken in slot (address)
-    // order, and segments whose K and V both continue where the previous one ends
-    // (neighbouring slots; the current block when the caller staged it in the ring's
-    // next slot) are joined, as long as the kernel's 32-bit byte offsets still reach
-    // past the joined segment's end.
-    bool in_window[LA_MAX_WINDOW + 1] = {};
-    for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b)
-      in_window[(b - 1) % ns] = true;
-    const size_t row_bytes = (size_t)r->heads * r->head_dim * elem_size(r->dtype);
-    int64_t rows = 0;  // rows of segment n - 1 when it may still grow
-    auto add = [&](const void* k, const void* v, int len) {
-      const bool joins =
-          n > 1 && static_cast<const char*>(segs.k[n - 1]) + rows * row_bytes == k &&
-          static_cast<const char*>(segs.v[n - 1]) + rows * row_bytes == v &&
-          (rows + len + 64) * (int64_t)row_bytes < ((int64_t)1 << 32);
-      end += len;
-      if (joins) {
-        rows += len;
-        segs.end[n - 1] = end;
-      } else {
-        rows = len;
-        segs.k[n] = k;
-        segs.v[n] = v;
-        segs.end[n++] = end;
-      }
-    };
-    // the current block staged in the ring's next slot (K and V) takes its place
-    // among the slots
-    const int next = (int)(r->last_block % ns);
-    const bool cur_in_slot =
-        !in_window[next] &&
-        k_cur_rot == static_cast<const char*>(r->k_slots) + next * slot_bytes &&
-        v_cur == static_cast<const char*>(r->v_slots) + next * slot_bytes;
-    if (cur_in_slot) in_window[next] = true;
-    for (int slot = 0; slot < ns; ++slot)
-      if (in_window[slot])
-        add(static_cast<const char*>(r->k_slots) + slot * slot_bytes,
-            static_cast<const char*>(r->v_slots) + slot * slot_bytes, r->block_tokens);
-    if (!cur_in_slot) add(k_cur_rot, v_cur, r->block_tokens);
+    end = joined_segments(r, count, sink_k_rot, r->sink_v, k_cur_rot, v_cur, segs);
   } else {
-    // cached blocks, oldest first
+    // the float32 kernel: the sink, the cached blocks oldest first, the current block
+    memset(&segs, 0, sizeof(segs));
+    const size_t slot_bytes =
+        (size_t)r->block_tokens * r->heads * r->head_dim * elem_size(r->dtype);
+    int n = 0;
+    end = 0;
+    segs.k[n] = sink_k_rot;
+    segs.v[n] = r->sink_v;
+    end += r->sink_tokens;
+    segs.end[n++] = end;
+    const int ns = ring_slots(r);
     for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b) {
       const int slot = (int)((b - 1) % ns);
       segs.k[n] = static_cast<const char*>(r->k_slots) + slot * slot_bytes;
@@ -405,11 +429,7 @@ la_status attn_fwd(const la_kvring* r, const void* q_rot, const void* sink_k_rot
     segs.v[n] = v_cur;
     end += r->block_tokens;
     segs.end[n++] = end;
-  }
-  segs.nseg = n;
-  for (int i = 0, t = 0; i < n; ++i) {
-    t += (segs.end[i] - (i ? segs.end[i - 1] : 0) + 63) / 64;
-    segs.tend[i] = t;
+    segs.nseg = n;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -499,30 +519,7 @@ la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* 
   if (seg_rows * r->heads * r->head_dim >= ((int64_t)1 << 32)) return LA_ERR_SHAPE;
 
   la::AttnSegs segs;
-  memset(&segs, 0, sizeof(segs));
-  const size_t slot_bytes = (size_t)r->block_tokens * r->heads * r->head_dim;
-  int n = 0, end = 0;
-  segs.k[n] = sink_k8;
-  segs.v[n] = sink_v8;
-  end += r->sink_tokens;
-  segs.end[n++] = end;
-  const int ns = ring_slots(r);
-  for (int64_t b = r->last_block - count + 1; b <= r->last_block; ++b) {
-    const int slot = (int)((b - 1) % ns);
-    segs.k[n] = static_cast<const char*>(r->k_slots) + slot * slot_bytes;
-    segs.v[n] = static_cast<const char*>(r->v_slots) + slot * slot_bytes;
-    end += r->block_tokens;
-    segs.end[n++] = end;
-  }
-  segs.k[n] = k8_cur;
-  segs.v[n] = v8_cur;
-  end += r->block_tokens;
-  segs.end[n++] = end;
-  segs.nseg = n;
-  for (int i = 0, t = 0; i < n; ++i) {
-    t += (segs.end[i] - (i ? segs.end[i - 1] : 0) + 63) / 64;
-    segs.tend[i] = t;
-  }
+  const int end = joined_segments(r, count, sink_k8, sink_v8, k8_cur, v8_cur, segs);
   return hip_status(la::launch_attn_fp8(q8, out, lse_or_null, segs, n_q, end, r->heads, scale,
                                         dq, dk, dv, static_cast<hipStream_t>(stream), t_timing));
 }

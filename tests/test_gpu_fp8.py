@@ -333,9 +333,11 @@ def oracle_fp8_step_block(shape, layer, b, dq, dk, dv):
 def test_fp8_denoise_step_matches_oracle(L):
     """la_denoise_step_fp8 over 2 layers and W + 2 blocks (sink replacement after block 1,
     evictions, an Euler step per block): each layer's output against the oracle's e4m3
-    attention of the rotated, bf16-rounded and quantised operands (the fp8 bars above);
-    staged rings give the same bits as plain ones; the window's K/V codes equal the
-    oracle's except where RoPE's bf16 rounding differs by one ulp (then by one code)."""
+    attention of the rotated, bf16-rounded and quantised operands (the fp8 bars above),
+    for staged and for plain rings (staged, the block and the window are one run of
+    keys, so the sums are rounded along another order than plain rings'); the latent is
+    the same bits; the window's K/V codes equal the oracle's except where RoPE's bf16
+    rounding differs by one ulp (then by one code)."""
     t = torch()
     s = si.SMALL_BF16
     n_layers = 2
@@ -374,9 +376,9 @@ def test_fp8_denoise_step_matches_oracle(L):
                 x=xs[m], vel=vel, dt=-0.25)
         t.cuda.synchronize()
         for l in range(n_layers):
-            assert t.equal(outs["staged"][l].view(t.int16), outs["plain"][l].view(t.int16)), (b, l)
             out, lse, a, vmax, (k8, v8) = oracle_fp8_step_block(s, l, b, dq, dk, dv)
             r = check_fp8(to_f64(outs["staged"][l]), out, a, vmax, f"fp8 step layer {l} block {b}")
+            check_fp8(to_f64(outs["plain"][l]), out, a, vmax, f"fp8 step plain {l} block {b}")
             for m, st in stacks.items():
                 slot = (b - 1) % st.states[l].nslots
                 assert int(st.states[l].slot_block[slot]) == b
