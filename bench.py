@@ -64,7 +64,16 @@ def attn_flops(nq, nk, d, h):
 
 
 # --------------------------------------------------------------------------- GPU
-FP8_SCALE = 5.0 / 448.0  # per-tensor e4m3 scale of Q, K and V: |x| = 5 maps to 448
+FP8_SCALE = 5.0 / 448.0  # per-tensor e4m3 scale of K and V: |x| = 5 maps to 448
+
+
+def fp8_factors(d):
+    """(dq, dk, dv) of the e4m3 workloads: K and V at 5/448; Q at the least factor >= 5/448
+    for which the logit factor scale dq dk log2(e) is a power of two (the attention's
+    faster path; |q| up to at least 5 still maps into the e4m3 range)."""
+    import streaming_causal_video_amd as L
+    dq = L.la_fp8_q_factor_pow2(d ** -0.5, FP8_SCALE, FP8_SCALE)
+    return dq, FP8_SCALE, FP8_SCALE
 
 
 def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
@@ -99,6 +108,7 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
     L.la_rope_table_fill(table, Hl, Wl, d, THETA)
     aws = L.AttnWorkspace(bt, H) if args.attn_schedule == "balanced" and not fp8 else None
     if fp8:
+        fdq, fdk, fdv = fp8_factors(d)
         u8 = lambda shp: torch.empty(shp, dtype=torch.uint8, device=dev)
         q8 = u8((bt, H, d))
         k8, v8 = (None, None) if staged else (u8((bt, H, d)), u8((bt, H, d)))
@@ -118,7 +128,7 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
         if fp8:
             L.la_denoise_step_fp8(stack.states, b, q, k, v, outs, qws, kws, sws, q8, k8, v8, sk8,
                                   sv8, table, Hl, Wl, FRAMES, DELTA, THETA, scale=d ** -0.5,
-                                  dq=FP8_SCALE, dk=FP8_SCALE, dv=FP8_SCALE, sink_k_new=skn,
+                                  dq=fdq, dk=fdk, dv=fdv, sink_k_new=skn,
                                   sink_v_new=svn, x=x, vel=vels[e] if with_euler else None,
                                   dt=DT, timing_events=events)
             return
@@ -524,23 +534,22 @@ def gpu_fp8_attn_bench(args, Hl, Wl, W, H, d):
     nk = st + (W + 1) * bt
     gen = torch.Generator(device=dev)
     gen.manual_seed(99)
-    sc = 5.0 / 448.0
-    inv = float(np.float32(1.0) / np.float32(sc))
+    dq, dk, dv = fp8_factors(d)
 
-    def q8(n):
+    def q8(n, f):
         x = torch.randn((n, H, d), device=dev, dtype=torch.float32, generator=gen).to(torch.bfloat16)
         out = torch.empty((n, H, d), dtype=torch.uint8, device=dev)
-        L.la_quantize_fp8(x, out, inv)
+        L.la_quantize_fp8(x, out, float(np.float32(1.0) / np.float32(f)))
         return out
 
     ring = L.KVRing(W, bt, st, H, d, torch.uint8, NOISE)
     for b in range(1, W + 1):
-        L.la_kvcache_append_evict(ring.state, q8(bt), q8(bt), b, NOISE)
-    q, k, v, sk, sv = q8(bt), q8(bt), q8(bt), q8(st), q8(st)
+        L.la_kvcache_append_evict(ring.state, q8(bt, dk), q8(bt, dv), b, NOISE)
+    q, k, v, sk, sv = q8(bt, dq), q8(bt, dk), q8(bt, dv), q8(st, dk), q8(st, dv)
     out = torch.empty((bt, H, d), dtype=torch.bfloat16, device=dev)
 
     def run():
-        L.la_block_attn_fwd_fp8(ring.state, q, sk, sv, k, v, out, sc, sc, sc, scale=d ** -0.5)
+        L.la_block_attn_fwd_fp8(ring.state, q, sk, sv, k, v, out, dq, dk, dv, scale=d ** -0.5)
 
     for _ in range(args.warmup + 3):
         run()
@@ -583,7 +592,8 @@ def fp8_main(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8-e4m3",
-        "data": "synthetic N(0,1) Q/K/V quantised to e4m3 (per-tensor scale 5/448), resident in HBM",
+        "data": ("synthetic N(0,1) Q/K/V quantised to e4m3 (per-tensor factors: K, V 5/448, Q the "
+                 "least >= 5/448 with a power-of-two logit factor), resident in HBM"),
         "config": {"workload": "C2 e4m3 block attention 40x128, Nq 4680, Nk 24960 (W=4 e4m3 ring)",
                    "heads": geo["H"], "head_dim": geo["d"], "nq": r["nq"], "nk": r["nk"]},
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_FP8_TFLOPS,
@@ -615,7 +625,8 @@ def c4fp8_main(args):
         "vs_baseline": None,
         "dtype": "fp8-e4m3",
         "data": ("synthetic N(0,1) Q/K/V (bf16), sinks, latent and velocity resident in HBM; "
-                 "Q, K, V quantised to e4m3 with per-tensor scale 5/448"),
+                 "Q, K, V quantised to e4m3 with per-tensor factors (K, V 5/448, Q the least "
+                 ">= 5/448 with a power-of-two logit factor)"),
         "config": {"workload": ("C4 denoise step on e4m3 rings: 40 layers x (3D Rolling RoPE + "
                                 "e4m3 quantisation + e4m3 block attention 40x128, Nq 4680, Nk "
                                 "24960 + ring append/evict, W=4) + Euler on fp32 16x3x60x104"),

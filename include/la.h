@@ -501,11 +501,30 @@ la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t 
  * <= 2^-4 per probability); the row sum that normalises the output is taken
  * from the same rounded probabilities.
  * Pointers 16-byte aligned (lse 4-byte); factors and scale > 0 and finite.
+ * When the logit factor scale * dq * dk * log2(e), evaluated in float32 in that
+ * order, is a power of two 2^e (-127 <= e <= 127), the kernel applies it through
+ * the score MFMA's operand scale and forms each score's exponent inside the MFMA
+ * (no multiply-add per score; la_fp8_q_factor_pow2 picks such a dq); the result
+ * is the same function, rounded in another order.
  */
 la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* sink_k8,
                                 const void* sink_v8, const void* k8_cur, const void* v8_cur,
                                 int32_t n_q, void* out, float* lse_or_null, float scale,
                                 float dq, float dk, float dv, la_stream_t stream);
+
+/*
+ * la_fp8_q_factor_pow2 - the least float dq >= dq_min for which the e4m3
+ * attention's logit factor scale * dq * dk * log2(e) (float32, in that order) is a
+ * power of two 2^e with -127 <= e <= 127, in *dq_out: quantising Q with that dq
+ * (la_quantize_fp8 with inv_scale 1 / dq) lets la_block_attn_fwd_fp8 and
+ * la_denoise_step_fp8 take their faster path.  The FP8 scaling recipe is the
+ * caller's choice (NOTES, Table 3 names FP8 without one): a dq at most about twice
+ * dq_min keeps Q's range (448 dq) at least that of dq_min.  Host-only: no GPU call.
+ *   scale, dk, dq_min : > 0 and finite (else LA_ERR_INVALID_ARG).
+ *   dq_out            : non-NULL; written only on LA_OK.
+ * LA_ERR_INVALID_ARG also when no such float exists (the factor overflows).
+ */
+la_status la_fp8_q_factor_pow2(float scale, float dk, float dq_min, float* dq_out);
 
 /*
  * One stage of a timestep-forcing chain (la_denoise_chain): the per-layer

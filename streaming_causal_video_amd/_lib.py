@@ -29,6 +29,7 @@ EXPORTED = [
     "la_block_attn_fwd", "la_kvcache_append_evict", "la_sink_replace", "la_fm_euler_step",
     "la_denoise_step", "la_denoise_chain", "la_quantize_fp8", "la_block_attn_fwd_fp8",
     "la_attn_workspace_bytes", "la_block_attn_fwd_noalloc", "la_denoise_step_fp8",
+    "la_fp8_q_factor_pow2",
 ]
 
 
@@ -150,6 +151,7 @@ def _load():
         "la_quantize_fp8": (ctypes.c_int, [VP, ctypes.c_int, VP, I64, F, VP]),
         "la_block_attn_fwd_fp8": (ctypes.c_int, [R, VP, VP, VP, VP, VP, I32, VP, VP, F, F, F, F,
                                                  VP]),
+        "la_fp8_q_factor_pow2": (ctypes.c_int, [F, F, F, P(F)]),
         "la_denoise_chain": (ctypes.c_int, [P(la_stage), I32, I32, I64, VP, VP, VP, VP, I32, I32,
                                             I32, I64, D, F, VP, SZ, VP, I64, VP]),
     }
@@ -391,6 +393,13 @@ def la_block_attn_fwd_fp8(ring: "la_kvring", q8, sink_k8, sink_v8, k8_cur, v8_cu
         _ptr(sink_v8, "sink_v8", snk, u8), _ptr(k8_cur, "k8_cur", blk, u8),
         _ptr(v8_cur, "v8_cur", blk, u8), ring.block_tokens, _ptr(out, "out", blk, torch.bfloat16),
         lse_p, scale, dq, dk, dv, _stream()), "la_block_attn_fwd_fp8")
+
+
+def la_fp8_q_factor_pow2(scale: float, dk: float, dq_min: float) -> float:
+    """The least float32 dq >= dq_min whose e4m3 logit factor is a power of two (host only)."""
+    dq = ctypes.c_float()
+    _check(_load().la_fp8_q_factor_pow2(scale, dk, dq_min, ctypes.byref(dq)), "la_fp8_q_factor_pow2")
+    return dq.value
 
 
 def la_kvcache_append_evict(ring: "la_kvring", k_rot, v, block_id: int, noise_level: float) -> int:

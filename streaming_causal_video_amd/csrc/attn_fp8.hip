@@ -43,7 +43,12 @@
 //    of one key hand every lane the 8 keys of its dim.
 //  * Softmax in float32 with scale * dq * dk * log2(e) folded into the exponent;
 //    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
-//    of the subnormal range).
+//    of the subnormal range).  When that factor is a power of two (the caller
+//    picks dq for it), the score MFMA applies it as its E8M0 operand scale and
+//    takes 6 - m as its accumulator input, so each score leaves the MFMA as its
+//    exponent and costs one v_exp_f32 instead of a multiply-add and the exp
+//    (1.7 % faster at the C2 shape; the input is formed per tile, because
+//    keeping it live spilled a Q fragment).
 //  * The row sum is one more MFMA per tile, of an all-ones A operand with the
 //    same e4m3 P: it moves 32 additions per lane off the VALU, which bounds
 //    this kernel, and numerator and denominator use the same rounded P.
@@ -105,12 +110,22 @@ __device__ __forceinline__ int vswz(int k) { return ((k >> 1) & 3) << 1; }
 __device__ __forceinline__ f32x16_t mma(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// The same product with A scaled by 2^(sc - 127) (the MFMA's E8M0 operand scale; B by
+// 2^0): c + 2^(sc - 127) A B, measured exact on gfx950 for powers of two.
+__device__ __forceinline__ f32x16_t mma_scaled(const i32x8_t& a, const i32x8_t& b,
+                                               const f32x16_t& c, int sc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sc, 0, 127);
+}
 
+// kFold: the logit factor c2 is 2^(sc - 127), applied by the score MFMA's operand scale,
+// and the MFMA's accumulator input carries the reference (6 - m): the scores come out
+// in the exponent's units and P = exp2(S) needs no multiply-add per score.
+template <bool kFold>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(3, 3))) void
 attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
                 float* __restrict__ lse, const AttnSegs segs, int nq, int heads,
-                float c2, float dv, float ln_scale, int qtiles, int nwg) {
+                float c2, int sc, float dv, float ln_scale, int qtiles, int nwg) {
   // The K and V buffers of the two stages are separate objects, so that the compiler
   // can tell a DMA into one stage from the fragment reads of the other.
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[KBUF], lds_v0[VBUF], lds_k1[KBUF],
@@ -161,8 +176,12 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
   f32x16_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
-  float m_run = -1e30f;  // reference max (exp2 units; finite: no inf - inf)
-  float l_run = 0.f;      // running sum of the lifted, rounded P of this lane's query
+  // Reference max (exp2 units).  Without kFold it starts at -1e30 (finite: no
+  // inf - inf), so that the first tile's probabilities overflow and set it.  With kFold
+  // the scores carry 6 - m_run from the MFMA's accumulator input, which must not
+  // swamp them: m_run starts at 6 (the input is 0) and the first tile always sets it.
+  float m_run = kFold ? kPLift : -1e30f;
+  float l_run = 0.f;  // running sum of the lifted, rounded P of this lane's query
   const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
@@ -275,25 +294,42 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint8_t* vb = vbuf(cur);
 
     // S^T for the two 32-row key blocks: A = LDS row 32 b + l32, bytes 64 ks + 32 hh ..
-    f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
+    auto kfrag = [&](int b, int ks) __attribute__((always_inline)) -> i32x8_t {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(kb + b * 32 * D + kro[ks][0]);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(kb + b * 32 * D + kro[ks][1]);
+      return i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    // the last tile of a segment: x[b][r] holds key 32 hh + 16 b + r of the tile
+    auto mask = [&](f32x16_t (&x)[2]) __attribute__((always_inline)) {
+      if (__builtin_expect(nvalid < BN, 0)) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(kb + b * 32 * D + kro[ks][0]);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(kb + b * 32 * D + kro[ks][1]);
-        const i32x8_t a = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                           (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        st[b] = mma(a, qf[ks], st[b]);
+          for (int r = 0; r < 16; ++r)
+            if (32 * hh + 16 * b + r >= nvalid) x[b][r] = -INFINITY;
       }
-    if (__builtin_expect(nvalid < BN, 0)) {
-      // the last tile of a segment: st[b][r] holds key 32 hh + 16 b + r of the tile
+    };
+    f32x16_t st[2];
+    if constexpr (kFold) {
+      // S^T c2 + 6 - m: the exponents of the lifted probabilities (the accumulator
+      // input formed here each tile: 16 registers fewer live across the loop)
+      f32x16_t cref;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int i = 0; i < 16; ++i) cref[i] = kPLift - m_run;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * hh + 16 * b + r >= nvalid) st[b][r] = -INFINITY;
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) st[b] = mma_scaled(kfrag(b, ks), qf[ks], ks ? st[b] : cref, sc);
+    } else {
+      st[0] = f32x16_t{};
+      st[1] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) st[b] = mma(kfrag(b, ks), qf[ks], st[b]);
     }
+    mask(st);
 
     // P^T fragment against the current reference max: byte 16 b + r = key
     // 32 hh + 16 b + r; tsum = the tile's row sum of the rounded, lifted P.
@@ -308,7 +344,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
           float p[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            p[t] = __builtin_amdgcn_exp2f(fmaf(st[b][4 * g + t], c2, nm));
+            p[t] = __builtin_amdgcn_exp2f(kFold ? st[b][4 * g + t] : fmaf(st[b][4 * g + t], c2, nm));
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
           pf[4 * b + g] = w;
@@ -320,11 +356,29 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     // sum carries: only then is the reference max raised to this tile's max
     // (always on the first tile, whose reference starts at -1e30), O and the
     // row sum rescaled and the tile's probabilities redone.
-    if (__builtin_amdgcn_ballot_w64((__float_as_uint(tsum[0]) & 0x7fffffffu) > 0x7f800000u) != 0) {
+    const bool first = kFold && j == 0;
+    if (__builtin_amdgcn_ballot_w64(first ||
+                                    (__float_as_uint(tsum[0]) & 0x7fffffffu) > 0x7f800000u) != 0) {
       float mx = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(st[0][r], st[1][r]));
-      mx = swap_halves_max(mx) * c2;
+      mx = swap_halves_max(mx);
+      if constexpr (kFold) {
+        // mx - 6 is the tile's excess over the reference: raise the reference by it
+        // (on the first tile set it to the tile's max, whatever the sign)
+        const float delta = first ? mx - kPLift : fmaxf(mx - kPLift, 0.f);
+        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-delta);
+        m_run += delta;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= alpha;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[b][i] -= delta;
+        probs();
+      } else {
+      mx *= c2;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -332,6 +386,7 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
       probs();
+      }
     }
     l_run += tsum[0];
 
@@ -378,10 +433,16 @@ hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs&
                            hipStream_t s, const KernelTiming* tm) {
   (void)nk;
   const int qtiles = (nq + BM - 1) / BM;
-  const float c2 = scale * dq * dk * 1.4426950408889634f;
-  launch_kernel(tm, attn_fp8_kernel, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
-                static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
-                heads, c2, dv, 0.69314718055994531f, qtiles, qtiles * heads);
+  const float c2 = fp8_logit_factor(scale, dq, dk);
+  const int sc = fp8_pow2_scale_code(c2);
+  if (sc >= 0)
+    launch_kernel(tm, attn_fp8_kernel<true>, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
+                  static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
+                  heads, c2, sc, dv, 0.69314718055994531f, qtiles, qtiles * heads);
+  else
+    launch_kernel(tm, attn_fp8_kernel<false>, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
+                  static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,
+                  heads, c2, 0, dv, 0.69314718055994531f, qtiles, qtiles * heads);
   return hipGetLastError();
 }
 

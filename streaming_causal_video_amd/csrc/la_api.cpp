@@ -87,7 +87,7 @@ size_t attn_ws_bytes(int n_q, int heads, int slots) {
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v8"; }
+const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v9"; }
 
 const char* la_status_string(int st) {
   switch (st) {
@@ -522,6 +522,40 @@ la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* 
   const int end = joined_segments(r, count, sink_k8, sink_v8, k8_cur, v8_cur, segs);
   return hip_status(la::launch_attn_fp8(q8, out, lse_or_null, segs, n_q, end, r->heads, scale,
                                         dq, dk, dv, static_cast<hipStream_t>(stream), t_timing));
+}
+
+la_status la_fp8_q_factor_pow2(float scale, float dk, float dq_min, float* dq_out) {
+  if (!dq_out) return LA_ERR_INVALID_ARG;
+  const float f[3] = {scale, dk, dq_min};
+  for (float x : f)
+    if (!(x > 0.f) || !isfinite(x)) return LA_ERR_INVALID_ARG;
+  // The factor is a product of positive floats rounded to nearest, so it does not
+  // decrease as dq grows: find the least dq >= dq_min whose factor reaches the next
+  // power of two; if the factor steps over that power, aim at the next one.
+  auto bits = [](float x) { uint32_t u; memcpy(&u, &x, 4); return u; };
+  auto from_bits = [](uint32_t u) { float x; memcpy(&x, &u, 4); return x; };
+  uint32_t lo = bits(dq_min);
+  for (int attempt = 0; attempt < 64; ++attempt) {
+    const float c = la::fp8_logit_factor(scale, from_bits(lo), dk);
+    if (!(c > 0.f) || !isfinite(c)) return LA_ERR_INVALID_ARG;
+    if (la::fp8_pow2_scale_code(c) >= 0) {
+      *dq_out = from_bits(lo);
+      return LA_OK;
+    }
+    int e = 0;
+    frexpf(c, &e);
+    const float target = ldexpf(1.f, e);  // the least power of two above c
+    uint32_t hi = bits(INFINITY);         // the factor at +inf is >= target
+    if (!(la::fp8_logit_factor(scale, from_bits(hi - 1), dk) >= target)) return LA_ERR_INVALID_ARG;
+    hi -= 1;
+    while (lo + 1 < hi) {  // invariant: factor(lo) < target <= factor(hi)
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (la::fp8_logit_factor(scale, from_bits(mid), dk) >= target) hi = mid;
+      else lo = mid;
+    }
+    lo = hi;
+  }
+  return LA_ERR_INVALID_ARG;
 }
 
 la_status la_kvcache_append_evict(la_kvring* r, const void* k_rot, const void* v,

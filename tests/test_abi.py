@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import streaming_causal_video_amd as L
@@ -537,3 +538,43 @@ def test_fp8_step_refusals_change_nothing():
     # and the bf16 step refuses e4m3 rings
     assert lib.la_denoise_step(r8, n, 1, *arrs, p, p, p, None, None, p, Hl, Wl, 3, -1, 1e4, 0.1,
                                None, 0, None, None, 0, -0.25, 0, None, None) == _lib.LA_ERR_DTYPE
+
+
+def _logit_factor32(scale, dq, dk):
+    """scale dq dk log2(e) evaluated in float32, left to right (as the library does)."""
+    f = np.float32
+    return ((f(scale) * f(dq)) * f(dk)) * f(1.4426950408889634)
+
+
+@pytest.mark.parametrize("scale,dk,dq_min", [(128 ** -0.5, 5 / 448, 5 / 448),
+                                              (64 ** -0.5, 3 / 448, 7 / 448),
+                                              (0.1, 1.0, 1e-3), (1.0, 0.5, 2.0 / 1.4426950408889634)])
+def test_fp8_q_factor_pow2_is_the_least_such_float(scale, dk, dq_min):
+    """The helper's dq makes the float32 logit factor an exact power of two, and no float in
+    [dq_min, dq) does (every one of them checked)."""
+    dq = L.la_fp8_q_factor_pow2(scale, dk, dq_min)
+    f32 = np.float32
+    assert f32(dq) >= f32(dq_min)
+    c = _logit_factor32(scale, dq, dk)
+    m, e = np.frexp(c)
+    assert m == 0.5 and -127 <= e - 1 <= 127, (c, m, e)
+    lo = np.array([f32(dq_min)]).view(np.uint32)[0]
+    hi = np.array([f32(dq)]).view(np.uint32)[0]
+    assert hi - lo < (1 << 24)  # at most one binade apart
+    cand = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
+    cs = _logit_factor32(scale, cand, dk)
+    mm, _ = np.frexp(cs)
+    assert not (mm == 0.5).any()
+
+
+def test_fp8_q_factor_pow2_refusals():
+    lib = L.lib()
+    out = ctypes.c_float(-1.0)
+    for args in [(0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, float("nan")),
+                 (1.0, 1.0, float("inf")), (3e38, 3e38, 1.0)]:
+        assert lib.la_fp8_q_factor_pow2(*args, ctypes.byref(out)) == _lib.LA_ERR_INVALID_ARG, args
+        assert out.value == -1.0
+    assert lib.la_fp8_q_factor_pow2(1.0, 1.0, 1.0, None) == _lib.LA_ERR_INVALID_ARG
+    # already a power of two: dq_min itself
+    dq = L.la_fp8_q_factor_pow2(1.0, 1.0, 1.0 / 1.4426950408889634 * 2.0)
+    assert _logit_factor32(1.0, dq, 1.0) in (np.float32(2.0), np.float32(4.0))

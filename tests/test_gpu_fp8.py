@@ -124,12 +124,15 @@ def test_e4m3_append_at_an_odd_token_count_is_bit_exact(L):
 class Fp8Stream:
     """One layer streamed through an e4m3 ring: per block, Q/K/V (bf16 stand-ins for the
     rotated projections) are quantised on the GPU with fixed per-tensor scales, the block
-    attends to [sink ; window ; itself], then its K/V codes are appended."""
+    attends to [sink ; window ; itself], then its K/V codes are appended.  q_pow2: Q's
+    factor is the least one >= scale that makes the logit factor a power of two (the
+    kernel's folded path), else Q shares K's and V's."""
 
-    def __init__(self, L, shape, layer=0, scale=SCALE_QKV, qk_mult=1.0):
+    def __init__(self, L, shape, layer=0, scale=SCALE_QKV, qk_mult=1.0, q_pow2=False):
         t = torch()
         self.L, self.s, self.layer = L, shape, layer
         self.scale, self.qk_mult = scale, qk_mult
+        self.dq = L.la_fp8_q_factor_pow2(shape.head_dim ** -0.5, scale, scale) if q_pow2 else scale
         s = shape
         self.ring = L.KVRing(s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, t.uint8, 0.75)
         sk, sv = s.initial_sink(layer)
@@ -149,12 +152,13 @@ class Fp8Stream:
         L, s, sc = self.L, self.s, self.scale
         q, k, v = s.block_inputs(self.layer, b)
         q, k = self._mult(q), self._mult(k)
-        q8, k8, v8 = (gpu_quant(L, to_dev(x), sc) for x in (q, k, v))
-        self.codes[b] = tuple(quantize(x.values.astype(np.float32), sc) for x in (q, k, v))
+        fs = (self.dq, sc, sc)
+        q8, k8, v8 = (gpu_quant(L, to_dev(x), f) for x, f in zip((q, k, v), fs))
+        self.codes[b] = tuple(quantize(x.values.astype(np.float32), f) for x, f in zip((q, k, v), fs))
         for dev, ref in zip((q8, k8, v8), self.codes[b]):
             assert np.array_equal(dev.cpu().numpy(), ref), f"block {b}: codes differ"
         L.la_block_attn_fwd_fp8(self.ring.state, q8, self.sink_k8, self.sink_v8, k8, v8, self.out,
-                                sc, sc, sc, lse=self.lse, scale=s.head_dim ** -0.5)
+                                self.dq, sc, sc, lse=self.lse, scale=s.head_dim ** -0.5)
         L.la_kvcache_append_evict(self.ring.state, k8, v8, b, 0.75)
 
     def reference(self, b, rows=None, heads=None):
@@ -166,12 +170,12 @@ class Fp8Stream:
         hs = slice(None) if heads is None else heads
         K8, V8 = np.concatenate(ks)[:, hs], np.concatenate(vs)[:, hs]
         Q8 = q8[:, hs] if rows is None else q8[rows][:, hs]
-        sc = self.scale
-        out, lse = attention_fp8(Q8, K8, V8, sc, sc, sc, s.head_dim ** -0.5)
+        sc, dq = self.scale, self.dq
+        out, lse = attention_fp8(Q8, K8, V8, dq, sc, sc, s.head_dim ** -0.5)
         # the same attention of |V|: bounds the effect of the probability rounding
         absv = np.abs(dequantize(V8, sc))
         from oracle import attention_lse
-        Qd, Kd = dequantize(Q8, sc), dequantize(K8, sc)
+        Qd, Kd = dequantize(Q8, dq), dequantize(K8, sc)
         bound_a, _ = attention_lse(Qd, Kd, absv, s.head_dim ** -0.5)
         self.lse_bar = lse_bar(Qd, Kd, s.head_dim ** -0.5)
         return out, lse, bound_a, absv.max()
@@ -209,10 +213,11 @@ def check_fp8(got, ref, bound_a, vmax, what):
     return r
 
 
+@pytest.mark.parametrize("q_pow2", [False, True], ids=["dq=dk", "dq-pow2"])
 @pytest.mark.parametrize("shape", [si.SMALL_BF16, si.MID_BF16], ids=lambda s: f"cfg{s.cfg_id}")
-def test_fp8_attention_stream_small(L, shape):
+def test_fp8_attention_stream_small(L, shape, q_pow2):
     t = torch()
-    fs = Fp8Stream(L, shape)
+    fs = Fp8Stream(L, shape, q_pow2=q_pow2)
     for b in range(1, shape.W + 3):
         fs.step(b)
         t.cuda.synchronize()
@@ -224,11 +229,12 @@ def test_fp8_attention_stream_small(L, shape):
 
 
 @pytest.mark.timeout(600)
-def test_fp8_attention_c2_sampled(L):
+@pytest.mark.parametrize("q_pow2", [False, True], ids=["dq=dk", "dq-pow2"])
+def test_fp8_attention_c2_sampled(L, q_pow2):
     """Full C2 shape (40 heads, Nk 24960 in steady state), sampled rows and heads."""
     t = torch()
     shape = si.C2
-    fs = Fp8Stream(L, shape)
+    fs = Fp8Stream(L, shape, q_pow2=q_pow2)
     rng = np.random.default_rng(17)
     rows = np.unique(np.concatenate([[0, shape.block_tokens - 1],
                                      rng.integers(0, shape.block_tokens, 48)]))
@@ -245,9 +251,10 @@ def test_fp8_attention_c2_sampled(L):
     say(f"fp8 C2 block {b}: rel-L2 {r:.4f}")
 
 
-def test_fp8_window_of_one_block(L):
+@pytest.mark.parametrize("q_pow2", [False, True], ids=["dq=dk", "dq-pow2"])
+def test_fp8_window_of_one_block(L, q_pow2):
     shape = si.LayerShape(107, "bf16", heads=2, head_dim=128, Hl=6, Wl=11, W=1)
-    fs = Fp8Stream(L, shape)
+    fs = Fp8Stream(L, shape, q_pow2=q_pow2)
     for b in range(1, 5):
         fs.step(b)
         torch().cuda.synchronize()
@@ -257,12 +264,13 @@ def test_fp8_window_of_one_block(L):
         say(f"fp8 W=1 block {b}: rel-L2 {r:.4f}")
 
 
-def test_fp8_peaked_logits(L):
+@pytest.mark.parametrize("q_pow2", [False, True], ids=["dq=dk", "dq-pow2"])
+def test_fp8_peaked_logits(L, q_pow2):
     """Q and K times 4 (logit std ~16 after quantisation, scale 20/448 so nothing
     saturates): the row max moves between tiles and segments, so the kernel raises its
     reference max during the stream."""
     shape = si.LayerShape(108, "bf16", heads=3, head_dim=128, Hl=10, Wl=13, W=2)
-    fs = Fp8Stream(L, shape, scale=20.0 / 448.0, qk_mult=4.0)
+    fs = Fp8Stream(L, shape, scale=20.0 / 448.0, qk_mult=4.0, q_pow2=q_pow2)
     for b in range(1, shape.W + 3):
         fs.step(b)
         torch().cuda.synchronize()
@@ -330,7 +338,8 @@ def oracle_fp8_step_block(shape, layer, b, dq, dk, dv):
     return out, lse, bound_a, absv.max(), (k8, v8)
 
 
-def test_fp8_denoise_step_matches_oracle(L):
+@pytest.mark.parametrize("q_pow2", [False, True], ids=["dq=dk", "dq-pow2"])
+def test_fp8_denoise_step_matches_oracle(L, q_pow2):
     """la_denoise_step_fp8 over 2 layers and W + 2 blocks (sink replacement after block 1,
     evictions, an Euler step per block): each layer's output against the oracle's e4m3
     attention of the rotated, bf16-rounded and quantised operands (the fp8 bars above),
@@ -342,6 +351,8 @@ def test_fp8_denoise_step_matches_oracle(L):
     s = si.SMALL_BF16
     n_layers = 2
     dq = dk = dv = SCALE_QKV
+    if q_pow2:
+        dq = L.la_fp8_q_factor_pow2(s.head_dim ** -0.5, dk, dk)
     stacks = {}
     for mode in ("staged", "plain"):
         st = L.KVRingStack(n_layers, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim,
@@ -404,10 +415,12 @@ def test_fp8_denoise_step_matches_oracle(L):
 def test_fp8_denoise_step_c2_sampled(L):
     """The e4m3 step at the C2 shape (one layer, staged ring, blocks 1..W+1: the ring
     full at the last one, Nk 24960): sampled rows of three heads against the oracle's
-    e4m3 attention, and the last block's window V codes bit for bit."""
+    e4m3 attention, and the last block's window V codes bit for bit.  Q's factor is the
+    power-of-two one of the e4m3 step benchmark (the kernel's folded path)."""
     t = torch()
     s = si.C2
-    dq = dk = dv = SCALE_QKV
+    dk = dv = SCALE_QKV
+    dq = L.la_fp8_q_factor_pow2(s.head_dim ** -0.5, dk, dk)
     st = L.KVRingStack(1, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, t.uint8, 0.75,
                        staged=True)
     sk, sv = s.initial_sink(0)
