@@ -70,8 +70,8 @@ FP8_SCALE = 5.0 / 448.0  # per-tensor e4m3 scale of K and V: |x| = 5 maps to 448
 
 def fp8_factors(d):
     """(dq, dk, dv) of the e4m3 workloads: K and V at 5/448; Q at the least factor >= 5/448
-    for which the logit factor scale dq dk log2(e) is a power of two (the attention's
-    faster path; |q| up to at least 5 still maps into the e4m3 range)."""
+    for which the logit factor scale dq dk log2(e) is a power of two to within 2^-24 (the
+    attention's faster path; |q| up to at least 5 still maps into the e4m3 range)."""
     import streaming_causal_video_amd as L
     dq = L.la_fp8_q_factor_pow2(d ** -0.5, FP8_SCALE, FP8_SCALE)
     return dq, FP8_SCALE, FP8_SCALE

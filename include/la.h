@@ -501,11 +501,12 @@ la_status la_quantize_fp8(const void* in, la_dtype in_dtype, void* out, int64_t 
  * <= 2^-4 per probability); the row sum that normalises the output is taken
  * from the same rounded probabilities.
  * Pointers 16-byte aligned (lse 4-byte); factors and scale > 0 and finite.
- * When the logit factor scale * dq * dk * log2(e), evaluated in float32 in that
- * order, is a power of two 2^e (-127 <= e <= 127), the kernel applies it through
- * the score MFMA's operand scale and forms each score's exponent inside the MFMA
- * (no multiply-add per score; la_fp8_q_factor_pow2 picks such a dq); the result
- * is the same function, rounded in another order.
+ * When the logit factor scale * dq * dk * log2(e) (float64 from the float32
+ * arguments) lies within a relative 2^-24 of a power of two 2^e (-127 <= e <= 127),
+ * the kernel applies 2^e through the score MFMA's operand scale and forms each
+ * score's exponent inside the MFMA (no multiply-add per score; la_fp8_q_factor_pow2
+ * picks such a dq).  The factor then differs from the exact one by no more than
+ * the float32 product of the other path does (up to 3 * 2^-24).
  */
 la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* sink_k8,
                                 const void* sink_v8, const void* k8_cur, const void* v8_cur,
@@ -514,8 +515,9 @@ la_status la_block_attn_fwd_fp8(const la_kvring* r, const void* q8, const void* 
 
 /*
  * la_fp8_q_factor_pow2 - the least float dq >= dq_min for which the e4m3
- * attention's logit factor scale * dq * dk * log2(e) (float32, in that order) is a
- * power of two 2^e with -127 <= e <= 127, in *dq_out: quantising Q with that dq
+ * attention's logit factor scale * dq * dk * log2(e) (float64 from the float32
+ * arguments) lies within a relative 2^-24 of a power of two 2^e with
+ * -127 <= e <= 127, in *dq_out: quantising Q with that dq
  * (la_quantize_fp8 with inv_scale 1 / dq) lets la_block_attn_fwd_fp8 and
  * la_denoise_step_fp8 take their faster path.  The FP8 scaling recipe is the
  * caller's choice (NOTES, Table 3 names FP8 without one): a dq at most about twice

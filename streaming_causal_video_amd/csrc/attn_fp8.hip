@@ -43,8 +43,9 @@
 //    of one key hand every lane the 8 keys of its dim.
 //  * Softmax in float32 with scale * dq * dk * log2(e) folded into the exponent;
 //    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
-//    of the subnormal range).  When that factor is a power of two (the caller
-//    picks dq for it), the score MFMA applies it as its E8M0 operand scale and
+//    of the subnormal range).  When that factor is a power of two to within a
+//    relative 2^-24 (the caller picks dq for it), the score MFMA applies that
+//    power as its E8M0 operand scale and
 //    takes 6 - m as its accumulator input, so each score leaves the MFMA as its
 //    exponent and costs one v_exp_f32 instead of a multiply-add and the exp
 //    (1.7 % faster at the C2 shape; the input is formed per tile, because
@@ -117,7 +118,7 @@ __device__ __forceinline__ f32x16_t mma_scaled(const i32x8_t& a, const i32x8_t& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sc, 0, 127);
 }
 
-// kFold: the logit factor c2 is 2^(sc - 127), applied by the score MFMA's operand scale,
+// kFold: the logit factor is 2^(sc - 127) (to 2^-24), applied by the score MFMA's operand scale,
 // and the MFMA's accumulator input carries the reference (6 - m): the scores come out
 // in the exponent's units and P = exp2(S) needs no multiply-add per score.
 template <bool kFold>
@@ -434,7 +435,7 @@ hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs&
   (void)nk;
   const int qtiles = (nq + BM - 1) / BM;
   const float c2 = fp8_logit_factor(scale, dq, dk);
-  const int sc = fp8_pow2_scale_code(c2);
+  const int sc = fp8_pow2_scale_code(fp8_logit_factor64(scale, dq, dk));
   if (sc >= 0)
     launch_kernel(tm, attn_fp8_kernel<true>, dim3(qtiles * heads), dim3(NTHREADS), 0, s,
                   static_cast<const uint8_t*>(q), static_cast<uint16_t*>(out), lse, segs, nq,

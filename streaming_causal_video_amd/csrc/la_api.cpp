@@ -529,31 +529,28 @@ la_status la_fp8_q_factor_pow2(float scale, float dk, float dq_min, float* dq_ou
   const float f[3] = {scale, dk, dq_min};
   for (float x : f)
     if (!(x > 0.f) || !isfinite(x)) return LA_ERR_INVALID_ARG;
-  // The factor is a product of positive floats rounded to nearest, so it does not
-  // decrease as dq grows: find the least dq >= dq_min whose factor reaches the next
-  // power of two; if the factor steps over that power, aim at the next one.
-  auto bits = [](float x) { uint32_t u; memcpy(&u, &x, 4); return u; };
-  auto from_bits = [](uint32_t u) { float x; memcpy(&x, &u, 4); return x; };
-  uint32_t lo = bits(dq_min);
-  for (int attempt = 0; attempt < 64; ++attempt) {
-    const float c = la::fp8_logit_factor(scale, from_bits(lo), dk);
-    if (!(c > 0.f) || !isfinite(c)) return LA_ERR_INVALID_ARG;
-    if (la::fp8_pow2_scale_code(c) >= 0) {
-      *dq_out = from_bits(lo);
-      return LA_OK;
+  // The factor is dq times K = scale dk log2(e); for the least power of two 2^e at or
+  // above the factor of dq_min, dq = 2^e / K rounded to float32 has a factor within a
+  // relative 2^-24 of 2^e, and so may the float below it (the window holds up to two
+  // floats): the least of the two, or the next float up when the rounding fell below
+  // dq_min, else the next power of two.
+  if (la::fp8_pow2_scale_code(la::fp8_logit_factor64(scale, dq_min, dk)) >= 0) {
+    *dq_out = dq_min;
+    return LA_OK;
+  }
+  const double K = la::fp8_logit_factor64(scale, 1.f, dk);
+  int k = 0;
+  const double m = frexp(la::fp8_logit_factor64(scale, dq_min, dk), &k);
+  int e = m == 0.5 ? k - 1 : k;
+  for (int attempt = 0; attempt < 4; ++attempt, ++e) {
+    const float dq = (float)ldexp(1.0 / K, e);
+    for (float c : {nextafterf(dq, 0.f), dq, nextafterf(dq, INFINITY)}) {  // least first
+      if (!(c >= dq_min) || !isfinite(c)) continue;
+      if (la::fp8_pow2_scale_code(la::fp8_logit_factor64(scale, c, dk)) >= 0) {
+        *dq_out = c;
+        return LA_OK;
+      }
     }
-    int e = 0;
-    frexpf(c, &e);
-    const float target = ldexpf(1.f, e);  // the least power of two above c
-    uint32_t hi = bits(INFINITY);         // the factor at +inf is >= target
-    if (!(la::fp8_logit_factor(scale, from_bits(hi - 1), dk) >= target)) return LA_ERR_INVALID_ARG;
-    hi -= 1;
-    while (lo + 1 < hi) {  // invariant: factor(lo) < target <= factor(hi)
-      const uint32_t mid = lo + (hi - lo) / 2;
-      if (la::fp8_logit_factor(scale, from_bits(mid), dk) >= target) hi = mid;
-      else lo = mid;
-    }
-    lo = hi;
   }
   return LA_ERR_INVALID_ARG;
 }

@@ -110,24 +110,30 @@ hipError_t launch_attn_bf16(const void* q, void* out, float* lse, const AttnSegs
                             int nk, int heads, float qmul, const AttnWorkspace& ws,
                             hipStream_t s, const KernelTiming* tm = nullptr,
                             const float* qcs = nullptr);
-// The e4m3 attention's logit factor in the exponent's units, scale dq dk log2(e),
-// evaluated in float32 in that order (the launcher and la_fp8_q_factor_pow2 share it).
+// The e4m3 attention's logit factor in the exponent's units, scale dq dk log2(e): in
+// float32 (the multiply-add path) and in float64 (the power-of-two test below).
 inline float fp8_logit_factor(float scale, float dq, float dk) {
   return scale * dq * dk * 1.4426950408889634f;
 }
-// The E8M0 code (127 + e, 0..254) of c when c == 2^e exactly with -127 <= e <= 127,
-// else -1.
-inline int fp8_pow2_scale_code(float c) {
-  if (!(c > 0.f) || !__builtin_isfinite(c)) return -1;
-  int e = 0;
-  const float fr = __builtin_frexpf(c, &e);  // c = fr 2^e, 0.5 <= fr < 1
-  if (fr != 0.5f) return -1;
-  const int k = e - 1;
-  return (k >= -127 && k <= 127) ? 127 + k : -1;
+inline double fp8_logit_factor64(float scale, float dq, float dk) {
+  return (double)scale * (double)dq * (double)dk * 1.4426950408889634;
 }
-// When the logit factor is a power of two (fp8_pow2_scale_code >= 0) the kernel applies
-// it with the score MFMA's operand scale and takes the reference through the MFMA's
-// accumulator input, else with one multiply-add per score.
+// The E8M0 code 127 + e (0..254) of the power of two 2^e, -127 <= e <= 127, that lies
+// within a relative 2^-24 of the factor f (the float32 product above may be off by three
+// times that), else -1.
+inline int fp8_pow2_scale_code(double f) {
+  if (!(f > 0.0) || !__builtin_isfinite(f)) return -1;
+  int k = 0;
+  const double m = __builtin_frexp(f, &k);  // f = m 2^k, 0.5 <= m < 1
+  int e;
+  if (m - 0.5 <= 0x1p-25) e = k - 1;
+  else if (1.0 - m <= 0x1p-24) e = k;
+  else return -1;
+  return (e >= -127 && e <= 127) ? 127 + e : -1;
+}
+// When the logit factor is a power of two in that sense (fp8_pow2_scale_code >= 0) the
+// kernel applies it with the score MFMA's operand scale and takes the reference through
+// the MFMA's accumulator input, else with one multiply-add per score.
 hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs& segs, int nq,
                            int nk, int heads, float scale, float dq, float dk, float dv,
                            hipStream_t s, const KernelTiming* tm = nullptr);

@@ -540,31 +540,38 @@ def test_fp8_step_refusals_change_nothing():
                                None, 0, None, None, 0, -0.25, 0, None, None) == _lib.LA_ERR_DTYPE
 
 
-def _logit_factor32(scale, dq, dk):
-    """scale dq dk log2(e) evaluated in float32, left to right (as the library does)."""
-    f = np.float32
-    return ((f(scale) * f(dq)) * f(dk)) * f(1.4426950408889634)
+def _factor64(scale, dq, dk):
+    """scale dq dk log2(e) in float64 from the float32 arguments, left to right."""
+    f, d = np.float32, np.float64
+    return d(f(scale)) * d(f(dq)) * d(f(dk)) * 1.4426950408889634
+
+
+def _near_pow2(F):
+    """Within a relative 2^-24 of a power of two 2^e, -127 <= e <= 127 (elementwise)."""
+    m, k = np.frexp(F)
+    lo = (m - 0.5 <= 2.0 ** -25) & (k - 1 >= -127) & (k - 1 <= 127)
+    hi = (1.0 - m <= 2.0 ** -24) & (k >= -127) & (k <= 127)
+    return lo | hi
 
 
 @pytest.mark.parametrize("scale,dk,dq_min", [(128 ** -0.5, 5 / 448, 5 / 448),
                                               (64 ** -0.5, 3 / 448, 7 / 448),
-                                              (0.1, 1.0, 1e-3), (1.0, 0.5, 2.0 / 1.4426950408889634)])
+                                              (0.1, 1.0, 1e-3), (500822.7, 2 / 448, 2 / 448),
+                                              (1.0, 0.5, 2.0 / 1.4426950408889634)])
 def test_fp8_q_factor_pow2_is_the_least_such_float(scale, dk, dq_min):
-    """The helper's dq makes the float32 logit factor an exact power of two, and no float in
-    [dq_min, dq) does (every one of them checked)."""
+    """The helper's dq puts the logit factor within a relative 2^-24 of a power of two, and
+    no float in [dq_min, dq) does (every one of them checked)."""
     dq = L.la_fp8_q_factor_pow2(scale, dk, dq_min)
     f32 = np.float32
     assert f32(dq) >= f32(dq_min)
-    c = _logit_factor32(scale, dq, dk)
-    m, e = np.frexp(c)
-    assert m == 0.5 and -127 <= e - 1 <= 127, (c, m, e)
+    F = _factor64(scale, dq, dk)
+    assert _near_pow2(np.array([F]))[0], F
+    assert abs(F / 2.0 ** np.round(np.log2(F)) - 1) <= 2.0 ** -24
     lo = np.array([f32(dq_min)]).view(np.uint32)[0]
     hi = np.array([f32(dq)]).view(np.uint32)[0]
     assert hi - lo < (1 << 24)  # at most one binade apart
     cand = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
-    cs = _logit_factor32(scale, cand, dk)
-    mm, _ = np.frexp(cs)
-    assert not (mm == 0.5).any()
+    assert not _near_pow2(_factor64(scale, cand, dk)).any()
 
 
 def test_fp8_q_factor_pow2_refusals():
@@ -575,6 +582,5 @@ def test_fp8_q_factor_pow2_refusals():
         assert lib.la_fp8_q_factor_pow2(*args, ctypes.byref(out)) == _lib.LA_ERR_INVALID_ARG, args
         assert out.value == -1.0
     assert lib.la_fp8_q_factor_pow2(1.0, 1.0, 1.0, None) == _lib.LA_ERR_INVALID_ARG
-    # already a power of two: dq_min itself
-    dq = L.la_fp8_q_factor_pow2(1.0, 1.0, 1.0 / 1.4426950408889634 * 2.0)
-    assert _logit_factor32(1.0, dq, 1.0) in (np.float32(2.0), np.float32(4.0))
+    # dq_min already gives a power of two: dq_min itself
+    assert L.la_fp8_q_factor_pow2(1.0, 1.0 / 1.4426950408889634, 4.0) == 4.0

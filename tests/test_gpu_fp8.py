@@ -281,6 +281,47 @@ def test_fp8_peaked_logits(L, q_pow2):
         say(f"fp8 peaked block {b}: rel-L2 {r:.4f}")
 
 
+@pytest.mark.parametrize("target_exp", [-60, 4])
+def test_fp8_folded_factor_far_from_one(L, target_exp):
+    """The folded path with a logit factor of 2^-60 (tiny logits: near-uniform attention)
+    and 2^4 (factors near 1, so the codes are the values themselves, and logits of about
+    160 in base 2: nearly an argmax), i.e. MFMA operand-scale codes far from 127, against
+    the oracle; the attention scale is picked so that the helper's Q factor is near K's."""
+    shape = si.LayerShape(109, "bf16", heads=2, head_dim=128, Hl=6, Wl=9, W=2)
+    sc = SCALE_QKV if target_exp < 0 else 1.0
+    # the attention scale that puts sc * sc * log2(e) * scale at about 2^target_exp
+    attn_scale = 2.0 ** target_exp / (sc * sc * 1.4426950408889634) * 0.9
+    dq = L.la_fp8_q_factor_pow2(attn_scale, sc, sc)
+    f, d = np.float32, np.float64
+    F = d(f(attn_scale)) * d(f(dq)) * d(f(sc)) * 1.4426950408889634
+    e = np.round(np.log2(F))
+    assert abs(F / 2.0 ** e - 1) <= 2.0 ** -24 and abs(e - target_exp) <= 1
+    fs = Fp8Stream(L, shape, scale=sc)
+    fs.dq = dq
+    s = shape
+    for b in range(1, s.W + 3):
+        q, k, v = s.block_inputs(fs.layer, b)
+        fsq = (dq, sc, sc)
+        q8, k8, v8 = (gpu_quant(L, to_dev(x), f) for x, f in zip((q, k, v), fsq))
+        fs.codes[b] = tuple(quantize(x.values.astype(np.float32), f) for x, f in zip((q, k, v), fsq))
+        L.la_block_attn_fwd_fp8(fs.ring.state, q8, fs.sink_k8, fs.sink_v8, k8, v8, fs.out, dq, sc,
+                                sc, lse=fs.lse, scale=attn_scale)
+        L.la_kvcache_append_evict(fs.ring.state, k8, v8, b, 0.75)
+        torch().cuda.synchronize()
+        ids = list(range(max(1, b - s.W), b))
+        K8 = np.concatenate([fs.codes["sink"][0]] + [fs.codes[i][1] for i in ids] + [fs.codes[b][1]])
+        V8 = np.concatenate([fs.codes["sink"][1]] + [fs.codes[i][2] for i in ids] + [fs.codes[b][2]])
+        out, lse = attention_fp8(fs.codes[b][0], K8, V8, dq, sc, sc, attn_scale)
+        from oracle import attention_lse
+        absv = np.abs(dequantize(V8, sc))
+        Qd, Kd = dequantize(fs.codes[b][0], dq), dequantize(K8, sc)
+        a, _ = attention_lse(Qd, Kd, absv, attn_scale)
+        r = check_fp8(to_f64(fs.out), out, a, absv.max(), f"factor 2^{target_exp} block {b}")
+        check_lse(fs.lse.cpu().numpy().astype(np.float64), lse, lse_bar(Qd, Kd, attn_scale),
+                  f"fp8 factor 2^{target_exp} block {b}")
+        say(f"fp8 factor 2^{target_exp} block {b}: rel-L2 {r:.4f}")
+
+
 @pytest.mark.timeout(900)
 def test_fp8_attention_c5_sampled(L):
     """720p-shaped layer (Nk 56320 at block 5, eviction at 6), sampled rows of two heads."""
