@@ -127,7 +127,7 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
         skn = [t[:st] for t in k] if b == 1 else None
         svn = [t[:st] for t in v] if b == 1 else None
         if fp8:
-            L.la_denoise_step_fp8(stack.states, b, q, k, v, outs, qws, kws, sws, q8, k8, v8, sk8,
+            L.la_denoise_step_fp8(stack.states, b, q, k, v, outs, None, None, None, q8, k8, v8, sk8,
                                   sv8, table, Hl, Wl, FRAMES, DELTA, THETA, scale=d ** -0.5,
                                   dq=fdq, dk=fdk, dv=fdv, sink_k_new=skn,
                                   sink_v_new=svn, x=x, vel=vels[e] if with_euler else None,
@@ -201,9 +201,10 @@ def gpu_step_bench(args, Hl, Wl, W, H, d, n_layers, with_euler=True, fp8=False):
     if staged and not fp8:
         rope_bytes += 2 * bt * H * d * 2
     if fp8:
-        # RoPE and the quantisation of Q, K, V, sink K and sink V (bf16 in, e4m3 out);
-        # a staged e4m3 ring takes K and V codes in place, so the append copies nothing
-        rope_bytes += (3 * bt + 2 * st) * H * d * 3
+        # one launch rotates Q, K and the sink K and quantises them with V and the sink V
+        # (bf16 in, e4m3 out); a staged e4m3 ring takes the K and V codes in place, so the
+        # append copies nothing
+        rope_bytes = (3 * bt + 2 * st) * H * d * 3
         app_bytes = 0 if staged else 2 * 2 * bt * H * d
     res = {
         "ms_per_step": ms_step,

@@ -428,17 +428,18 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
  * la_denoise_step_fp8 - la_denoise_step with the attention on e4m3 operands, for
  * rings of dtype LA_FP8_E4M3 (NOTES, Table 3: FP8 quantisation together with
  * FlashAttention-3 and fused kernels).  For every layer l, in order, on `stream`:
- *   1. la_rope3d_rolling as in la_denoise_step, bf16 out (no Q pre-scale), into
- *      q_rot_ws, k_rot_ws and sink_k_rot_ws;
- *   2. one launch quantises five bf16 tensors, each with its own per-tensor
- *      scale as la_quantize_fp8 does (code = E4M3(x * fl32(1 / d))): the rotated
- *      Q into q8_ws (dq), the rotated K (dk) and v_raw[l] (dv) into the ring's next
- *      slot when the ring is staged and the step appends (else into k8_ws and
- *      v8_ws), the rotated sink K into sink_k8_ws (dk) and the ring's sink V into
- *      sink_v8_ws (dv);
- *   3. la_block_attn_fwd_fp8 of these codes with (dq, dk, dv) and `scale` into
+ *   1. one launch: the rotations of la_rope3d_rolling (Q, K at the block's
+ *      positions, the ring's raw sink K at the sink's; no Q pre-scale), each
+ *      result rounded to bf16 and then quantised with its per-tensor scale as
+ *      la_quantize_fp8 does (code = E4M3(x * fl32(1 / d))), together with the
+ *      quantisation of v_raw[l] and of the ring's sink V: Q into q8_ws (dq), K (dk)
+ *      and V (dv) into the ring's next slot when the ring is staged and the step
+ *      appends (else into k8_ws and v8_ws), the sink K into sink_k8_ws (dk) and the
+ *      sink V into sink_v8_ws (dv) - the same codes as la_rope3d_rolling to bf16
+ *      followed by la_quantize_fp8, with no bf16 intermediate in memory;
+ *   2. la_block_attn_fwd_fp8 of these codes with (dq, dk, dv) and `scale` into
  *      attn_out[l] (bf16);
- *   4. la_kvcache_append_evict of the block's K and V codes as block block_id
+ *   3. la_kvcache_append_evict of the block's K and V codes as block block_id
  *      (nothing is copied when they are already in the slot), and at block 1 the
  *      sink replacement, as in la_denoise_step;
  * then la_fm_euler_step(x, vel, n_latent, dt) if x != NULL.
@@ -447,9 +448,10 @@ la_status la_denoise_step(la_kvring* rings, int32_t n_layers, int64_t block_id,
  * aligned, caller-owned: q8_ws, k8_ws, v8_ws [block_tokens][heads][head_dim]
  * bytes (k8_ws and v8_ws may be NULL when every ring is staged and flags lacks
  * LA_STEP_ATTEND_ONLY), sink_k8_ws and sink_v8_ws [sink_tokens][heads][head_dim]
- * bytes; q_rot_ws, k_rot_ws and sink_k_rot_ws bf16 as in la_denoise_step.  The
- * other arguments, flags, timing events (the quantisation is timed with RoPE)
- * and errors are those of la_denoise_step (it takes no attention workspace).
+ * bytes; q_rot_ws, k_rot_ws and sink_k_rot_ws are not used (may be NULL).  q_raw,
+ * k_raw, v_raw 16-byte aligned.  The other arguments, flags, timing events (the
+ * first pair of a layer spans the RoPE and quantisation launch) and errors are
+ * those of la_denoise_step (it takes no attention workspace).
  */
 la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_id,
                               const void* const* q_raw, const void* const* k_raw,

@@ -522,7 +522,8 @@ def la_denoise_step_fp8(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_r
                         dt: float = -0.25, timing_events=None, flags: int = 0) -> None:
     """la_denoise_step for e4m3 rings (KVRingStack(..., torch.uint8)): bf16 activations,
     uint8 code workspaces (k8_ws / v8_ws may be None when the rings are staged and the
-    step appends).  dq, dk, dv: the per-tensor dequantisation scales."""
+    step appends; q_rot_ws, k_rot_ws and sink_k_rot_ws are unused and may be None).
+    dq, dk, dv: the per-tensor dequantisation scales."""
     torch = _torch()
     n = len(rings)
     if n < 1:
@@ -538,9 +539,7 @@ def la_denoise_step_fp8(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_r
     for ts, name in ((sink_k_new, "sink_k_new"), (sink_v_new, "sink_v_new")):
         if ts is not None:
             _check_list(ts, name, snk, bf, n)
-    for t, name, shp, dt_ in ((q_rot_ws, "q_rot_ws", blk, bf), (k_rot_ws, "k_rot_ws", blk, bf),
-                              (sink_k_rot_ws, "sink_k_rot_ws", snk, bf), (q8_ws, "q8_ws", blk, u8),
-                              (sink_k8_ws, "sink_k8_ws", snk, u8),
+    for t, name, shp, dt_ in ((q8_ws, "q8_ws", blk, u8), (sink_k8_ws, "sink_k8_ws", snk, u8),
                               (sink_v8_ws, "sink_v8_ws", snk, u8)):
         _check_tensor(t, name, shp, dt_)
     for t, name in ((k8_ws, "k8_ws"), (v8_ws, "v8_ws")):
@@ -560,8 +559,7 @@ def la_denoise_step_fp8(rings, block_id: int, q_raw, k_raw, v_raw, attn_out, q_r
     _check(_load().la_denoise_step_fp8(
         rings, n, block_id, _ptr_array(q_raw, "q_raw", blk, bf, n),
         _ptr_array(k_raw, "k_raw", blk, bf, n), _ptr_array(v_raw, "v_raw", blk, bf, n),
-        _ptr_array(attn_out, "attn_out", blk, bf, n), _ptr(q_rot_ws, "q_rot_ws"),
-        _ptr(k_rot_ws, "k_rot_ws"), _ptr(sink_k_rot_ws, "sink_k_rot_ws"), _ptr(q8_ws, "q8_ws"),
+        _ptr_array(attn_out, "attn_out", blk, bf, n), None, None, None, _ptr(q8_ws, "q8_ws"),
         _ptr(k8_ws, "k8_ws"), _ptr(v8_ws, "v8_ws"), _ptr(sink_k8_ws, "sink_k8_ws"),
         _ptr(sink_v8_ws, "sink_v8_ws"), skn, svn, _ptr(rope_table, "rope_table"), Hl, Wl,
         frames_per_block, sink_delta, theta, scale, dq, dk, dv, _ptr(x, "x"), _ptr(vel, "vel"),

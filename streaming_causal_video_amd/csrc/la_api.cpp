@@ -230,6 +230,39 @@ namespace {
 //    rotates its raw Q itself);
 //  * v_in, v_out != NULL: a plain copy of the block's V (the step stages it in a ring
 //    slot).
+// The geometry and the frame-axis cos/sin (float64 on the host) of one block's RoPE
+// launch: the block's frames f0 .. f0 + n_frames - 1 in rows 0 .. n_frames - 1, the
+// sink's position f0 + sink_delta in row n_frames.
+la_status rope_setup(int32_t n_frames, int64_t f0, int64_t sink_delta, int32_t Hl, int32_t Wl,
+                     int32_t heads, int32_t head_dim, double theta, la::RopeGeom* g,
+                     la::RopeTemporal* tc) {
+  if (!(theta > 1.0)) return LA_ERR_INVALID_ARG;
+  if (n_frames < 1 || n_frames > LA_MAX_BLOCK_FRAMES || Hl < 1 || Wl < 1 || heads < 1 ||
+      head_dim < 8 || head_dim % 8 != 0 || head_dim > 256)
+    return LA_ERR_SHAPE;
+  int tband, hw;
+  bands(head_dim, &tband, &hw);
+  const int tpairs = tband / 2;
+  if (tpairs > la::kMaxTPairs || hw < 2) return LA_ERR_SHAPE;
+  const int64_t hwtok = (int64_t)Hl * Wl;
+  if (hwtok * n_frames > INT32_MAX / 2) return LA_ERR_SHAPE;
+  memset(tc, 0, sizeof(*tc));
+  for (int row = 0; row <= n_frames; ++row) {
+    const int64_t pos = row < n_frames ? f0 + row : f0 + sink_delta;
+    for (int k = 0; k < tpairs; ++k)
+      frame_cs(pos, k, tband, theta, &tc->cs[row][k][0], &tc->cs[row][k][1]);
+  }
+  g->HW = (int32_t)hwtok;
+  g->Wl = Wl;
+  g->Hl = Hl;
+  g->heads = heads;
+  g->head_dim = head_dim;
+  g->tpairs = tpairs;
+  g->hpairs = hw / 2;
+  g->wpairs = hw / 2;
+  return LA_OK;
+}
+
 la_status rope_rolling(const void* q_in, void* q_out, const void* k_in, void* k_out,
                        int32_t n_frames, int64_t f0, const void* sink_k_in, void* sink_k_out,
                        int64_t sink_delta, const void* dev_table, int32_t Hl, int32_t Wl,
@@ -241,36 +274,14 @@ la_status rope_rolling(const void* q_in, void* q_out, const void* k_in, void* k_
   if (!(q_scale > 0.f) || !isfinite(q_scale)) return LA_ERR_INVALID_ARG;
   if ((!q_in) != (!q_out) || (!k_in) != (!k_out) || (!sink_k_in) != (!sink_k_out))
     return LA_ERR_INVALID_ARG;
-  if (n_frames < 1 || n_frames > LA_MAX_BLOCK_FRAMES || Hl < 1 || Wl < 1 || heads < 1 ||
-      head_dim < 8 || head_dim % 8 != 0 || head_dim > 256)
-    return LA_ERR_SHAPE;
+  la::RopeGeom g;
+  la::RopeTemporal tc;
+  const la_status st = rope_setup(n_frames, f0, sink_delta, Hl, Wl, heads, head_dim, theta, &g, &tc);
+  if (st != LA_OK) return st;
   const void* ptrs[6] = {q_in, q_out, k_in, k_out, sink_k_in, sink_k_out};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
-  int tband, hw;
-  bands(head_dim, &tband, &hw);
-  const int tpairs = tband / 2;
-  if (tpairs > la::kMaxTPairs || hw < 2) return LA_ERR_SHAPE;
   const int64_t hwtok = (int64_t)Hl * Wl;
-  if (hwtok * n_frames > INT32_MAX / 2) return LA_ERR_SHAPE;
-
-  // Frame-axis cos/sin for the block's frames and the sink's position, float64 on the host.
-  la::RopeTemporal tc;
-  memset(&tc, 0, sizeof(tc));
-  for (int row = 0; row <= n_frames; ++row) {
-    const int64_t pos = row < n_frames ? f0 + row : f0 + sink_delta;
-    for (int k = 0; k < tpairs; ++k)
-      frame_cs(pos, k, tband, theta, &tc.cs[row][k][0], &tc.cs[row][k][1]);
-  }
-  la::RopeGeom g;
-  g.HW = (int32_t)hwtok;
-  g.Wl = Wl;
-  g.Hl = Hl;
-  g.heads = heads;
-  g.head_dim = head_dim;
-  g.tpairs = tpairs;
-  g.hpairs = hw / 2;
-  g.wpairs = hw / 2;
   if (q_cs_out && (!k_in || !aligned16(q_cs_out))) return LA_ERR_INVALID_ARG;
   if ((!v_in) != (!v_out) || (v_in && (!aligned16(v_in) || !aligned16(v_out))))
     return LA_ERR_INVALID_ARG;
@@ -797,9 +808,10 @@ la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_
                               const float* vel, int64_t n_latent, float dt, uint32_t flags,
                               void* const* timing_events, la_stream_t stream) {
   // ---- validate the whole step before enqueuing anything
-  if (!q_rot_ws || !k_rot_ws || !sink_k_rot_ws || !rope_table || !q8_ws || !sink_k8_ws ||
-      !sink_v8_ws)
-    return LA_ERR_INVALID_ARG;
+  (void)q_rot_ws;  // unused: RoPE and the quantisation run as one launch
+  (void)k_rot_ws;
+  (void)sink_k_rot_ws;
+  if (!rope_table || !q8_ws || !sink_k8_ws || !sink_v8_ws) return LA_ERR_INVALID_ARG;
   const la_status v = validate_stage(rings, n_layers, block_id, q_raw, k_raw, v_raw, attn_out,
                                      sink_k_new, sink_v_new, Hl, Wl, frames_per_block, flags,
                                      true);
@@ -815,6 +827,9 @@ la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_
   for (const void* p : ws)
     if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
   if (x && (!vel || n_latent < 0 || !isfinite(dt))) return LA_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l)
+    if (!aligned16(q_raw[l]) || !aligned16(k_raw[l]) || !aligned16(v_raw[l]))
+      return LA_ERR_INVALID_ARG;
 
   const int64_t f0 = (int64_t)frames_per_block * (block_id - 1);
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -830,34 +845,28 @@ la_status la_denoise_step_fp8(la_kvring* rings, int32_t n_layers, int64_t block_
   } while (0)
   for (int l = 0; l < n_layers; ++l) {
     la_kvring* r = &rings[l];
-    const int64_t blk = (int64_t)r->block_tokens * r->heads * r->head_dim;
-    const int64_t snk = (int64_t)r->sink_tokens * r->heads * r->head_dim;
     void* k8 = k8_ws;
     void* v8 = v8_ws;
     if (append && r->nslots == r->W + 1) LA_TRY(la_kvring_next_slot(r, &k8, &v8));
-    // RoPE and the quantisation are timed as one span: RoPE's begin, the quantisation's end
-    const la::KernelTiming t_rope = {ev(6 * l), nullptr}, t_quant = {nullptr, ev(6 * l + 1)},
+    const la::KernelTiming t_rope = {ev(6 * l), ev(6 * l + 1)},
                            t_attn = {ev(6 * l + 2), ev(6 * l + 3)},
                            t_app = {ev(6 * l + 4), ev(6 * l + 5)};
-    {
-      TimedOp op(&t_rope);
-      LA_TRY(la_rope3d_rolling(q_raw[l], q_rot_ws, k_raw[l], k_rot_ws, frames_per_block, f0,
-                               r->sink_k_raw, sink_k_rot_ws, sink_delta, rope_table, Hl, Wl,
-                               r->heads, r->head_dim, LA_BF16, theta, 1.0f, stream));
-    }
-    la::QuantJobs jobs = {};
-    const void* ins[5] = {q_rot_ws, k_rot_ws, v_raw[l], sink_k_rot_ws, r->sink_v};
-    void* outs[5] = {q8_ws, k8, v8, sink_k8_ws, sink_v8_ws};
-    const int64_t ns[5] = {blk, blk, blk, snk, snk};
-    const float invs[5] = {iq, ik, iv, ik, iv};
-    for (int j = 0; j < 5; ++j) {
-      jobs.in[j] = ins[j];
-      jobs.out[j] = outs[j];
-      jobs.n[j] = ns[j];
-      jobs.inv[j] = invs[j];
-    }
-    jobs.count = 5;
-    LA_TRY(hip_status(la::launch_quantize_fp8_many(jobs, hs, &t_quant)));
+    // One launch: Q, K and the sink K rotated (no Q pre-scale), each rounded to bf16 and
+    // quantised; the block's V and the ring's sink V quantised as they are.
+    la::RopeGeom g;
+    la::RopeTemporal tc;
+    LA_TRY(rope_setup(frames_per_block, f0, sink_delta, Hl, Wl, r->heads, r->head_dim, theta,
+                      &g, &tc));
+    const int32_t bt = r->block_tokens, stk = r->sink_tokens;
+    const la::RopeTensor t[5] = {
+        {q_raw[l], q8_ws, bt, 0, 1.0f, nullptr, 1.0f, 0, 1, iq},
+        {k_raw[l], k8, bt, 0, 1.0f, nullptr, 1.0f, 0, 1, ik},
+        {r->sink_k_raw, sink_k8_ws, stk, frames_per_block, 1.0f, nullptr, 1.0f, 0, 1, ik},
+        {v_raw[l], v8, bt, 0, 1.0f, nullptr, 1.0f, 1, 1, iv},
+        {r->sink_v, sink_v8_ws, stk, 0, 1.0f, nullptr, 1.0f, 1, 1, iv},
+    };
+    LA_TRY(hip_status(la::launch_rope(t, 5, g, tc, static_cast<const float*>(rope_table),
+                                      LA_BF16, hs, &t_rope)));
     {
       TimedOp op(&t_attn);
       LA_TRY(la_block_attn_fwd_fp8(r, q8_ws, sink_k8_ws, sink_v8_ws, k8, v8, r->block_tokens,

@@ -69,9 +69,13 @@ struct RopeTensor {
   float* cs_out;
   float cs_scale;
   int32_t copy_only;  // 1: copy the rows unrotated (no cos/sin use)
+  // 1 (bf16 only): out receives e4m3 codes [tokens][heads][head_dim] bytes of the bf16
+  // result times inv8, rounded as la_quantize_fp8 rounds them
+  int32_t e4m3_out;
+  float inv8;
 };
 // One launch serves up to this many tensors (rows of each in order).
-constexpr int kMaxRopeTensors = 4;
+constexpr int kMaxRopeTensors = 5;
 
 struct RopeGeom {
   int32_t HW, Wl, Hl, heads, head_dim, tpairs, hpairs, wpairs;
@@ -139,18 +143,6 @@ hipError_t launch_attn_fp8(const void* q, void* out, float* lse, const AttnSegs&
                            hipStream_t s, const KernelTiming* tm = nullptr);
 hipError_t launch_quantize_fp8(const void* in, int in_dtype, void* out, int64_t n, float inv_scale,
                                hipStream_t s);
-// Several bf16 tensors to e4m3 in one launch (one grid row per tensor); every n is a
-// multiple of 16 and every pointer 16-byte aligned.
-constexpr int kMaxQuantJobs = 6;
-struct QuantJobs {
-  const void* in[kMaxQuantJobs];
-  void* out[kMaxQuantJobs];
-  int64_t n[kMaxQuantJobs];
-  float inv[kMaxQuantJobs];
-  int32_t count;
-};
-hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s,
-                                    const KernelTiming* tm = nullptr);
 // la_block_attn_fwd with its workspace given explicitly: slot_cap > 0 limits the
 // persistent grid to that many workgroups; clear_counters zeroes the arrival counters
 // (with a small fill kernel) before the launch.

@@ -31,6 +31,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+#include "e4m3_dev.h"
+
 constexpr int kThreads = 128;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -50,21 +52,26 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // safe: a thread writes exactly the chunks it read.
 //
 // A tensor marked copy_only is copied as it is (the step stages the block's V in
-// the ring's next slot within the same launch).
+// the ring's next slot within the same launch).  A tensor marked e4m3_out (bf16) is
+// stored as e4m3 codes of its bf16 result times inv8, the arithmetic of the
+// quantisation kernel (the e4m3 step rotates and quantises in one pass).
 template <bool kBF16, int kNH>
 __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTensor t1,
                                                           RopeTensor t2, RopeTensor t3,
-                                                          RopeGeom g, RopeTemporal tc,
+                                                          RopeTensor t4, RopeGeom g,
+                                                          RopeTemporal tc,
                                                           const float* __restrict__ table,
-                                                          int wg0, int wg1, int wg2) {
+                                                          int wg0, int wg1, int wg2, int wg3) {
   constexpr int kPPC = kBF16 ? 4 : 2;  // pairs per 16-byte chunk
   constexpr int kEB = kBF16 ? 2 : 4;   // element bytes
   const int bid = __builtin_amdgcn_workgroup_id_x();
   const int tid = __builtin_amdgcn_workitem_id_x();
-  const int e1 = wg0 + wg1, e2 = e1 + wg2;
-  const int which = bid < wg0 ? 0 : (bid < e1 ? 1 : (bid < e2 ? 2 : 3));
-  const RopeTensor T = which == 0 ? t0 : (which == 1 ? t1 : (which == 2 ? t2 : t3));
-  const int tok = bid - (which == 0 ? 0 : (which == 1 ? wg0 : (which == 2 ? e1 : e2)));
+  const int e1 = wg0 + wg1, e2 = e1 + wg2, e3 = e2 + wg3;
+  const int which = bid < wg0 ? 0 : (bid < e1 ? 1 : (bid < e2 ? 2 : (bid < e3 ? 3 : 4)));
+  const RopeTensor T =
+      which == 0 ? t0 : (which == 1 ? t1 : (which == 2 ? t2 : (which == 3 ? t3 : t4)));
+  const int tok =
+      bid - (which == 0 ? 0 : (which == 1 ? wg0 : (which == 2 ? e1 : (which == 3 ? e2 : e3))));
   const int cpr = g.head_dim / (2 * kPPC);  // chunks per head row
   const int hg_n = kThreads / cpr;          // head groups
   const int ch = tid % cpr;
@@ -74,6 +81,19 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
   const size_t row_bytes = (size_t)g.heads * g.head_dim * kEB;
   const char* src = static_cast<const char*>(T.in) + (size_t)tok * row_bytes;
   char* dst = static_cast<char*>(T.out) + (size_t)tok * row_bytes;
+  // e4m3 output: one byte per element, 8 bytes per 16-byte input chunk
+  char* dst8 = static_cast<char*>(T.out) + (size_t)tok * g.heads * g.head_dim;
+  const bool to8 = kBF16 && T.e4m3_out;
+  auto store8 = [&](int head, const u32x4_t& v) __attribute__((always_inline)) {
+    const float inv = T.inv8;
+    const uint32_t lo = e4m3x4(bf_lo(v[0]) * inv, bf_hi(v[0]) * inv, bf_lo(v[1]) * inv,
+                               bf_hi(v[1]) * inv);
+    const uint32_t hi = e4m3x4(bf_lo(v[2]) * inv, bf_hi(v[2]) * inv, bf_lo(v[3]) * inv,
+                               bf_hi(v[3]) * inv);
+    const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC);
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(dst8 + off));
+  };
 
   u32x4_t x[kNH];
   auto load_pass = [&](int h0) __attribute__((always_inline)) {
@@ -94,8 +114,12 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
       for (int k = 0; k < kNH; ++k) {
         const int head = h0 + hg + k * hg_n;
         if (head < g.heads) {
-          const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
-          __builtin_nontemporal_store(x[k], reinterpret_cast<u32x4_t*>(dst + off));
+          if (to8) {
+            store8(head, x[k]);
+          } else {
+            const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
+            __builtin_nontemporal_store(x[k], reinterpret_cast<u32x4_t*>(dst + off));
+          }
         }
       }
     }
@@ -180,8 +204,12 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeTensor t0, RopeTen
     for (int k = 0; k < kNH; ++k) {
       const int head = h0 + hg + k * hg_n;
       if (head < g.heads) {
-        const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
-        __builtin_nontemporal_store(y[k], reinterpret_cast<u32x4_t*>(dst + off));
+        if (to8) {
+          store8(head, y[k]);
+        } else {
+          const uint32_t off = (uint32_t)(head * g.head_dim + ch * 2 * kPPC) * kEB;
+          __builtin_nontemporal_store(y[k], reinterpret_cast<u32x4_t*>(dst + off));
+        }
       }
     }
   }
@@ -216,7 +244,7 @@ static void launch_rope_nh(int nh, dim3 grid, hipStream_t s, const RopeTensor* t
 #define LA_ROPE_NH(N)                                                                        \
   case N:                                                                                    \
     launch_kernel(tm, rope3d_kernel<kBF16, N>, grid, dim3(kThreads), 0, s, tt[0], tt[1],     \
-                  tt[2], tt[3], g, tc, table, wg[0], wg[1], wg[2]);                          \
+                  tt[2], tt[3], tt[4], g, tc, table, wg[0], wg[1], wg[2], wg[3]);            \
     break;
   switch (nh) {
     LA_ROPE_NH(1) LA_ROPE_NH(2) LA_ROPE_NH(3) LA_ROPE_NH(4)
@@ -233,7 +261,8 @@ hipError_t launch_rope(const RopeTensor* t, int nt, const RopeGeom& g, const Rop
     tt[i] = t[i];
     if (t[i].in) wg[i] = t[i].tokens;
   }
-  const int total = wg[0] + wg[1] + wg[2] + wg[3];
+  int total = 0;
+  for (int i = 0; i < kMaxRopeTensors; ++i) total += wg[i];
   if (total == 0) return timing_without_kernel(tm, s);
   const int cpr = g.head_dim / (dt == LA_BF16 ? 8 : 4);
   const int hg_n = kThreads / cpr;

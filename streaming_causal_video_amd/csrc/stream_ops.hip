@@ -114,27 +114,7 @@ __global__ __launch_bounds__(kThreads) void euler_scalar_kernel(float* __restric
     x[i] = fmaf(dt, v[i], x[i]);
 }
 
-// e4m3 code of each float, round to nearest even (v_cvt_pk_fp8_f32) after
-// clamping to +-448: the conversion instruction maps magnitudes that round past
-// 448 to NaN, the quantisation saturates them.  A NaN becomes the NaN code of its
-// sign, 0x7F / 0xFF (the clamp alone would turn it into -448).
-__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
-
-__device__ __forceinline__ uint32_t nan_fix(uint32_t code, float x, int byte) {
-  if (x == x) return code;
-  const uint32_t nanc = 0x7Fu | ((__float_as_uint(x) >> 31) << 7);
-  return (code & ~(0xFFu << (8 * byte))) | (nanc << (8 * byte));
-}
-
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
-  uint32_t u = (uint32_t)w;
-  u = nan_fix(u, a, 0);
-  u = nan_fix(u, b, 1);
-  u = nan_fix(u, c, 2);
-  return nan_fix(u, d, 3);
-}
+#include "e4m3_dev.h"
 
 // out[i] = e4m3(in[i] * inv): 16 elements per thread (two or four 16-byte loads,
 // one 16-byte store); the last n % 16 elements by the thread after the last chunk.
@@ -178,31 +158,6 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const void* __restr
   }
 }
 
-// The bf16 tensors of QuantJobs, each a multiple of 16 elements: grid row y is
-// tensor y, a bounded grid of workgroups loops over its 16-element chunks with the
-// element arithmetic of quant_fp8_kernel (so the codes are the same bits).
-__global__ __launch_bounds__(kThreads) void quant_fp8_many_kernel(QuantJobs jobs) {
-  const int j = blockIdx.y;
-  const u32x4_t* __restrict__ in = static_cast<const u32x4_t*>(jobs.in[j]);
-  uint4* __restrict__ out = static_cast<uint4*>(jobs.out[j]);
-  const int64_t n16 = jobs.n[j] / 16;
-  const float inv = jobs.inv[j];
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
-       i += (int64_t)gridDim.x * kThreads) {
-    const u32x4_t a = __builtin_nontemporal_load(in + 2 * i);
-    const u32x4_t b = __builtin_nontemporal_load(in + 2 * i + 1);
-    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    float x[16];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      x[2 * k] = __uint_as_float(w[k] << 16) * inv;
-      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u) * inv;
-    }
-    out[i] = make_uint4(e4m3x4(x[0], x[1], x[2], x[3]), e4m3x4(x[4], x[5], x[6], x[7]),
-                        e4m3x4(x[8], x[9], x[10], x[11]), e4m3x4(x[12], x[13], x[14], x[15]));
-  }
-}
-
 __global__ __launch_bounds__(kThreads) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads)
@@ -233,21 +188,6 @@ hipError_t launch_copy2(void* d0, const void* s0, void* d1, const void* s1, size
   launch_kernel(tm, copy2_kernel, grid, dim3(kThreads), 0, s, static_cast<u32x4_t*>(d0),
                      static_cast<const u32x4_t*>(s0), static_cast<u32x4_t*>(d1),
                      static_cast<const u32x4_t*>(s1), n16, tail);
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_fp8_many(const QuantJobs& jobs, hipStream_t s, const KernelTiming* tm) {
-  if (jobs.count < 1 || jobs.count > kMaxQuantJobs) return hipErrorInvalidValue;
-  int64_t most = 0;
-  for (int j = 0; j < jobs.count; ++j) {
-    if (jobs.n[j] % 16 != 0) return hipErrorInvalidValue;
-    most = jobs.n[j] > most ? jobs.n[j] : most;
-  }
-  if (most == 0) return timing_without_kernel(tm, s);
-  int64_t wgs = (most / 16 + kThreads - 1) / kThreads;
-  if (wgs > 2048) wgs = 2048;
-  launch_kernel(tm, quant_fp8_many_kernel, dim3((unsigned)wgs, jobs.count), dim3(kThreads), 0, s,
-                jobs);
   return hipGetLastError();
 }
 
