@@ -608,8 +608,8 @@ def fp8_main(args):
 
 
 def c4fp8_main(args):
-    """--workload c4fp8: the C4 step on e4m3 rings (la_denoise_step_fp8): RoPE, one
-    quantisation launch, e4m3 attention, the append of K/V codes, Euler."""
+    """--workload c4fp8: the C4 step on e4m3 rings (la_denoise_step_fp8): one launch of
+    RoPE and quantisation, e4m3 attention, the append of K/V codes, Euler."""
     geo = dict(Hl=30, Wl=52, W=4, H=40, d=128, n_layers=40)
     r = gpu_step_bench(args, fp8=True, **geo)
     version = kernel_version("fp8-")
