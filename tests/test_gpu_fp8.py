@@ -510,3 +510,48 @@ def test_fp8_denoise_step_c2_sampled(L):
     gv = st.v_slots[0, slot].cpu().numpy()[:, heads]
     assert np.array_equal(gv, vals[-1]), "C2 last block: V codes differ"
     say(f"fp8 step C2 block {last}: rel-L2 {r:.4f}")
+
+
+@pytest.mark.parametrize("block_id", [1, 3])
+def test_fp8_step_codes_equal_rope_then_quantise(L, block_id):
+    """The e4m3 step's one RoPE + quantisation launch writes, bit for bit, the codes of
+    la_rope3d_rolling (bf16 out) followed by la_quantize_fp8: Q, the sink K and the sink V
+    in their workspaces, K and V in k8_ws / v8_ws (plain ring, attend-only, so the step
+    keeps them there), at block 1 and at a later block (other frame positions)."""
+    t = torch()
+    s = si.MID_BF16
+    dk = dv = SCALE_QKV
+    dq = L.la_fp8_q_factor_pow2(s.head_dim ** -0.5, dk, dk)
+    st = L.KVRingStack(1, s.W, s.block_tokens, s.sink_tokens, s.heads, s.head_dim, t.uint8,
+                       0.75, staged=False)
+    sk, sv = s.initial_sink(0)
+    st.sink_k_raw[0].copy_(to_dev(sk))
+    st.sink_v[0].copy_(to_dev(sv))
+    # bring the ring to block_id - 1 (appending zero codes) so the step accepts block_id
+    z8 = t.zeros((s.block_tokens, s.heads, s.head_dim), dtype=t.uint8, device="cuda")
+    for b in range(1, block_id):
+        L.la_kvcache_append_evict(st.states[0], z8, z8, b, 0.75)
+    blk, snk = (s.block_tokens, s.heads, s.head_dim), (s.sink_tokens, s.heads, s.head_dim)
+    u8 = lambda shp: t.full(shp, 0xAA, dtype=t.uint8, device="cuda")
+    bf = lambda shp: t.empty(shp, dtype=t.bfloat16, device="cuda")
+    table = t.empty(L.la_rope_table_bytes(s.Hl, s.Wl, s.head_dim) // 4, dtype=t.float32,
+                    device="cuda")
+    L.la_rope_table_fill(table, s.Hl, s.Wl, s.head_dim, 10000.0)
+    q, k, v = (to_dev(z) for z in s.block_inputs(0, block_id))
+    q8, k8, v8, sk8, sv8 = u8(blk), u8(blk), u8(blk), u8(snk), u8(snk)
+    L.la_denoise_step_fp8(st.states, block_id, [q], [k], [v], [bf(blk)], None, None, None, q8,
+                          k8, v8, sk8, sv8, table, s.Hl, s.Wl, 3, -1, 10000.0,
+                          scale=s.head_dim ** -0.5, dq=dq, dk=dk, dv=dv,
+                          flags=L.LA_STEP_ATTEND_ONLY)
+    qr, kr, skr = bf(blk), bf(blk), bf(snk)
+    L.la_rope3d_rolling(q, qr, k, kr, 3, 3 * (block_id - 1), st.sink_k_raw[0], skr, -1, table,
+                        s.Hl, s.Wl, s.heads, s.head_dim, 10000.0, 1.0)
+    want = []
+    for x, f in ((qr, dq), (kr, dk), (v, dv), (skr, dk), (st.sink_v[0], dv)):
+        o = t.empty(x.shape, dtype=t.uint8, device="cuda")
+        L.la_quantize_fp8(x, o, inv32(f))
+        want.append(o)
+    t.cuda.synchronize()
+    for name, got, ref in zip(("Q", "K", "V", "sink K", "sink V"), (q8, k8, v8, sk8, sv8), want):
+        assert t.equal(got, ref), f"block {block_id} {name}: {(got != ref).sum().item()} codes differ"
+    say(f"fp8 step block {block_id}: the five code tensors equal RoPE then quantisation")
