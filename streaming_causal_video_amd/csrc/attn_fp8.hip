@@ -45,11 +45,10 @@
 //    P = exp2(s - m + 6) rounded to e4m3 (the 2^6 lifts small probabilities out
 //    of the subnormal range).  When that factor is a power of two to within a
 //    relative 2^-24 (the caller picks dq for it), the score MFMA applies that
-//    power as its E8M0 operand scale and
-//    takes 6 - m as its accumulator input, so each score leaves the MFMA as its
-//    exponent and costs one v_exp_f32 instead of a multiply-add and the exp
-//    (1.7 % faster at the C2 shape; the input is formed per tile, because
-//    keeping it live spilled a Q fragment).
+//    power as its E8M0 operand scale and takes 6 - m as its accumulator input,
+//    so each score leaves the MFMA as its exponent and costs one v_exp_f32
+//    instead of a multiply-add and the exp (1.7 % faster at the C2 shape; the
+//    input is formed per tile, because keeping it live spilled a Q fragment).
 //  * The row sum is one more MFMA per tile, of an all-ones A operand with the
 //    same e4m3 P: it moves 32 additions per lane off the VALU, which bounds
 //    this kernel, and numerator and denominator use the same rounded P.
@@ -118,9 +117,9 @@ __device__ __forceinline__ f32x16_t mma_scaled(const i32x8_t& a, const i32x8_t& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sc, 0, 127);
 }
 
-// kFold: the logit factor is 2^(sc - 127) (to 2^-24), applied by the score MFMA's operand scale,
-// and the MFMA's accumulator input carries the reference (6 - m): the scores come out
-// in the exponent's units and P = exp2(S) needs no multiply-add per score.
+// kFold: the logit factor is 2^(sc - 127) (to 2^-24), applied by the score MFMA's
+// operand scale, and the MFMA's accumulator input carries the reference (6 - m): the
+// scores come out in the exponent's units and P = exp2(S) needs no multiply-add.
 template <bool kFold>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(3, 3))) void
@@ -345,7 +344,8 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
           float p[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            p[t] = __builtin_amdgcn_exp2f(kFold ? st[b][4 * g + t] : fmaf(st[b][4 * g + t], c2, nm));
+            p[t] = __builtin_amdgcn_exp2f(kFold ? st[b][4 * g + t]
+                                                : fmaf(st[b][4 * g + t], c2, nm));
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
           pf[4 * b + g] = w;
@@ -355,8 +355,9 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
     probs();
     // A probability past the e4m3 range converts to a NaN code, which the row
     // sum carries: only then is the reference max raised to this tile's max
-    // (always on the first tile, whose reference starts at -1e30), O and the
-    // row sum rescaled and the tile's probabilities redone.
+    // (always on the first tile: without kFold its reference starts at -1e30, with
+    // kFold the first tile is taken here by its index), O and the row sum rescaled
+    // and the tile's probabilities redone.
     const bool first = kFold && j == 0;
     if (__builtin_amdgcn_ballot_w64(first ||
                                     (__float_as_uint(tsum[0]) & 0x7fffffffu) > 0x7f800000u) != 0) {
@@ -379,14 +380,14 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
           for (int i = 0; i < 16; ++i) st[b][i] -= delta;
         probs();
       } else {
-      mx *= c2;
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+        mx *= c2;
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-      probs();
+        for (int i = 0; i < 4; ++i) o[i] *= alpha;
+        probs();
       }
     }
     l_run += tsum[0];
