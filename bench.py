@@ -639,7 +639,9 @@ def c4fp8_main(args):
         "attn_ms": round(r["attn_ms"], 4),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_fp8_kernel", "kernel_version": version,
+                     # the same launch shape as --workload c2fp8's, where the counters were read
+                     "traffic": FP8_TRAFFIC_BYTES.get(version), "kernel": "attn_fp8_kernel",
+                     "kernel_version": version,
                      "flop_per_launch": r["attn_flop_per_launch"]},
         "streaming_kernels": {
             "method": ("in the step: each kernel's own begin and end timestamps (HIP events "
