@@ -323,10 +323,11 @@ def test_fp8_folded_factor_far_from_one(L, target_exp):
 
 
 @pytest.mark.timeout(900)
-def test_fp8_attention_c5_sampled(L):
+@pytest.mark.parametrize("q_pow2", [False, True], ids=["dq=dk", "dq-pow2"])
+def test_fp8_attention_c5_sampled(L, q_pow2):
     """720p-shaped layer (Nk 56320 at block 5, eviction at 6), sampled rows of two heads."""
     shape = si.C5
-    fs = Fp8Stream(L, shape)
+    fs = Fp8Stream(L, shape, q_pow2=q_pow2)
     rng = np.random.default_rng(19)
     rows = np.unique(np.concatenate([[0, 255, 256, shape.block_tokens - 1],
                                      rng.integers(0, shape.block_tokens, 40)]))
@@ -340,7 +341,6 @@ def test_fp8_attention_c5_sampled(L):
             r = check_fp8(got, out, a, vmax, f"C5 fp8 block {b}")
             got_lse = fs.lse.cpu().numpy().astype(np.float64)[heads][:, rows]
             check_lse(got_lse, lse, fs.lse_bar, f"fp8 C5 block {b}")
-            say(f"fp8 C5 block {b}: rel-L2 {r:.4f}")
             say(f"fp8 C5 block {b}: rel-L2 {r:.4f}")
 
 
