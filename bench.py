@@ -50,7 +50,7 @@ ATTN_TRAFFIC_BYTES = {"attn-v9": 8.618e8, "attn-v12": 9.031e8, "attn-v13": 9.128
                       "attn-v15": 8.118e8, "attn-v16": 8.916e8, "attn-v17": 8.962e8}
 # The same for the e4m3 attention kernel at the C2 shape (--workload c2fp8).
 FP8_TRAFFIC_BYTES = {"fp8-v6": 5.337e+08, "fp8-v7": 5.276e+08, "fp8-v8": 5.274e+08,
-                     "fp8-v9": 5.338e+08}
+                     "fp8-v9": 5.338e+08, "fp8-v10": 4.739e+08}
 
 
 _T0 = time.perf_counter()

@@ -49,6 +49,8 @@
 //    so each score leaves the MFMA as its exponent and costs one v_exp_f32
 //    instead of a multiply-add and the exp (1.7 % faster at the C2 shape; the
 //    input is formed per tile, because keeping it live spilled a Q fragment).
+//  * Issue priority (s_setprio) is raised while a wave computes its tile's
+//    probabilities, as in the bf16 kernel.
 //  * The row sum is one more MFMA per tile, of an all-ones A operand with the
 //    same e4m3 P: it moves 32 additions per lane off the VALU, which bounds
 //    this kernel, and numerator and denominator use the same rounded P.
@@ -352,7 +354,13 @@ attn_fp8_kernel(const uint8_t* __restrict__ q, uint16_t* __restrict__ out,
         }
       tsum = mma(ones, pf, f32x16_t{});
     };
+    // Issue priority raised for the probabilities only (the SIMD's three waves belong
+    // to different workgroups): this wave's exp chain goes first while the others'
+    // MFMAs fill the matrix core.  Measured 2.0-2.3 % faster at the C2 shape; raising
+    // it through the overflow check as well gained less.
+    __builtin_amdgcn_s_setprio(1);
     probs();
+    __builtin_amdgcn_s_setprio(0);
     // A probability past the e4m3 range converts to a NaN code, which the row
     // sum carries: only then is the reference max raised to this tile's max
     // (always on the first tile: without kFold its reference starts at -1e30, with

@@ -87,7 +87,7 @@ size_t attn_ws_bytes(int n_q, int heads, int slots) {
 
 extern "C" {
 
-const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v9"; }
+const char* la_version(void) { return "liblahip 0.8 (gfx950) attn-v17 fp8-v10"; }
 
 const char* la_status_string(int st) {
   switch (st) {
